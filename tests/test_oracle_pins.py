@@ -1,0 +1,202 @@
+"""Pins for the CPU oracle (no GPU): each check is fixed by mathematics or by
+the pages, not by the oracle itself.
+
+Recurrence (Kimi K3 technical report summary, "Key claims"/"Method", section
+2.1): per head S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,
+o_t = S_t^T q_t / sqrt(dk).  Gate (section 2.1.1, Fig. 3): g = gmin*Sigmoid(exp(A) z),
+gmin = -5.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_96_amd import synth
+from oracle import brute, chunkwise, gate, seq
+
+
+def _rand_case(rng, B, T, H, dk, dv, g_low=-5.0, with_h0=True):
+    q = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, dk))
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    g = rng.uniform(g_low, 0.0, (B, T, H, dk)).astype(np.float32)
+    beta = rng.uniform(0.05, 1.0, (B, T, H)).astype(np.float32)
+    h0 = rng.standard_normal((B, H, dk, dv)) if with_h0 else None
+    return q, k, v, g, beta, h0
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return np.max(np.abs(a - b)) / max(np.sqrt(np.mean(b * b)), 1e-300)
+
+
+# ---------------------------------------------------------------- brute force
+@pytest.mark.parametrize("B,T,H,dk,dv", [(1, 1, 1, 1, 1), (1, 5, 2, 3, 2), (2, 6, 1, 4, 3), (1, 4, 1, 2, 4)])
+def test_seq_matches_brute_force(B, T, H, dk, dv):
+    rng = np.random.default_rng(1000 + T * 7 + dk)
+    q, k, v, g, beta, h0 = _rand_case(rng, B, T, H, dk, dv, g_low=-1.5)
+    o, ht = seq.kda_seq(q, k, v, g, beta, h0)
+    ob, hb = brute.kda_brute(q, k, v, g, beta, h0)
+    ob = np.array([[[[float(x) for x in ob[b][t][h]] for h in range(H)] for t in range(T)] for b in range(B)])
+    hb = np.array([[[[float(x) for x in row] for row in hb[b][h]] for h in range(H)] for b in range(B)])
+    assert _rel(o, ob) <= 1e-12
+    assert _rel(ht, hb) <= 1e-12
+
+
+def test_scalar_state_hand_values():
+    # dk = dv = 1, three tokens, exact arithmetic by hand:
+    # S1 = (1 - b1 k1^2) e^{g1} S0 + b1 k1 v1, o1 = S1 q1 (scale = 1)
+    # S0 = 2, g = (0, ln 1/2, 0), k = (1, 1, 0.5), v = (3, -1, 4), beta = (0.5, 1, 0.25), q = 1
+    # S1 = 0.5*2 + 0.5*3 = 2.5 ; S2 = 0*(0.5*2.5) + 1*(-1) = -1 ; S3 = (1-1/16)*(-1) + 0.25*0.5*4 = -0.4375
+    g = np.array([0.0, math.log(0.5), 0.0]).reshape(1, 3, 1, 1)
+    k = np.array([1.0, 1.0, 0.5]).reshape(1, 3, 1, 1)
+    v = np.array([3.0, -1.0, 4.0]).reshape(1, 3, 1, 1)
+    beta = np.array([0.5, 1.0, 0.25]).reshape(1, 3, 1)
+    q = np.ones((1, 3, 1, 1))
+    # g is passed as fp32 in the oracle; ln(1/2) rounds, so compare at fp32 level
+    o, ht = seq.kda_seq(q, k, v, g, beta, np.full((1, 1, 1, 1), 2.0), scale=1.0)
+    np.testing.assert_allclose(o[0, :, 0, 0], [2.5, -1.0, -0.4375], rtol=0, atol=1e-7)
+    np.testing.assert_allclose(ht[0, 0, 0, 0], -0.4375, atol=1e-7)
+
+
+# ---------------------------------------------------------------- chunkwise form
+@pytest.mark.parametrize("chunk", [1, 16, 64])
+def test_chunkwise_matches_seq(chunk):
+    rng = np.random.default_rng(7)
+    q, k, v, g, beta, h0 = _rand_case(rng, 1, 200, 2, 16, 12)
+    o, ht = seq.kda_seq(q, k, v, g, beta, h0)
+    oc, hc = chunkwise.kda_chunkwise(q, k, v, g, beta, h0, chunk=chunk)
+    assert _rel(oc, o) <= 1e-12
+    assert _rel(hc, ht) <= 1e-12
+
+
+def test_chunkwise_matches_seq_generator_inputs():
+    d = synth.make_inputs(1, 130, 2, 32, 16, seed=5)
+    g = gate.gate(d["z"], d["A"]).astype(np.float32)
+    o, ht = seq.kda_seq(d["q"], d["k"], d["v"], g, d["beta"], d["h0"])
+    oc, hc = chunkwise.kda_chunkwise(d["q"], d["k"], d["v"], g, d["beta"], d["h0"], chunk=64)
+    assert _rel(oc, o) <= 1e-12 and _rel(hc, ht) <= 1e-12
+
+
+# ---------------------------------------------------------------- closed forms / invariants
+def test_beta_zero_is_pure_decay():
+    # beta = 0: S_t = Diag(exp(G_t)) S_0 with G the global cumulative sum;
+    # o_t = scale * S_0^T (exp(G_t) * q_t)
+    rng = np.random.default_rng(3)
+    q, k, v, g, beta, h0 = _rand_case(rng, 2, 40, 2, 8, 5)
+    beta[:] = 0.0
+    o, ht = seq.kda_seq(q, k, v, g, beta, h0)
+    G = np.cumsum(g.astype(np.float64), axis=1)
+    sc = 1 / math.sqrt(8)
+    o_cf = sc * np.einsum("bthc,bhcj->bthj", np.exp(G) * q.astype(np.float64), h0)
+    h_cf = np.exp(G[:, -1])[..., None] * h0
+    assert _rel(o, o_cf) <= 1e-12
+    assert _rel(ht, h_cf) <= 1e-12
+
+
+def test_orthonormal_keys_write_and_read_back():
+    # g = 0, beta = 1, orthonormal keys: S_T^T k_s = v_s exactly for every s
+    dk, dv, T = 8, 5, 6
+    K = synth.orthonormal_keys(11, T, dk)
+    rng = np.random.default_rng(4)
+    V = rng.standard_normal((T, dv))
+    k = K.reshape(1, T, 1, dk).astype(np.float32)
+    v = V.reshape(1, T, 1, dv).astype(np.float32)
+    q = np.zeros_like(k)
+    g = np.zeros_like(k)
+    beta = np.ones((1, T, 1), np.float32)
+    h0 = rng.standard_normal((1, 1, dk, dv))
+    _, ht = seq.kda_seq(q, k, v, g, beta, h0)
+    kf = k[0, :, 0].astype(np.float64)
+    read = kf @ ht[0, 0]
+    # keys were rounded to fp32 before the run, so they are orthonormal to ~1e-7
+    np.testing.assert_allclose(read, v[0, :, 0], atol=2e-6)
+
+
+def test_pad_tokens_are_identity():
+    rng = np.random.default_rng(5)
+    q, k, v, g, beta, h0 = _rand_case(rng, 1, 37, 2, 8, 6)
+    o1, h1 = seq.kda_seq(q, k, v, g, beta, h0)
+    pad = 27
+    z = lambda x: np.concatenate([x, np.zeros((x.shape[0], pad) + x.shape[2:], x.dtype)], axis=1)
+    o2, h2 = seq.kda_seq(z(q), z(k), z(v), z(g), z(beta), h0)
+    assert np.array_equal(h1, h2)
+    assert np.array_equal(o1, o2[:, :37])
+
+
+def test_segment_split_is_exact():
+    rng = np.random.default_rng(6)
+    q, k, v, g, beta, h0 = _rand_case(rng, 2, 90, 2, 8, 6)
+    o, ht = seq.kda_seq(q, k, v, g, beta, h0)
+    cut = 33
+    oa, ha = seq.kda_seq(q[:, :cut], k[:, :cut], v[:, :cut], g[:, :cut], beta[:, :cut], h0)
+    ob, hb = seq.kda_seq(q[:, cut:], k[:, cut:], v[:, cut:], g[:, cut:], beta[:, cut:], ha)
+    assert np.array_equal(np.concatenate([oa, ob], axis=1), o)
+    assert np.array_equal(hb, ht)
+
+
+def test_heads_and_batches_are_independent():
+    rng = np.random.default_rng(8)
+    q, k, v, g, beta, h0 = _rand_case(rng, 2, 20, 3, 4, 3)
+    o, ht = seq.kda_seq(q, k, v, g, beta, h0)
+    perm = [2, 0, 1]
+    o2, h2 = seq.kda_seq(q[:, :, perm], k[:, :, perm], v[:, :, perm], g[:, :, perm], beta[:, :, perm], h0[:, perm])
+    assert np.array_equal(o2, o[:, :, perm]) and np.array_equal(h2, ht[:, perm])
+    o3, h3 = seq.kda_seq(q[::-1], k[::-1], v[::-1], g[::-1], beta[::-1], h0[::-1])
+    assert np.array_equal(o3, o[::-1]) and np.array_equal(h3, ht[::-1])
+
+
+def test_nan_stays_in_its_head():
+    rng = np.random.default_rng(9)
+    q, k, v, g, beta, h0 = _rand_case(rng, 1, 10, 3, 4, 3)
+    v[0, 4, 1, 0] = np.nan
+    o, ht = seq.kda_seq(q, k, v, g, beta, h0)
+    assert np.isnan(o[0, 4:, 1]).any() and np.isfinite(o[0, :, [0, 2]]).all()
+    assert np.isfinite(ht[0, [0, 2]]).all()
+
+
+# ---------------------------------------------------------------- gate
+def test_gate_closed_forms():
+    A = np.array([-1.0, 0.0, 0.7])
+    z0 = np.zeros((1, 1, 3, 4))
+    assert np.all(gate.gate(z0, A) == -2.5)                       # sigmoid(0) = 1/2
+    z = (np.log(3.0) / np.exp(A))[None, None, :, None] * np.ones((1, 1, 3, 4))
+    np.testing.assert_allclose(gate.gate(z, A), -3.75, rtol=0, atol=1e-14)   # sigmoid(ln 3) = 3/4
+    rng = np.random.default_rng(2)
+    zz = rng.standard_normal((2, 5, 3, 4))
+    np.testing.assert_allclose(gate.gate(zz, A) + gate.gate(-zz, A), -5.0, atol=1e-14)  # odd symmetry
+    assert np.all(gate.gate(np.full((1, 1, 3, 1), 200.0), A) == -5.0)    # floor reached
+
+
+def test_gate_monotone_and_in_range():
+    d = synth.make_inputs(1, 256, 4, 64, 8, seed=1, with_h0=False)
+    g = gate.gate(d["z"], d["A"])
+    assert g.min() >= -5.0 and g.max() < 0.0
+    zs = np.linspace(-30, 30, 2001)[None, None, None, :].repeat(2, axis=2)
+    gs = gate.gate(zs, np.array([-0.3, 0.9]))
+    assert np.all(np.diff(gs, axis=-1) <= 0)
+    # mean of g over the base distribution is gmin/2 by the odd symmetry
+    assert abs(g.mean() + 2.5) < 0.05
+
+
+def test_chunk_cumsum_definition():
+    rng = np.random.default_rng(12)
+    g = rng.uniform(-5, 0, (2, 150, 3, 4))
+    G = gate.chunk_cumsum(g, 64)
+    for t0 in (0, 64, 128):
+        np.testing.assert_array_equal(G[:, t0], g[:, t0])              # restarts at each chunk
+    d = np.diff(G, axis=1)
+    mask = np.ones(149, bool); mask[[63, 127]] = False
+    np.testing.assert_allclose(d[:, mask], g[:, 1:][:, mask], atol=1e-12)
+    np.testing.assert_allclose(G[:, 149], g[:, 128:150].sum(axis=1), atol=1e-12)
+
+
+def test_sixteen_row_rescaling_bound_fits_bf16():
+    # With g >= gmin = -5, 16 rows accumulate at most -80, so exp(+80) is the
+    # largest reciprocal rescaling factor on a 16-row sub-chunk; the largest
+    # finite bf16 is (2 - 2^-7) * 2^127.
+    bf16_max = (2 - 2 ** -7) * 2.0 ** 127
+    assert 16 * 5 < math.log(bf16_max)
+    assert math.exp(-80) > 2.0 ** -126            # its inverse is a normal number too
+    assert 17 * 5 < math.log(bf16_max) < 18 * 5   # 17 rows still fit, 18 could overflow
