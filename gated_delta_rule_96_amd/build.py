@@ -1,0 +1,72 @@
+"""Build libkda.so (gfx950) in-tree with hipcc.
+
+Every HIP translation unit is compiled with packed fp32 instructions
+disabled (-packed-fp32-ops) and linked with the C-ABI layer into
+gated_delta_rule_96_amd/libkda.so.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+OUT = PKG / "libkda.so"
+BUILD = PKG / "_build"
+ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
+
+SOURCES = ["kda_api.cpp", "kda_decay.hip", "kda_chunk.hip", "kda_decode.hip"]
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", f"-I{ROOT / 'include'}",
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src: Path, obj: Path) -> str:
+    lang = ["-x", "hip"] if src.suffix == ".cpp" else []
+    cmd = [hipcc(), *COMMON, *lang, "-c", str(src), "-o", str(obj)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r.stderr
+
+
+def build(verbose: bool = False) -> Path:
+    BUILD.mkdir(exist_ok=True)
+    objs = []
+    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        futs = {}
+        for s in SOURCES:
+            src = CSRC / s
+            obj = BUILD / (src.stem + ".o")
+            objs.append(obj)
+            futs[ex.submit(_compile, src, obj)] = s
+        for f in cf.as_completed(futs):
+            msg = f.result()
+            if verbose and msg.strip():
+                print(f"[{futs[f]}]\n{msg}", file=sys.stderr)
+    tmp = OUT.with_suffix(f".so.tmp{os.getpid()}")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,112 @@
+// C ABI of libkda.so (declared in include/kda.h): synchronous argument
+// validation, then dispatch to the gfx950 kernels on the caller's stream.
+// Nothing here allocates device memory or keeps mutable global state.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_launch.h"
+
+namespace {
+
+constexpr int kChunk = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool supported_d(int d) { return d == 64 || d == 128; }
+bool valid_dtype(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+
+// Largest element count of any [B, T, H, d] tensor accepted (64-bit offsets
+// are used throughout; this only rejects sizes whose byte count overflows).
+bool size_ok(long long a, long long b, long long c, long long d) {
+  const long long lim = (1LL << 62);
+  long long x = a;
+  for (long long y : {b, c, d}) {
+    if (y <= 0 || x > lim / y) return false;
+    x *= y;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_str(int s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is non-positive or too large";
+    case KDA_ERR_DTYPE: return "dtype is not KDA_F32 or KDA_BF16";
+    case KDA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case KDA_ERR_UNSUPPORTED: return "unsupported dk/dv/chunk (dk, dv in {64,128}; chunk 64)";
+    case KDA_ERR_WORKSPACE: return "workspace missing or smaller than kda_fwd_workspace_bytes";
+    case KDA_ERR_RANGE: return "input value out of range";
+    case KDA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int kda_prepare_decay(const void* z, const float* A, float gmin, void* g, float* gcum, int dtype, int B, int T,
+                      int H, int dk, int chunk, void* stream) {
+  if (!valid_dtype(dtype)) return KDA_ERR_DTYPE;
+  if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || chunk <= 0 || !size_ok(B, T, H, dk)) return KDA_ERR_SHAPE;
+  if (!supported_d(dk) || chunk != kChunk) return KDA_ERR_UNSUPPORTED;
+  if (z) {
+    if (!A || (!g && !gcum)) return KDA_ERR_NULL;
+  } else {
+    if (!g || !gcum) return KDA_ERR_NULL;
+  }
+  if ((z && !aligned16(z)) || (g && !aligned16(g)) || (gcum && !aligned16(gcum)) || (A && !aligned16(A)))
+    return KDA_ERR_ALIGN;
+  hipError_t e = kda::launch_prepare_decay(dtype == KDA_BF16, z, A, gmin, g, gcum, B, T, H, dk, chunk,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+  if (!valid_dtype(dtype) || B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) ||
+      chunk != kChunk)
+    return 0;
+  const size_t nchunks = ((size_t)T + kChunk - 1) / kChunk;
+  return (size_t)B * (size_t)H * nchunks * kda::fwd_record_bytes(dtype == KDA_BF16, dk, dv);
+}
+
+int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                    const void* beta, float scale, const float* h0, float* ht, float* o, int dtype, int B, int T,
+                    int H, int dk, int dv, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return KDA_ERR_DTYPE;
+  if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0 || !size_ok(B, T, H, dk) ||
+      !size_ok(B, T, H, dv) || (long long)B * H * ((T + kChunk - 1) / kChunk) > 2147483647LL)
+    return KDA_ERR_SHAPE;
+  if (!supported_d(dk) || !supported_d(dv) || chunk != kChunk) return KDA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !beta || !o || (!g && !gcum)) return KDA_ERR_NULL;
+  if (!workspace) return KDA_ERR_WORKSPACE;
+  for (const void* p : {q, k, v, beta, (const void*)o})
+    if (!aligned16(p)) return KDA_ERR_ALIGN;
+  if ((g && !aligned16(g)) || (gcum && !aligned16(gcum)) || (h0 && !aligned16(h0)) || (ht && !aligned16(ht)))
+    return KDA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_ALIGN;
+  if (workspace_bytes < kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
+  hipError_t e = kda::launch_fwd_chunked(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk,
+                                         dv, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                    float* state, float* o, int dtype, int B, int H, int dk, int dv, void* stream) {
+  if (!valid_dtype(dtype)) return KDA_ERR_DTYPE;
+  if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0 || !size_ok(B, H, dk, dv)) return KDA_ERR_SHAPE;
+  if (!supported_d(dk) || !supported_d(dv)) return KDA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+  for (const void* p : {q, k, v, g, beta, (const void*)state, (const void*)o})
+    if (!aligned16(p)) return KDA_ERR_ALIGN;
+  if ((long long)B * H > 2147483647LL) return KDA_ERR_SHAPE;
+  hipError_t e = kda::launch_decode_step(dtype == KDA_BF16, q, k, v, g, beta, scale, state, o, B, H, dk, dv,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

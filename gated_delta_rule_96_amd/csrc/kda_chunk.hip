@@ -1,0 +1,628 @@
+// Chunked KDA prefill on gfx950: an intra-chunk kernel (parallel over every
+// chunk of every head) followed by a state pass (sequential over chunks,
+// parallel over heads and value-column blocks).
+//
+// Method (Kimi K3 technical report summary, page "Kimi K3 Technical Report -
+// Open Frontier Intelligence"): "Key claims" section 2.1 (delta-rule state
+// with channel-wise decay), section 2.1.1 / Fig. 3 (log-decay floored at
+// gmin = -5 so that the reciprocal rescaling factors stay inside the bf16
+// range and every causal tile, diagonal ones included, is a dense matrix
+// product), "Method" section 2.1 (chunkwise-parallel form).
+//
+// Per (b, h) and chunk of C = 64 rows, Gamma = inclusive cumsum of g inside
+// the chunk, S the state entering the chunk:
+//   A[r,s]  = beta_r sum_c k_rc k_sc e^{Gamma_rc - Gamma_sc}      s <  r
+//   M[r,s]  =        sum_c q_rc k_sc e^{Gamma_rc - Gamma_sc}      s <= r
+//   Tm      = (I + A)^-1 Diag(beta)
+//   W       = Tm (e^Gamma * K)          Ut = Tm V
+//   Q'      = scale (e^Gamma * Q - M W) Ot = scale M Ut
+//   U       = Ut - W S
+//   O       = Q' S + Ot                 (= scale (e^Gamma Q) S + scale M U)
+//   S      <- e^{Gamma_C} * S + (e^{Gamma_C - Gamma} * K)^T U
+// Everything that does not depend on S (A, M, Tm, W, Ut, Q', Ot) is built by
+// the intra-chunk kernel; the state pass only does three products per chunk.
+//
+// Rescaling (the point of the bounded decay): a tile of A or M whose rows
+// lie in 16-row sub-chunk a is a plain product of
+//   row operand  k_r (or q_r) * e^{Gamma_r - Gamma_p}   in [e^-80, 1]
+//   col operand  k_s         * e^{Gamma_p - Gamma_s}
+// with p = 16a - 1 (the row just before the sub-chunk).  For s in an
+// earlier sub-chunk the column factor is <= 1; in the same sub-chunk it is
+// <= e^80, inside the bf16 range (max e^88.7), so these operands are bf16.
+// Entries above the diagonal of the diagonal tiles are finite and are
+// discarded with a select.
+//
+// Precision policy with bf16 inputs (fp32 state, fp32 output):
+//   * A: bf16 operands.  M: bf16 operands off the block diagonal; on the
+//     diagonal tiles each operand is split into bf16 hi + lo and three
+//     products are summed (the diagonal term q_r.k_r dominates the output).
+//   * every other product uses fp16 operands (11-bit significand) with
+//     fp32 accumulation.  Quantities whose range is not bounded by the
+//     normalised inputs (V, Ut, S, U) are first scaled by a power of two
+//     chosen from their current maximum (exact), so fp16 never overflows.
+//   * Ut and Ot are kept in fp32.
+// With fp32 inputs every operand is fp32 (v_mfma_f32_16x16x4_f32).
+//
+// Workspace record per (b, h, chunk), every matrix stored as 16x16 tiles in
+// MFMA lane order (tile = 64 lanes x 4 consecutive values), so the state
+// pass reads each operand with one contiguous vector load per lane:
+//   W  : tile (ct, rt) lane l = W[16rt + l%16][16ct + 4(l/16) + i]     (Op)
+//   Q  : tile (ct, rt) lane l = Q'[16rt + l%16][16ct + 4(l/16) + i]    (Op)
+//   K  : tile (st, ct) lane l = Khat[16st + 4(l/16) + i][16ct + l%16]  (Op)
+//   dec: fp32 [dk] = e^{Gamma_C}
+//   U  : tile (st, jt) lane l = Ut[16st + 4(l/16) + i][16jt + l%16]    (fp32)
+//   O  : tile (rt, jt) lane l = Ot[16rt + 4(l/16) + i][16jt + l%16]    (fp32)
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+constexpr int kC = 64;   // chunk rows
+constexpr int kNW = 4;   // waves per intra-chunk work-group
+
+template <typename TIn> struct Policy;
+template <> struct Policy<float> {
+  using Op = float;
+  using Gram = float;
+  static constexpr bool kMixed = false;
+};
+template <> struct Policy<bf16> {
+  using Op = f16;
+  using Gram = bf16;
+  static constexpr bool kMixed = true;
+};
+
+template <typename TIn, int DK, int DV>
+struct Rec {
+  using Op = typename Policy<TIn>::Op;
+  static constexpr size_t W = 0;                               // Op elements
+  static constexpr size_t Q = (size_t)DK * kC;
+  static constexpr size_t K = 2 * (size_t)DK * kC;
+  static constexpr size_t DEC_OFF_BYTES = 3 * (size_t)DK * kC * sizeof(Op);
+  static constexpr size_t SHARED_BYTES = DEC_OFF_BYTES + 4 * (size_t)DK;   // staged in LDS
+  static constexpr size_t U_OFF_BYTES = SHARED_BYTES;                      // fp32 [C*DV]
+  static constexpr size_t O_OFF_BYTES = U_OFF_BYTES + 4 * (size_t)kC * DV; // fp32 [C*DV]
+  static constexpr size_t BYTES = (O_OFF_BYTES + 4 * (size_t)kC * DV + 255) / 256 * 256;
+  static_assert(SHARED_BYTES % 16 == 0, "record alignment");
+};
+
+typedef float raw16 __attribute__((ext_vector_type(4)));   // 16 raw bytes
+
+// Element x of 16 raw bytes holding values of type T, as fp32.
+template <typename T> __device__ __forceinline__ float raw_elem(raw16 v, int x);
+template <> __device__ __forceinline__ float raw_elem<float>(raw16 v, int x) { return v[x]; }
+template <> __device__ __forceinline__ float raw_elem<bf16>(raw16 v, int x) {
+  return (float)__builtin_bit_cast(bf16x8, v)[x];
+}
+
+// acc = sum over the first 16*n16 reduction indices of pa-row . pb-row
+// (both rows k-contiguous): the lower-triangular ranges of the chunk.
+template <typename T>
+__device__ __forceinline__ f32x4 tri_mma(const T* pa, const T* pb, int n16) {
+  f32x4 acc = zero4();
+  int k = 0;
+  for (; k + 2 <= n16; k += 2) acc = mma(load_slab(pa + 16 * k), load_slab(pb + 16 * k), acc);
+  if (k < n16) acc = mma(load_half(pa + 16 * k), load_half(pb + 16 * k), acc);
+  return acc;
+}
+
+// Right operand half slab read down a column of a row-major fp32 matrix:
+// lane (g, j) gets p[(4g + i) * ld + j], i = 0..3.
+__device__ __forceinline__ Half<float> load_half_col(const float* p, int ld) {
+  const int l = lane_id(), j = l & 15, g4 = 4 * (l >> 4);
+  return Half<float>{f32x4{p[(g4 + 0) * ld + j], p[(g4 + 1) * ld + j], p[(g4 + 2) * ld + j], p[(g4 + 3) * ld + j]}};
+}
+
+__device__ __forceinline__ float block_max(float x, float* sred) {
+  x = wave_max(x);
+  if ((threadIdx.x & 63) == 0) sred[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float m = sred[0];
+#pragma unroll
+  for (int i = 1; i < kNW; ++i) m = fmaxf(m, sred[i]);
+  __syncthreads();
+  return m;
+}
+
+// ---------------------------------------------------------------------------
+// Intra-chunk kernel: one work-group (4 waves) per (b*h, chunk).
+// LDS regions are reused across phases (lifetimes in brackets):
+//   G  : fp32 Gamma*log2(e) [C][DK+4]                          [all]
+//   R1 : k [C][DK] (in)  | Kbar^T [DK][C] (Op) | V^T [DV][C] (Op)
+//   X  : A, X fp32 [C][C+4] each | W^T [DK][C] (Op) | Ut^T [DV][C] (Op)
+//   R2 : q [C][DK] (in)  | M [C][C] (Op) + Tm [C][C] (Op)
+// ---------------------------------------------------------------------------
+template <typename TIn, int DK, int DV>
+struct IntraLds {
+  using Op = typename Policy<TIn>::Op;
+  static constexpr int PI = 16 / sizeof(TIn), PO = 16 / sizeof(Op);
+  static constexpr int LG = DK + 4;     // Gamma rows (fp32)
+  static constexpr int LK = DK + PI;    // k / q rows (input type)
+  static constexpr int LB = kC + PO;    // channel-major Op rows (Kbar^T, V^T, W^T, Ut^T) and M / Tm rows
+  static constexpr int LA = kC + 4;     // A / X rows (fp32)
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t G = 0;
+  static constexpr size_t R1 = G + (size_t)kC * LG * 4;
+  static constexpr size_t R1_SIZE = mx((size_t)kC * LK * sizeof(TIn), mx((size_t)DK, (size_t)DV) * LB * sizeof(Op));
+  static constexpr size_t X = R1 + R1_SIZE;
+  static constexpr size_t X_SIZE = mx(2 * (size_t)kC * LA * 4, mx((size_t)DK, (size_t)DV) * LB * sizeof(Op));
+  static constexpr size_t R2 = X + X_SIZE;
+  static constexpr size_t R2_SIZE = mx((size_t)kC * LK * sizeof(TIn), 2 * (size_t)kC * LB * sizeof(Op));
+  static constexpr size_t BETA = R2 + R2_SIZE;
+  static constexpr size_t RED = BETA + kC * 4;
+  static constexpr size_t BYTES = RED + 16 * 4;
+};
+
+// The 10 tiles (a, b) of the lower 4x4 block triangle: diagonal first.
+__constant__ signed char kTileA[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
+__constant__ signed char kTileB[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
+
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(256) void intra_chunk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                          const TIn* __restrict__ v, const TIn* __restrict__ g,
+                                                          const float* __restrict__ gcum,
+                                                          const TIn* __restrict__ beta, float scale,
+                                                          char* __restrict__ ws, int T_len, int H, int nchunks) {
+  using P = Policy<TIn>;
+  using Op = typename P::Op;
+  using Gm = typename P::Gram;
+  using L = IntraLds<TIn, DK, DV>;
+  using R = Rec<TIn, DK, DV>;
+  constexpr int VE = 16 / sizeof(TIn);   // input elements per 16-byte vector
+  constexpr int NQT = (DK / 16) * 4;     // Q'^T / W^T tiles
+  constexpr int NQW = NQT / kNW;         // ... per wave
+  __shared__ __align__(16) char smem[L::BYTES];
+  float* sG = reinterpret_cast<float*>(smem + L::G);
+  TIn* sK = reinterpret_cast<TIn*>(smem + L::R1);
+  Op* sKbt = reinterpret_cast<Op*>(smem + L::R1);
+  Op* sVt = reinterpret_cast<Op*>(smem + L::R1);
+  float* sA = reinterpret_cast<float*>(smem + L::X);
+  float* sX = sA + kC * L::LA;
+  Op* sWt = reinterpret_cast<Op*>(smem + L::X);
+  Op* sUt = reinterpret_cast<Op*>(smem + L::X);
+  TIn* sQ = reinterpret_cast<TIn*>(smem + L::R2);
+  Op* sM = reinterpret_cast<Op*>(smem + L::R2);
+  Op* sTm = sM + kC * L::LB;
+  float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
+  float* sRed = reinterpret_cast<float*>(smem + L::RED);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g4 = 4 * (lane >> 4);
+  const int ch = blockIdx.x % nchunks, bh = blockIdx.x / nchunks;
+  const int b = bh / H, h = bh % H;
+  const int t0 = ch * kC;
+  const int Lrows = min(kC, T_len - t0);
+  const size_t tokk = (size_t)H * DK, tokv = (size_t)H * DV;
+  const size_t base_k = ((size_t)b * T_len + t0) * tokk + (size_t)h * DK;
+  const size_t base_v = ((size_t)b * T_len + t0) * tokv + (size_t)h * DV;
+  char* rec = ws + ((size_t)bh * nchunks + ch) * R::BYTES;
+  Op* rW = reinterpret_cast<Op*>(rec) + R::W;
+  Op* rQ = reinterpret_cast<Op*>(rec) + R::Q;
+  Op* rK = reinterpret_cast<Op*>(rec) + R::K;
+  float* rDec = reinterpret_cast<float*>(rec + R::DEC_OFF_BYTES);
+  float* rU = reinterpret_cast<float*>(rec + R::U_OFF_BYTES);
+  float* rO = reinterpret_cast<float*>(rec + R::O_OFF_BYTES);
+  const raw16 zero16 = raw16{0.f, 0.f, 0.f, 0.f};
+
+  // ---- phase 0: stage k, q (rows >= Lrows are zero), beta, Gamma; v to registers
+  constexpr int NVK = kC * DK / VE;
+  for (int n = tid; n < NVK; n += 256) {
+    const int r = n / (DK / VE), c = (n % (DK / VE)) * VE;
+    raw16 kv = zero16, qv = zero16;
+    if (r < Lrows) {
+      kv = *reinterpret_cast<const raw16*>(k + base_k + r * tokk + c);
+      qv = *reinterpret_cast<const raw16*>(q + base_k + r * tokk + c);
+    }
+    *reinterpret_cast<raw16*>(sK + r * L::LK + c) = kv;
+    *reinterpret_cast<raw16*>(sQ + r * L::LK + c) = qv;
+  }
+  constexpr int NVV = kC * DV / VE;
+  constexpr int VPT = (NVV + 255) / 256;
+  raw16 vreg[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int n = tid + 256 * i;
+    const int r = n / (DV / VE), c = (n % (DV / VE)) * VE;
+    vreg[i] = (n < NVV && r < Lrows) ? *reinterpret_cast<const raw16*>(v + base_v + r * tokv + c) : zero16;
+  }
+  if (tid < kC) sBeta[tid] = tid < Lrows ? to_f32(beta[((size_t)b * T_len + t0 + tid) * H + h]) : 0.f;
+  if (gcum) {
+    for (int n = tid; n < kC * DK / 4; n += 256) {
+      const int r = n / (DK / 4), c = (n % (DK / 4)) * 4;
+      const int rr = min(r, Lrows - 1);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(gcum + base_k + rr * tokk + c);
+      *reinterpret_cast<f32x4*>(sG + r * L::LG + c) = gv * kLog2e;
+    }
+  } else if (tid < DK) {
+    float acc = 0.f;
+    for (int r = 0; r < kC; ++r) {
+      if (r < Lrows) acc += to_f32(g[base_k + r * tokk + tid]);
+      sG[r * L::LG + tid] = acc * kLog2e;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 1: Gram tiles (A -> LDS, M kept in registers), Khat, dec, Qbar
+  f32x4 mreg[3];
+  for (int ti = 0; ti < 3; ++ti) {
+    const int idx = w + kNW * ti;
+    if (idx >= 10) break;
+    const int a = kTileA[idx], bb = kTileB[idx];
+    const bool diag = a == bb;
+    const int p = 16 * a - 1;
+    const int r = 16 * a + l16, s = 16 * bb + l16;
+    f32x4 accA = zero4(), accM = zero4();
+#pragma unroll 2
+    for (int sl = 0; sl < DK / 32; ++sl) {
+      const int c0 = 32 * sl + g4, c1 = c0 + 16;
+      const f32x4 gp0 = p >= 0 ? *reinterpret_cast<const f32x4*>(sG + p * L::LG + c0) : zero4();
+      const f32x4 gp1 = p >= 0 ? *reinterpret_cast<const f32x4*>(sG + p * L::LG + c1) : zero4();
+      const f32x4 er0 = exp2v(*reinterpret_cast<const f32x4*>(sG + r * L::LG + c0) - gp0);
+      const f32x4 er1 = exp2v(*reinterpret_cast<const f32x4*>(sG + r * L::LG + c1) - gp1);
+      const f32x4 fs0 = exp2v(gp0 - *reinterpret_cast<const f32x4*>(sG + s * L::LG + c0));
+      const f32x4 fs1 = exp2v(gp1 - *reinterpret_cast<const f32x4*>(sG + s * L::LG + c1));
+      const f32x4 rk0 = widen4(load4(sK + r * L::LK + c0)) * er0, rk1 = widen4(load4(sK + r * L::LK + c1)) * er1;
+      const f32x4 rq0 = widen4(load4(sQ + r * L::LK + c0)) * er0, rq1 = widen4(load4(sQ + r * L::LK + c1)) * er1;
+      const f32x4 ck0 = widen4(load4(sK + s * L::LK + c0)) * fs0, ck1 = widen4(load4(sK + s * L::LK + c1)) * fs1;
+      const Slab<Gm> RK = make_slab<Gm>(rk0, rk1);
+      if (P::kMixed && diag) {
+        Slab<Gm> CKh, CKl, RQh, RQl;
+        make_slab_split<Gm>(ck0, ck1, CKh, CKl);
+        make_slab_split<Gm>(rq0, rq1, RQh, RQl);
+        accA = mma(CKh, RK, accA);
+        accM = mma(CKh, RQh, accM);
+        accM = mma(CKl, RQh, accM);
+        accM = mma(CKh, RQl, accM);
+      } else {
+        const Slab<Gm> CK = make_slab<Gm>(ck0, ck1);
+        accA = mma(CK, RK, accA);                         // A^T tile: lane holds A[r][16bb + g4 + i]
+        accM = mma(CK, make_slab<Gm>(rq0, rq1), accM);    // M^T tile: lane holds M[r][16bb + g4 + i]
+      }
+    }
+    const float br = sBeta[r];
+    f32x4 arow, mrow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sc = 16 * bb + g4 + i;
+      arow[i] = sc < r ? br * accA[i] : 0.f;
+      mrow[i] = sc <= r ? accM[i] : 0.f;
+    }
+    *reinterpret_cast<f32x4*>(sA + r * L::LA + 16 * bb + g4) = arow;
+    mreg[ti] = mrow;
+  }
+  // Khat tiles (st, ct) and dec
+  for (int n = tid; n < DK * 16; n += 256) {
+    const int tile = n >> 6, ln = n & 63;
+    const int st = tile / (DK / 16), ct = tile % (DK / 16);
+    const int col = 16 * ct + (ln & 15), row0 = 16 * st + 4 * (ln >> 4);
+    const float gC = sG[(kC - 1) * L::LG + col];
+    f32x4 val;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      val[i] = to_f32(sK[(row0 + i) * L::LK + col]) * exp2_fast(gC - sG[(row0 + i) * L::LG + col]);
+    store4<Op>(rK + tile * 256 + 4 * ln, narrow4<Op>(val));
+  }
+  if (tid < DK) rDec[tid] = exp2_fast(sG[(kC - 1) * L::LG + tid]);
+  // Qbar = e^Gamma q for this wave's Q'^T tiles (ct, rt): lane holds Qbar[16rt + l16][16ct + g4 + i]
+  f32x4 qbar[NQW];
+#pragma unroll
+  for (int j = 0; j < NQW; ++j) {
+    const int n = w + kNW * j, ct = n >> 2, rt = (n + ct) & 3;
+    const int row = 16 * rt + l16, col = 16 * ct + g4;
+    qbar[j] = widen4(load4(sQ + row * L::LK + col)) * exp2v(*reinterpret_cast<const f32x4*>(sG + row * L::LG + col));
+  }
+  __syncthreads();   // sQ is dead from here on; R2 becomes M + Tm
+
+  // M (Op) into R2, zero above the diagonal inside diagonal tiles
+  for (int ti = 0; ti < 3; ++ti) {
+    const int idx = w + kNW * ti;
+    if (idx >= 10) break;
+    const int a = kTileA[idx], bb = kTileB[idx];
+    store4<Op>(sM + (16 * a + l16) * L::LB + 16 * bb + g4, narrow4<Op>(mreg[ti]));
+  }
+
+  // ---- phase 2: X = (I + A)^-1 by 16x16 blocks, fp32
+  if (w == 0) {   // diagonal blocks by forward substitution; lane = (block, column)
+    const int a = lane >> 4, j = lane & 15;
+    const float* Ab = sA + 16 * a * L::LA + 16 * a;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) acc -= Ab[i * L::LA + m] * x[m];
+      x[i] = acc;
+    }
+    float* Xb = sX + 16 * a * L::LA + 16 * a;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Xb[i * L::LA + j] = x[i];
+  }
+  __syncthreads();
+  // off-diagonal blocks by distance d = a - b: X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb
+  for (int d = 1; d < 4; ++d) {
+    if (w < 4 - d) {
+      const int bb = w, a = w + d;
+      f32x4 y = zero4();
+      for (int c = bb; c < a; ++c)
+        y = mma(load_half(sA + (16 * a + l16) * L::LA + 16 * c), load_half_col(sX + 16 * c * L::LA + 16 * bb, L::LA), y);
+      const f32x4 xr = mma(load_half(sX + (16 * a + l16) * L::LA + 16 * a), Half<float>{y}, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sX[(16 * a + g4 + i) * L::LA + 16 * bb + l16] = -xr[i];
+    }
+    __syncthreads();
+  }
+  // Tm = X Diag(beta), lower triangle
+  for (int n = tid; n < kC * kC; n += 256) {
+    const int r = n >> 6, s = n & 63;
+    sTm[r * L::LB + s] = from_f32<Op>(s <= r ? sX[r * L::LA + s] * sBeta[s] : 0.f);
+  }
+
+  // ---- phase 3a: Kbar^T = (e^Gamma k)^T into R1 (through registers), then W^T
+  constexpr int NKB = kC * DK / 256;
+  Op kb[NKB];
+#pragma unroll
+  for (int i = 0; i < NKB; ++i) {
+    const int n = tid + 256 * i, s = n & 63, c = n >> 6;
+    kb[i] = from_f32<Op>(to_f32(sK[s * L::LK + c]) * exp2_fast(sG[s * L::LG + c]));
+  }
+  __syncthreads();   // sK and sX dead; sTm complete
+#pragma unroll
+  for (int i = 0; i < NKB; ++i) {
+    const int n = tid + 256 * i, s = n & 63, c = n >> 6;
+    sKbt[c * L::LB + s] = kb[i];
+  }
+  __syncthreads();
+  for (int n = w; n < NQT; n += kNW) {   // W^T tile (ct, rt)
+    const int ct = n >> 2, rt = (n + ct) & 3;
+    const f32x4 acc = tri_mma(sKbt + (16 * ct + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
+    store4<Op>(rW + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(acc));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sWt[(16 * ct + g4 + i) * L::LB + 16 * rt + l16] = from_f32<Op>(acc[i]);
+  }
+  __syncthreads();
+
+  // ---- phase 4a: Q'^T = scale (Qbar^T - W^T M^T)
+#pragma unroll
+  for (int j = 0; j < NQW; ++j) {
+    const int n = w + kNW * j, ct = n >> 2, rt = (n + ct) & 3;
+    const f32x4 mw = tri_mma(sWt + (16 * ct + l16) * L::LB, sM + (16 * rt + l16) * L::LB, rt + 1);
+    store4<Op>(rQ + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>((qbar[j] - mw) * scale));
+  }
+
+  // ---- phase 3b: V^T (range-scaled) into R1, then Ut = Tm V
+  float vmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+#pragma unroll
+    for (int x = 0; x < VE; ++x) vmax = fmaxf(vmax, fabsf(raw_elem<TIn>(vreg[i], x)));
+  const float sv = P::kMixed ? fp16_range_scale(block_max(vmax, sRed)) : 1.f;   // barriers inside
+  if (!P::kMixed) __syncthreads();   // R1 (Kbar^T) and X (W^T) readers done
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int n = tid + 256 * i;
+    if (n < NVV) {
+      const int r = n / (DV / VE), c = (n % (DV / VE)) * VE;
+#pragma unroll
+      for (int x = 0; x < VE; ++x) sVt[(c + x) * L::LB + r] = from_f32<Op>(raw_elem<TIn>(vreg[i], x) * sv);
+    }
+  }
+  __syncthreads();
+  constexpr int NUT = (DV / 16) * 4;
+  constexpr int NUW = NUT / kNW;
+  f32x4 ut[NUW];
+  float umax = 0.f;
+#pragma unroll
+  for (int j = 0; j < NUW; ++j) {   // Ut tile (st, jt)
+    const int n = w + kNW * j, jt = n >> 2, st = (n + jt) & 3;
+    ut[j] = tri_mma(sTm + (16 * st + l16) * L::LB, sVt + (16 * jt + l16) * L::LB, st + 1) * (1.f / sv);
+    *reinterpret_cast<f32x4*>(rU + (st * (DV / 16) + jt) * 256 + 4 * lane) = ut[j];
+    umax = fmaxf(umax, absmax4(ut[j]));
+  }
+  const float su = P::kMixed ? fp16_range_scale(block_max(umax, sRed)) : 1.f;   // X (W^T) readers done too
+  if (!P::kMixed) __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NUW; ++j) {   // Ut^T (range-scaled) into X
+    const int n = w + kNW * j, jt = n >> 2, st = (n + jt) & 3;
+    store4<Op>(sUt + (16 * jt + l16) * L::LB + 16 * st + g4, narrow4<Op>(ut[j] * su));
+  }
+  __syncthreads();
+
+  // ---- phase 4b: Ot = scale M Ut
+#pragma unroll
+  for (int j = 0; j < NUW; ++j) {   // Ot tile (rt, jt)
+    const int n = w + kNW * j, jt = n >> 2, rt = (n + jt) & 3;
+    const f32x4 acc = tri_mma(sM + (16 * rt + l16) * L::LB, sUt + (16 * jt + l16) * L::LB, rt + 1);
+    *reinterpret_cast<f32x4*>(rO + (rt * (DV / 16) + jt) * 256 + 4 * lane) = acc * (scale / su);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// State pass: one work-group per (b*h, 64 value columns); each of its 4
+// waves owns 16 value columns and keeps that dk x 16 slice of S in fp32
+// accumulators for the whole sequence.  The chunk's shared operands
+// (W, Q', Khat, dec) are staged once in LDS for the four waves; the next
+// chunk's copy is prefetched into registers during the current one.
+// ---------------------------------------------------------------------------
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(256) void state_pass_kernel(const char* __restrict__ ws, const float* __restrict__ h0,
+                                                         float* __restrict__ ht, float* __restrict__ o, int T_len,
+                                                         int H, int nchunks) {
+  using P = Policy<TIn>;
+  using Op = typename P::Op;
+  using R = Rec<TIn, DK, DV>;
+  constexpr int NCT = DK / 16;
+  constexpr int NV16 = R::SHARED_BYTES / 16;
+  constexpr int PPT = (NV16 + 255) / 256;
+  constexpr int NVB = DV / 64;   // value-column blocks per head
+  __shared__ __align__(16) char smem[R::SHARED_BYTES];
+  const Op* sW = reinterpret_cast<const Op*>(smem) + R::W;
+  const Op* sQ = reinterpret_cast<const Op*>(smem) + R::Q;
+  const Op* sK = reinterpret_cast<const Op*>(smem) + R::K;
+  const float* sDec = reinterpret_cast<const float*>(smem + R::DEC_OFF_BYTES);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g4 = 4 * (lane >> 4);
+  const int bh = blockIdx.x / NVB, b = bh / H, h = bh % H;
+  const int jt = (blockIdx.x % NVB) * 4 + w;
+  const int j = 16 * jt + l16;
+  const char* rec0 = ws + (size_t)bh * nchunks * R::BYTES;
+
+  f32x4 S[NCT];
+  const size_t sbase = (size_t)bh * DK * DV;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[ct][i] = h0 ? h0[sbase + (size_t)(16 * ct + g4 + i) * DV + j] : 0.f;
+
+  raw16 pre[PPT];
+  f32x4 preU[4], preO[4];
+  auto prefetch = [&](int c) {
+    const char* rec = rec0 + (size_t)c * R::BYTES;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int n = tid + 256 * i;
+      if (n < NV16) pre[i] = reinterpret_cast<const raw16*>(rec)[n];
+    }
+    const float* rU = reinterpret_cast<const float*>(rec + R::U_OFF_BYTES);
+    const float* rO = reinterpret_cast<const float*>(rec + R::O_OFF_BYTES);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      preU[t] = *reinterpret_cast<const f32x4*>(rU + (t * (DV / 16) + jt) * 256 + 4 * lane);
+      preO[t] = *reinterpret_cast<const f32x4*>(rO + (t * (DV / 16) + jt) * 256 + 4 * lane);
+    }
+  };
+  prefetch(0);
+
+  for (int c = 0; c < nchunks; ++c) {
+    __syncthreads();   // every wave is done with the previous chunk's LDS copy
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int n = tid + 256 * i;
+      if (n < NV16) reinterpret_cast<raw16*>(smem)[n] = pre[i];
+    }
+    f32x4 Ut[4], Ot[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      Ut[t] = preU[t];
+      Ot[t] = preO[t];
+    }
+    __syncthreads();
+    if (c + 1 < nchunks) prefetch(c + 1);
+
+    // S as an operand, range-scaled by a power of two
+    float smax = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) smax = fmaxf(smax, absmax4(S[ct]));
+    const float ss = P::kMixed ? fp16_range_scale(wave_max(smax)) : 1.f;
+    const float iss = 1.f / ss;
+    V4<Op> Sb[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) Sb[ct] = narrow4<Op>(S[ct] * ss);
+
+    // U = Ut - W S
+    f32x4 U[4];
+    float umax = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      f32x4 Pv = zero4();
+#pragma unroll
+      for (int sl = 0; sl < DK / 32; ++sl)
+        Pv = mma(slab_of<Op>(load4(sW + ((2 * sl) * 4 + st) * 256 + 4 * lane), load4(sW + ((2 * sl + 1) * 4 + st) * 256 + 4 * lane)),
+                 slab_of<Op>(Sb[2 * sl], Sb[2 * sl + 1]), Pv);
+      U[st] = Ut[st] - Pv * iss;
+      umax = fmaxf(umax, absmax4(U[st]));
+    }
+    const float us = P::kMixed ? fp16_range_scale(wave_max(umax)) : 1.f;
+    const float ius = 1.f / us;
+    V4<Op> Ub[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) Ub[st] = narrow4<Op>(U[st] * us);
+
+    // O = Q' S + Ot
+    const int t0 = c * kC;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int sl = 0; sl < DK / 32; ++sl)
+        acc = mma(slab_of<Op>(load4(sQ + ((2 * sl) * 4 + rt) * 256 + 4 * lane), load4(sQ + ((2 * sl + 1) * 4 + rt) * 256 + 4 * lane)),
+                  slab_of<Op>(Sb[2 * sl], Sb[2 * sl + 1]), acc);
+      acc = acc * iss + Ot[rt];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * rt + g4 + i;
+        if (t < T_len) o[(((size_t)b * T_len + t) * H + h) * DV + j] = acc[i];
+      }
+    }
+
+    // S <- e^{Gamma_C} S + Khat^T U
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+        acc = mma(slab_of<Op>(load4(sK + ((2 * sl) * NCT + ct) * 256 + 4 * lane), load4(sK + ((2 * sl + 1) * NCT + ct) * 256 + 4 * lane)),
+                  slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), acc);
+      S[ct] = S[ct] * d + acc * ius;
+    }
+  }
+
+  if (ht) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ht[sbase + (size_t)(16 * ct + g4 + i) * DV + j] = S[ct][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename TIn, int DK, int DV>
+static hipError_t go_fwd(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                         const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
+                         int H, void* ws, hipStream_t st) {
+  const int nchunks = (T_len + kC - 1) / kC;
+  const unsigned nbh = (unsigned)B * (unsigned)H;
+  hipLaunchKernelGGL((intra_chunk_kernel<TIn, DK, DV>), dim3(nchunks * nbh), dim3(256), 0, st, (const TIn*)q,
+                     (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, (char*)ws, T_len,
+                     H, nchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((state_pass_kernel<TIn, DK, DV>), dim3((DV / 64) * nbh), dim3(256), 0, st, (const char*)ws,
+                     h0, ht, o, T_len, H, nchunks);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+static size_t rec_bytes(int dk, int dv) {
+  if (dk == 128 && dv == 128) return Rec<TIn, 128, 128>::BYTES;
+  if (dk == 128 && dv == 64) return Rec<TIn, 128, 64>::BYTES;
+  if (dk == 64 && dv == 128) return Rec<TIn, 64, 128>::BYTES;
+  return Rec<TIn, 64, 64>::BYTES;
+}
+
+size_t fwd_record_bytes(int is_bf16, int dk, int dv) {
+  return is_bf16 ? rec_bytes<bf16>(dk, dv) : rec_bytes<float>(dk, dv);
+}
+
+template <typename TIn>
+static hipError_t dispatch_fwd(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                               const void* beta, float scale, const float* h0, float* ht, float* o, int B,
+                               int T_len, int H, int dk, int dv, void* ws, hipStream_t st) {
+  if (dk == 128 && dv == 128)
+    return go_fwd<TIn, 128, 128>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, st);
+  if (dk == 128 && dv == 64)
+    return go_fwd<TIn, 128, 64>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, st);
+  if (dk == 64 && dv == 128)
+    return go_fwd<TIn, 64, 128>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, st);
+  return go_fwd<TIn, 64, 64>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, st);
+}
+
+hipError_t launch_fwd_chunked(int is_bf16, const void* q, const void* k, const void* v, const void* g,
+                              const float* gcum, const void* beta, float scale, const float* h0, float* ht,
+                              float* o, int B, int T_len, int H, int dk, int dv, void* ws, hipStream_t st) {
+  if (is_bf16) return dispatch_fwd<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, st);
+  return dispatch_fwd<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, st);
+}
+
+}  // namespace kda

@@ -1,0 +1,29 @@
+// Internal host-side launch interface between the C ABI (kda_api.cpp) and
+// the kernel translation units.  Arguments are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Decay preparation: gate (z != nullptr) and/or chunk-local cumsum.
+hipError_t launch_prepare_decay(int is_bf16, const void* z, const float* A, float gmin, void* g,
+                                float* gcum, int B, int T, int H, int dk, int chunk,
+                                hipStream_t stream);
+
+// Bytes of one per-chunk record of the prefill workspace.
+size_t fwd_record_bytes(int is_bf16, int dk, int dv);
+
+// Chunked prefill: intra-chunk kernel then the sequential state pass.
+hipError_t launch_fwd_chunked(int is_bf16, const void* q, const void* k, const void* v,
+                              const void* g, const float* gcum, const void* beta, float scale,
+                              const float* h0, float* ht, float* o, int B, int T, int H, int dk,
+                              int dv, void* workspace, hipStream_t stream);
+
+// One decode token per (b, h), state updated in place.
+hipError_t launch_decode_step(int is_bf16, const void* q, const void* k, const void* v,
+                              const void* g, const void* beta, float scale, float* state, float* o,
+                              int B, int H, int dk, int dv, hipStream_t stream);
+
+}  // namespace kda

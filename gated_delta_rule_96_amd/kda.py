@@ -1,0 +1,171 @@
+"""Python binding of libkda.so: marshals torch device tensors into the C ABI
+declared in include/kda.h.  Every step of the computation runs in the HIP
+kernels; this module only checks tensor metadata, allocates outputs with
+torch (device memory plumbing) and passes pointers plus the current stream.
+
+Raises KDAError (with the library's status string) on any non-zero status,
+and RuntimeError if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+import torch
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libkda.so"
+
+KDA_F32, KDA_BF16 = 0, 1
+CHUNK = 64
+GMIN = -5.0
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() "
+                               "(python -m gated_delta_rule_96_amd.build) first")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.kda_abi_version.restype = I
+        L.kda_abi_version.argtypes = []
+        L.kda_status_str.restype = ctypes.c_char_p
+        L.kda_status_str.argtypes = [I]
+        L.kda_prepare_decay.restype = I
+        L.kda_prepare_decay.argtypes = [P, P, F, P, P, I, I, I, I, I, I, P]
+        L.kda_fwd_workspace_bytes.restype = S
+        L.kda_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.kda_fwd_chunked.restype = I
+        L.kda_fwd_chunked.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, P]
+        L.kda_decode_step.restype = I
+        L.kda_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, I, P]
+        _lib = L
+    return _lib
+
+
+def status_str(s: int) -> str:
+    return lib().kda_status_str(int(s)).decode()
+
+
+def abi_version() -> int:
+    return lib().kda_abi_version()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KDAError(status, where)
+
+
+def prepare_decay(z=None, A=None, g=None, *, want_g=True, want_gcum=True, gmin=GMIN, chunk=CHUNK):
+    """Gate mode: prepare_decay(z, A) -> (g, gcum); scan mode: prepare_decay(g=g) -> gcum.
+    z, g: [B, T, H, dk] (bf16 or fp32); A: [H] fp32."""
+    if z is not None:
+        B, T, H, dk = z.shape
+        dt = _dtype_code(z)
+        if A is None or A.dtype != torch.float32 or A.shape != (H,):
+            raise ValueError("A must be fp32 [H]")
+        g_out = torch.empty_like(z) if want_g else None
+        gcum = torch.empty(z.shape, dtype=torch.float32, device=z.device) if want_gcum else None
+        _check(lib().kda_prepare_decay(_ptr(z), _ptr(A), gmin, _ptr(g_out), _ptr(gcum), dt, B, T, H, dk, chunk,
+                                       _stream(z.device)), "kda_prepare_decay")
+        return g_out, gcum
+    if g is None:
+        raise ValueError("need z (gate mode) or g (scan mode)")
+    B, T, H, dk = g.shape
+    gcum = torch.empty(g.shape, dtype=torch.float32, device=g.device)
+    _check(lib().kda_prepare_decay(None, None, gmin, _ptr(g), _ptr(gcum), _dtype_code(g), B, T, H, dk, chunk,
+                                   _stream(g.device)), "kda_prepare_decay")
+    return gcum
+
+
+def fwd_workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16, chunk=CHUNK) -> int:
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(lib().kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, code))
+
+
+def alloc_workspace(B, T, H, dk, dv, dtype=torch.bfloat16, device="cuda", chunk=CHUNK) -> torch.Tensor:
+    n = fwd_workspace_bytes(B, T, H, dk, dv, dtype, chunk)
+    if n == 0:
+        raise ValueError("unsupported sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state=True, ht=None,
+                workspace=None, out=None, chunk=CHUNK):
+    """o, ht = fwd_chunked(q, k, v, g, beta, h0).  q,k,g [B,T,H,dk]; v [B,T,H,dv];
+    beta [B,T,H] (bf16 or fp32); h0/ht [B,H,dk,dv] fp32; o [B,T,H,dv] fp32.
+    ht may be h0 itself (in-place carry)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("beta", beta)) + ((("g", g),) if g is not None else ()):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if workspace is None:
+        workspace = alloc_workspace(B, T, H, dk, dv, q.dtype, q.device, chunk)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device) if out is None else out
+    if o.dtype != torch.float32 or o.shape != (B, T, H, dv):
+        raise ValueError("out must be fp32 [B, T, H, dv]")
+    if final_state and ht is None:
+        ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    for t in (h0, ht):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
+            raise ValueError("states must be fp32 [B, H, dk, dv]")
+    _check(lib().kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gcum), _ptr(beta), float(scale),
+                                 _ptr(h0), _ptr(ht if final_state else None), _ptr(o), dt, B, T, H, dk, dv,
+                                 chunk, _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "kda_fwd_chunked")
+    return o, (ht if final_state else None)
+
+
+def decode_step(q, k, v, g, beta, state, *, scale=None, out=None):
+    """o = decode_step(q, k, v, g, beta, state); state [B,H,dk,dv] fp32 is updated in place.
+    q,k,g [B,H,dk]; v [B,H,dv]; beta [B,H]; o [B,H,dv] fp32."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if state.dtype != torch.float32 or state.shape != (B, H, dk, dv):
+        raise ValueError("state must be fp32 [B, H, dk, dv]")
+    o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device) if out is None else out
+    if o.dtype != torch.float32 or o.shape != (B, H, dv):
+        raise ValueError("out must be fp32 [B, H, dv]")
+    _check(lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state),
+                                 _ptr(o), dt, B, H, dk, dv, _stream(q.device)), "kda_decode_step")
+    return o

@@ -1,0 +1,131 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) Kimi Delta Attention
+ * (KDA) forward library.
+ *
+ * The method (Kimi K3 technical report summary, page "Kimi K3 Technical
+ * Report - Open Frontier Intelligence"):
+ *   - "Key claims", section 2.1: KDA is the sequence mixer of a 3:1
+ *     KDA : Gated-MLA hybrid; it is a delta-rule attention with a fixed-size
+ *     per-head recurrent state and channel-wise decay.  Per head and token t,
+ *     with S in R^{dk x dv} (key channels as rows):
+ *         S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *         o_t = scale * S_t^T q_t              (scale is 1/sqrt(dk) in the model)
+ *   - "Key claims", section 2.1.1 and Fig. 3; "Method", section 2.1: the
+ *     log-decay is g = gmin * Sigmoid(exp(A) * z) with gmin = -5 and a
+ *     learnable per-head A.  The floor keeps the reciprocal rescaling
+ *     factors of the chunkwise form inside the bf16 range, so every causal
+ *     tile is a dense matrix product.
+ *   - "Method", section 2.1: the chunkwise-parallel form (prefill);
+ *     page "How a Frontier Model Gets Built, Read from the Kimi K3 Report",
+ *     "Technical Details": the fixed-size running state replaces the KV
+ *     cache (decode step, state carry between calls).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller,
+ *     contiguous row-major, 16-byte aligned.  Nothing is retained after the
+ *     call returns.  The library never allocates device memory and keeps no
+ *     mutable global state; calls are re-entrant.
+ *   - Layouts: q, k, g, z : [B, T, H, dk];  v, o : [B, T, H, dv];
+ *     beta : [B, T, H];  A : [H] (fp32);  states h0 / ht / state :
+ *     [B, H, dk, dv] fp32 (key channel = row, value channel = column).
+ *     Decode inputs drop the T axis: q, k, g : [B, H, dk]; v, o : [B, H, dv];
+ *     beta : [B, H].
+ *   - `dtype` (kda_dtype) is the element type of q, k, v, g, z and beta.
+ *     The output o, the states and gcum are always fp32 (the outputs of the
+ *     method have a heavy tail, max|o| of 10-20 times rms(o) on long
+ *     sequences, so a bf16 output alone would carry errors of several
+ *     percent of rms(o)).  Supported: dk, dv in {64, 128}; chunk == 64.
+ *     Any T >= 1 is accepted.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *     validates its arguments synchronously on the host; on any error
+ *     nothing is enqueued and no output is touched.  On success the work is
+ *     enqueued on `stream` and the call returns without synchronising.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - Return value: a kda_status code (0 = KDA_OK).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  KDA_ERR_SHAPE = 2,       /* a size is non-positive or too large                 */
+  KDA_ERR_DTYPE = 3,       /* dtype is not a kda_dtype value                      */
+  KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
+  KDA_ERR_UNSUPPORTED = 5, /* dk / dv / chunk outside the supported set           */
+  KDA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than kda_fwd_workspace_bytes */
+  KDA_ERR_RANGE = 7,       /* reserved: input value out of its documented range   */
+  KDA_ERR_HIP = 8          /* a HIP launch failed (hipGetLastError)               */
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Returns KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* kda_status_str(int status);
+
+/*
+ * Decay preparation ("Key claims", section 2.1.1; "Method", section 2.1).
+ *   z != NULL : gate mode.  g[b,t,h,c] = gmin * Sigmoid(exp(A[h]) * z[b,t,h,c])
+ *               computed in fp32 and rounded (RNE) to `dtype`; written to g
+ *               when g != NULL.  A must be non-NULL.
+ *   z == NULL : g is an input (A is ignored).
+ *   gcum != NULL : gcum[b,t,h,c] = inclusive sum of g over the rows of t's
+ *               chunk of `chunk` tokens up to t (the rounded g in gate mode),
+ *               accumulated in fp32.
+ * At least one output (g in gate mode, or gcum) must be requested.
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN,
+ *         KDA_ERR_UNSUPPORTED (dk, chunk), KDA_ERR_HIP.
+ */
+int kda_prepare_decay(const void* z, const float* A, float gmin, void* g, float* gcum,
+                      int dtype, int B, int T, int H, int dk, int chunk, void* stream);
+
+/* Bytes of device workspace kda_fwd_chunked needs for these sizes
+ * (0 if the sizes are invalid or unsupported). */
+size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
+
+/*
+ * Chunked prefill ("Method", section 2.1): o[b,t,h,:] = scale * S_t^T q_t
+ * for every token, with S_0 = h0[b,h] (zero state if h0 == NULL) and the
+ * recurrence above.  The final state S_T is written to ht when ht != NULL;
+ * ht may alias h0 (in-place carry from one segment of a sequence to the
+ * next).  g is the log-decay input; if gcum != NULL (fp32, from
+ * kda_prepare_decay with the same chunk) it is used instead and g may be
+ * NULL.  workspace (device, >= kda_fwd_workspace_bytes, 256-byte aligned)
+ * holds per-chunk intermediates; its contents on entry are ignored.
+ * Precondition, not checked: g in [gmin, 0] with gmin = -5.
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN,
+ *         KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP.
+ */
+int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g,
+                    const float* gcum, const void* beta, float scale, const float* h0,
+                    float* ht, float* o, int dtype, int B, int T, int H, int dk, int dv,
+                    int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode step (page "How a Frontier Model Gets Built...", "Technical
+ * Details": fixed-size running state instead of a KV cache): one new token
+ * per (b, h).  state [B,H,dk,dv] fp32 is read and overwritten in place with
+ * S_t; o[b,h,:] = scale * S_t^T q.
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN,
+ *         KDA_ERR_UNSUPPORTED, KDA_ERR_HIP.
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, float scale, float* state, float* o, int dtype,
+                    int B, int H, int dk, int dv, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,93 @@
+"""The C-ABI library loads and exports every symbol include/kda.h declares;
+argument validation rejects bad calls before anything is enqueued (these
+calls never reach a kernel launch, so they run without a GPU)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from gated_delta_rule_96_amd import kda
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+def declared_functions():
+    text = (ROOT / "include" / "kda.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("kda_prepare_decay", "kda_fwd_chunked", "kda_decode_step", "kda_fwd_workspace_bytes",
+              "kda_status_str", "kda_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = kda.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings():
+    assert kda.abi_version() == 1
+    for s in range(9):
+        assert kda.status_str(s)
+    assert "unknown" in kda.status_str(99)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gcum=None, beta=FAKE, scale=0.1, h0=None, ht=None, o=FAKE,
+             dtype=1, B=1, T=64, H=1, dk=128, dv=128, chunk=64, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return kda.lib().kda_fwd_chunked(a["q"], a["k"], a["v"], a["g"], a["gcum"], a["beta"], a["scale"], a["h0"],
+                                     a["ht"], a["o"], a["dtype"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                                     a["chunk"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(beta=None), 1), (dict(g=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(T=0), 2), (dict(H=-1), 2),
+    (dict(dtype=7), 3),
+    (dict(q=FAKE + 4), 4), (dict(h0=FAKE + 8), 4), (dict(ws=FAKE + 16), 4),
+    (dict(dk=96), 5), (dict(dv=32), 5), (dict(chunk=32), 5),
+    (dict(ws=None), 6), (dict(wsb=1024), 6),
+])
+def test_fwd_validation(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_workspace_bytes():
+    n = kda.fwd_workspace_bytes(1, 65536, 32, 128, 128)
+    assert n > 0 and n % 256 == 0
+    assert kda.fwd_workspace_bytes(1, 65, 1, 128, 128) == 2 * kda.fwd_workspace_bytes(1, 64, 1, 128, 128)
+    assert kda.lib().kda_fwd_workspace_bytes(1, 64, 1, 96, 128, 64, 1) == 0
+    assert kda.lib().kda_fwd_workspace_bytes(1, 64, 1, 128, 128, 32, 1) == 0
+
+
+def test_decode_validation():
+    L = kda.lib()
+    args = [FAKE] * 5 + [0.1, FAKE, FAKE, 1, 2, 2, 128, 128, None]
+    bad = list(args); bad[0] = None
+    assert L.kda_decode_step(*bad) == 1
+    bad = list(args); bad[11] = 32
+    assert L.kda_decode_step(*bad) == 5
+    bad = list(args); bad[6] = FAKE + 4
+    assert L.kda_decode_step(*bad) == 4
+    bad = list(args); bad[8] = 2
+    assert L.kda_decode_step(*bad) == 3
+
+
+def test_prepare_decay_validation():
+    L = kda.lib()
+    # gate mode without A, scan mode without gcum, unsupported chunk
+    assert L.kda_prepare_decay(FAKE, None, -5.0, FAKE, FAKE, 1, 1, 64, 1, 128, 64, None) == 1
+    assert L.kda_prepare_decay(None, None, -5.0, FAKE, None, 1, 1, 64, 1, 128, 64, None) == 1
+    assert L.kda_prepare_decay(None, None, -5.0, FAKE, FAKE, 1, 1, 64, 1, 128, 16, None) == 5
+    assert L.kda_prepare_decay(None, None, -5.0, FAKE, FAKE, 1, 0, 64, 1, 128, 64, None) == 2
