@@ -1,0 +1,231 @@
+"""Benchmark of the KDA forward hot path on one MI355X.
+
+Step = one KDA chunked prefill (decay scan, intra-chunk Gram/UT solve and
+state pass: kda_fwd_chunked) over the long-prefill workload
+B=1, H=32, T=65536, dk=dv=128, chunk 64, bf16 q/k/v/beta/g inputs, fp32
+initial/final state and fp32 output; the log-decay g is produced by the
+library's own gate (kda_prepare_decay) before timing.  Inputs are seeded
+synthetic data (gated_delta_rule_96_amd.synth), already resident in HBM when
+the timed region starts.
+
+Printed: ONE JSON line with the prefill tokens/s (value), the roofline of
+the prefill call (HBM-bound: algorithmic bytes / measured time), the MFMA
+fraction on the algorithmic flop count, per-kernel times (HIP events on the
+launch stream), the batched decode step (B=256, H=32, 1000 steps) against
+the HBM roofline, a parity check of the timed output against the CPU oracle
+on a sample, and the CPU oracle's own throughput (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+METRIC = "KDA chunked prefill tokens/s + % bf16 MFMA peak (T=64K); decode % HBM peak"
+
+# prefill workload
+B, H, T, DK, DV, CHUNK = 1, 32, 65536, 128, 128, 64
+# decode workload
+DB, DH, DSTEPS, DPOOL = 256, 32, 1000, 8
+
+
+def prefill_alg_counts(B, T, H, dk, dv, C=64):
+    """Algorithmic flop and HBM bytes of one prefill call (no dense upper-triangle
+    work, no intermediates): per token-head 6 dk dv + 1.25 C (3 dk + 2 dv) + C^2/3
+    flop; bytes = bf16 q, k, g, v, beta read, fp32 o written, fp32 h0 read and ht
+    written."""
+    th = B * T * H
+    flop = th * (6 * dk * dv + 1.25 * C * (3 * dk + 2 * dv) + C * C / 3.0)
+    bytes_ = th * (2 * (3 * dk + dv) + 2 + 4 * dv) + B * H * 2 * 4 * dk * dv
+    return flop, bytes_
+
+
+def decode_alg_bytes(B, H, dk, dv):
+    """fp32 state read + written, bf16 q, k, g, v, beta read, fp32 o written."""
+    return B * H * (2 * 4 * dk * dv + 2 * (3 * dk + dv) + 2 + 4 * dv)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=DSTEPS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards by "
+              "(batch, head) with no exchange, see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_96_amd import kda, synth
+
+    dev = torch.device("cuda:0")
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+
+    # ---------------- inputs (seeded, synthetic), resident in HBM
+    log(f"generating prefill inputs B={B} H={H} T={T} dk={DK} dv={DV}")
+    t_gen = time.time()
+    d = synth.make_inputs(B, T, H, DK, DV, seed=2)
+    bf = lambda x: torch.from_numpy(x).to(torch.bfloat16)
+    host = {n: bf(d[n]) for n in ("q", "k", "v", "beta", "z")}
+    q, k, v, beta, z = (host[n].to(dev) for n in ("q", "k", "v", "beta", "z"))
+    A = torch.from_numpy(d["A"].copy()).to(dev)
+    h0 = torch.from_numpy(d["h0"]).to(dev)
+    log(f"inputs ready in {time.time() - t_gen:.1f}s")
+    g, _ = kda.prepare_decay(z, A, want_gcum=False)
+    ws = kda.alloc_workspace(B, T, H, DK, DV, torch.bfloat16, dev)
+    o = torch.empty((B, T, H, DV), dtype=torch.float32, device=dev)
+    ht = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(stages=3):
+        kda.fwd_chunked(q, k, v, g, beta, h0, ht=ht, workspace=ws, out=o, stages=stages)
+
+    # ---------------- timed prefill
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"prefill: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f})")
+
+    # per-kernel split on the same stream (stage 1 = intra-chunk, stage 2 = state pass)
+    def time_stage(stages, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            step(stages)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n_k = max(3, args.steps // 2)
+    ms_intra = time_stage(1, n_k)
+    ms_state = time_stage(2, n_k)
+    step()
+    torch.cuda.synchronize()
+    log(f"intra-chunk {ms_intra:.3f} ms, state pass {ms_state:.3f} ms")
+
+    flop, abytes = prefill_alg_counts(B, T, H, DK, DV, CHUNK)
+    tok_s = B * T / (ms_step * 1e-3)
+    gbs = abytes / (ms_step * 1e-3) / 1e9
+    tflops = flop / (ms_step * 1e-3) / 1e12
+    bind_ms = max(flop / (BF16_PEAK_TFLOPS * 1e12), abytes / (HBM_PEAK_GBS * 1e9)) * 1e3
+
+    # ---------------- decode (B=256, H=32, fp32 state 512 MiB, 1000 steps)
+    decode = None
+    if not args.no_decode:
+        log(f"decode B={DB} H={DH} steps={args.decode_steps}")
+        st = torch.from_numpy(synth.initial_state(3, DB, DH, DK, DV)).to(dev)
+        pool = []
+        for s in range(DPOOL):
+            tk = synth.decode_tokens(DB, DH, DK, DV, seed=3, step=s)
+            tq, tkk, tv, tb, tz = (bf(tk[n]).to(dev) for n in ("q", "k", "v", "beta", "z"))
+            tg, _ = kda.prepare_decay(tz[:, None].contiguous(), torch.from_numpy(tk["A"]).to(dev), want_gcum=False)
+            pool.append((tq, tkk, tv, tg[:, 0].contiguous(), tb))
+        od = torch.empty((DB, DH, DV), dtype=torch.float32, device=dev)
+        for s in range(5):
+            kda.decode_step(*pool[s % DPOOL], st, out=od)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(args.decode_steps):
+            kda.decode_step(*pool[s % DPOOL], st, out=od)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        d_ms = e0.elapsed_time(e1) / args.decode_steps
+        d_bytes = decode_alg_bytes(DB, DH, DK, DV)
+        d_gbs = d_bytes / (d_ms * 1e-3) / 1e9
+        decode = {
+            "workload": f"KDA decode step B={DB} H={DH} dk=dv={DK}, fp32 state, {args.decode_steps} consecutive steps "
+                        f"(token inputs cycle through {DPOOL} seeded steps)",
+            "us_per_step": round(d_ms * 1e3, 2),
+            "tokens_per_s": round(DB / (d_ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(d_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "alg_bytes_per_step": d_bytes,
+        }
+        log(f"decode: {d_ms * 1e3:.1f} us/step, {d_gbs:.0f} GB/s")
+        del st, pool
+
+    # ---------------- parity of the timed output on a sample + CPU oracle baseline
+    parity = None
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import gate as ogate
+        from oracle import seq
+
+        Ts = T       # sample: the whole sequence, all heads
+        f = lambda t: t.float().numpy()
+        t_c0 = time.perf_counter()
+        gs = ogate.gate(f(host["z"][:, :Ts]), d["A"]).astype(np.float32)
+        g_ref = f(torch.from_numpy(gs).to(torch.bfloat16))
+        nthreads = seq.threads_default()
+        o_ref, _ = seq.kda_seq(f(host["q"][:, :Ts]), f(host["k"][:, :Ts]), f(host["v"][:, :Ts]), g_ref,
+                               f(host["beta"][:, :Ts]), d["h0"], nthreads=nthreads)
+        cpu_s = time.perf_counter() - t_c0
+        cpu = {"value": round(B * Ts / cpu_s, 1), "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+               "sample": f"fp64 sequential recurrence (+ fp64 gate) on the first {Ts} tokens of the same "
+                         f"B={B} H={H} workload, all heads; {cpu_s:.1f} s"}
+        o_gpu = o[:, :Ts].cpu().double().numpy()
+        rms = math.sqrt(float(np.mean(o_ref * o_ref)))
+        parity = {"sample": f"o[:, :{Ts}] all heads vs fp64 oracle (oracle uses its own gate on the same z)",
+                  "max_err_over_rms": float(np.max(np.abs(o_gpu - o_ref)) / rms), "tolerance": 2e-2}
+        log(f"cpu oracle {cpu['value']} tokens/s on {nthreads} threads; parity {parity['max_err_over_rms']:.2e}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
+                "g=-5*sigmoid(exp(A) z), z N(0,1), A U(-1,1), h0 N(0,0.02))",
+        "config": {"workload": f"KDA chunked prefill B={B} H={H} T={T} dk=dv={DK} chunk {CHUNK}, bf16 "
+                               f"q/k/v/beta/g inputs, fp32 state and output",
+                   "B": B, "H": H, "T": T, "dk": DK, "dv": DV, "chunk": CHUNK},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kda_fwd_chunked (intra_chunk_kernel + state_pass_kernel)",
+                     "alg_bytes_per_call": int(abytes)},
+        "mfma": {"achieved_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "alg_flop_per_call": int(flop)},
+        "binding_roofline_frac": round(bind_ms / ms_step, 4),
+        "kernels_ms": {"intra_chunk_kernel": round(ms_intra, 4), "state_pass_kernel": round(ms_state, 4)},
+        "decode": decode,
+        "parity": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -233,11 +233,26 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(const TIn* __restrict_
       const f32x4 gv = *reinterpret_cast<const f32x4*>(gcum + base_k + rr * tokk + c);
       *reinterpret_cast<f32x4*>(sG + r * L::LG + c) = gv * kLog2e;
     }
-  } else if (tid < DK) {
-    float acc = 0.f;
-    for (int r = 0; r < kC; ++r) {
-      if (r < Lrows) acc += to_f32(g[base_k + r * tokk + tid]);
-      sG[r * L::LG + tid] = acc * kLog2e;
+  } else {
+    // stage g (vector loads, rows >= Lrows are zero), then scan each channel
+    // from registers in row order
+    for (int n = tid; n < NVK; n += 256) {
+      const int r = n / (DK / VE), c = (n % (DK / VE)) * VE;
+      const raw16 gv = r < Lrows ? *reinterpret_cast<const raw16*>(g + base_k + r * tokk + c) : zero16;
+#pragma unroll
+      for (int x = 0; x < VE; ++x) sG[r * L::LG + c + x] = raw_elem<TIn>(gv, x);
+    }
+    __syncthreads();
+    if (tid < DK) {
+      float gr[kC];
+#pragma unroll
+      for (int r = 0; r < kC; ++r) gr[r] = sG[r * L::LG + tid];
+      float acc = 0.f;
+#pragma unroll
+      for (int r = 0; r < kC; ++r) {
+        acc += gr[r];
+        sG[r * L::LG + tid] = acc * kLog2e;
+      }
     }
   }
   __syncthreads();
@@ -580,17 +595,22 @@ __global__ __launch_bounds__(256) void state_pass_kernel(const char* __restrict_
 template <typename TIn, int DK, int DV>
 static hipError_t go_fwd(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                          const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                         int H, void* ws, hipStream_t st) {
+                         int H, void* ws, int stages, hipStream_t st) {
   const int nchunks = (T_len + kC - 1) / kC;
   const unsigned nbh = (unsigned)B * (unsigned)H;
-  hipLaunchKernelGGL((intra_chunk_kernel<TIn, DK, DV>), dim3(nchunks * nbh), dim3(256), 0, st, (const TIn*)q,
-                     (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, (char*)ws, T_len,
-                     H, nchunks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((state_pass_kernel<TIn, DK, DV>), dim3((DV / 64) * nbh), dim3(256), 0, st, (const char*)ws,
-                     h0, ht, o, T_len, H, nchunks);
-  return hipGetLastError();
+  if (stages & 1) {
+    hipLaunchKernelGGL((intra_chunk_kernel<TIn, DK, DV>), dim3(nchunks * nbh), dim3(256), 0, st, (const TIn*)q,
+                       (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, (char*)ws,
+                       T_len, H, nchunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & 2) {
+    hipLaunchKernelGGL((state_pass_kernel<TIn, DK, DV>), dim3((DV / 64) * nbh), dim3(256), 0, st,
+                       (const char*)ws, h0, ht, o, T_len, H, nchunks);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <typename TIn>
@@ -608,21 +628,23 @@ size_t fwd_record_bytes(int is_bf16, int dk, int dv) {
 template <typename TIn>
 static hipError_t dispatch_fwd(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                                const void* beta, float scale, const float* h0, float* ht, float* o, int B,
-                               int T_len, int H, int dk, int dv, void* ws, hipStream_t st) {
+                               int T_len, int H, int dk, int dv, void* ws, int stages, hipStream_t st) {
   if (dk == 128 && dv == 128)
-    return go_fwd<TIn, 128, 128>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, st);
+    return go_fwd<TIn, 128, 128>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
   if (dk == 128 && dv == 64)
-    return go_fwd<TIn, 128, 64>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, st);
+    return go_fwd<TIn, 128, 64>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
   if (dk == 64 && dv == 128)
-    return go_fwd<TIn, 64, 128>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, st);
-  return go_fwd<TIn, 64, 64>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, st);
+    return go_fwd<TIn, 64, 128>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
+  return go_fwd<TIn, 64, 64>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
 }
 
 hipError_t launch_fwd_chunked(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                               const float* gcum, const void* beta, float scale, const float* h0, float* ht,
-                              float* o, int B, int T_len, int H, int dk, int dv, void* ws, hipStream_t st) {
-  if (is_bf16) return dispatch_fwd<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, st);
-  return dispatch_fwd<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, st);
+                              float* o, int B, int T_len, int H, int dk, int dv, void* ws, int stages,
+                              hipStream_t st) {
+  if (is_bf16)
+    return dispatch_fwd<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, st);
+  return dispatch_fwd<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, st);
 }
 
 }  // namespace kda

@@ -19,7 +19,7 @@ size_t fwd_record_bytes(int is_bf16, int dk, int dv);
 hipError_t launch_fwd_chunked(int is_bf16, const void* q, const void* k, const void* v,
                               const void* g, const float* gcum, const void* beta, float scale,
                               const float* h0, float* ht, float* o, int B, int T, int H, int dk,
-                              int dv, void* workspace, hipStream_t stream);
+                              int dv, void* workspace, int stages, hipStream_t stream);
 
 // One decode token per (b, h), state updated in place.
 hipError_t launch_decode_step(int is_bf16, const void* q, const void* k, const void* v,

@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kda_fwd_chunked.restype = I
         L.kda_fwd_chunked.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, P]
+        L.kda_fwd_chunked_stages.restype = I
+        L.kda_fwd_chunked_stages.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, I, P]
         L.kda_decode_step.restype = I
         L.kda_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, I, P]
         _lib = L
@@ -124,7 +126,7 @@ def alloc_workspace(B, T, H, dk, dv, dtype=torch.bfloat16, device="cuda", chunk=
 
 
 def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state=True, ht=None,
-                workspace=None, out=None, chunk=CHUNK):
+                workspace=None, out=None, chunk=CHUNK, stages=3):
     """o, ht = fwd_chunked(q, k, v, g, beta, h0).  q,k,g [B,T,H,dk]; v [B,T,H,dv];
     beta [B,T,H] (bf16 or fp32); h0/ht [B,H,dk,dv] fp32; o [B,T,H,dv] fp32.
     ht may be h0 itself (in-place carry)."""
@@ -146,9 +148,10 @@ def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state
     for t in (h0, ht):
         if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
             raise ValueError("states must be fp32 [B, H, dk, dv]")
-    _check(lib().kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gcum), _ptr(beta), float(scale),
-                                 _ptr(h0), _ptr(ht if final_state else None), _ptr(o), dt, B, T, H, dk, dv,
-                                 chunk, _ptr(workspace), workspace.numel(), _stream(q.device)),
+    _check(lib().kda_fwd_chunked_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gcum), _ptr(beta),
+                                        float(scale), _ptr(h0), _ptr(ht if final_state else None), _ptr(o), dt,
+                                        B, T, H, dk, dv, chunk, _ptr(workspace), workspace.numel(), int(stages),
+                                        _stream(q.device)),
            "kda_fwd_chunked")
     return o, (ht if final_state else None)
 

@@ -36,7 +36,8 @@ VARIANTS = ("base", "extreme", "slow")
 
 
 def _rng(seed: int, part: int, tid: int, b: int = 0, h: int = 0) -> np.random.Generator:
-    return np.random.default_rng(np.random.SeedSequence([seed, part, tid, b, h]))
+    key = [seed, part, tid] + ([b, h] if b >= 0 else [])
+    return np.random.default_rng(np.random.SeedSequence(key))
 
 
 def _normal(seed, part, name, b, h, shape, mean=0.0, std=1.0) -> np.ndarray:
@@ -132,9 +133,20 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, seed: int, part: int =
 
 
 def decode_tokens(B: int, H: int, dk: int, dv: int, seed: int, step: int) -> dict:
-    """Inputs of one decode step (T = 1): same families as make_inputs, part = step."""
-    d = make_inputs(B, 1, H, dk, dv, seed, part=step, with_h0=False)
-    return {n: d[n][:, 0] for n in ("q", "k", "z", "v", "beta")} | {"A": d["A"]}
+    """Inputs of one decode step: q, k, z [B, H, dk], v [B, H, dv], beta [B, H]
+    (fp32) and A [H].  Same distributions as make_inputs; each tensor of a
+    step is one stream keyed by (seed, step, tensor), so a batch of 8192
+    sequences costs five draws per step."""
+    def nrm(name, shape):
+        return _rng(seed, step, TENSOR_ID[name], -1, -1).standard_normal(shape, dtype=np.float32)
+    return {
+        "q": _unit_rows(nrm("q", (B, H, dk))),
+        "k": _unit_rows(nrm("k", (B, H, dk))),
+        "z": nrm("z", (B, H, dk)),
+        "v": nrm("v", (B, H, dv)),
+        "beta": _logistic(nrm("beta", (B, H))),
+        "A": head_A(seed, H),
+    }
 
 
 def orthonormal_keys(seed: int, T: int, dk: int) -> np.ndarray:

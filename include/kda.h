@@ -113,6 +113,21 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g,
                     int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Same as kda_fwd_chunked, with the two device stages selectable: bit 0 =
+ * the intra-chunk stage (reads q, k, v, g/gcum, beta; writes workspace),
+ * bit 1 = the state pass (reads workspace, h0; writes o, ht).  stages == 3
+ * is kda_fwd_chunked.  Running stage 2 alone requires a workspace filled by
+ * stage 1 with the same sizes, inputs and scale.  For profiling each stage
+ * and for callers that schedule the stages on their own.
+ * Errors: as kda_fwd_chunked, plus KDA_ERR_SHAPE for stages outside 1..3.
+ */
+int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const void* g,
+                           const float* gcum, const void* beta, float scale, const float* h0,
+                           float* ht, float* o, int dtype, int B, int T, int H, int dk, int dv,
+                           int chunk, void* workspace, size_t workspace_bytes, int stages,
+                           void* stream);
+
+/*
  * Decode step (page "How a Frontier Model Gets Built...", "Technical
  * Details": fixed-size running state instead of a KV cache): one new token
  * per (b, h).  state [B,H,dk,dv] fp32 is read and overwritten in place with
