@@ -68,16 +68,25 @@ int kda_prepare_decay(const void* z, const float* A, float gmin, void* g, float*
 
 size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
   if (!valid_dtype(dtype) || B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) ||
-      chunk != kChunk)
+      chunk != kChunk || !size_ok(B, T, H, dk))
+    return 0;
+  return kda::fwd_fused_workspace_bytes(dtype == KDA_BF16, B * H, dk, dv);
+}
+
+size_t kda_fwd_stages_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+  if (!valid_dtype(dtype) || B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) ||
+      chunk != kChunk || !size_ok(B, T, H, dk))
     return 0;
   const size_t nchunks = ((size_t)T + kChunk - 1) / kChunk;
   return (size_t)B * (size_t)H * nchunks * kda::fwd_record_bytes(dtype == KDA_BF16, dk, dv);
 }
 
-int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const void* g, const float* gcum,
-                           const void* beta, float scale, const float* h0, float* ht, float* o, int dtype, int B,
-                           int T, int H, int dk, int dv, int chunk, void* workspace, size_t workspace_bytes,
-                           int stages, void* stream) {
+namespace {
+
+// Shared validation of the prefill calls; `stages` is 3 for kda_fwd_chunked.
+int check_fwd(const void* q, const void* k, const void* v, const void* g, const float* gcum, const void* beta,
+              const float* h0, const float* ht, const float* o, int dtype, int B, int T, int H, int dk, int dv,
+              int chunk, const void* workspace, int stages) {
   if (!valid_dtype(dtype)) return KDA_ERR_DTYPE;
   if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || dv <= 0 || chunk <= 0 || !size_ok(B, T, H, dk) ||
       !size_ok(B, T, H, dv) || (long long)B * H * ((T + kChunk - 1) / kChunk) > 2147483647LL || stages < 1 ||
@@ -87,21 +96,36 @@ int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const vo
   if ((stages & 1) && (!q || !k || !v || !beta || (!g && !gcum))) return KDA_ERR_NULL;
   if ((stages & 2) && !o) return KDA_ERR_NULL;
   if (!workspace) return KDA_ERR_WORKSPACE;
-  for (const void* p : {(const void*)q, k, v, beta, (const void*)g, (const void*)gcum, (const void*)h0,
-                        (const void*)ht, (const void*)o})
+  for (const void* p : {(const void*)q, k, v, beta, g, (const void*)gcum, (const void*)h0, (const void*)ht,
+                        (const void*)o})
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_ALIGN;
-  if (workspace_bytes < kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
-  hipError_t e = kda::launch_fwd_chunked(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk,
-                                         dv, workspace, stages, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return KDA_OK;
 }
+
+}  // namespace
 
 int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                     const void* beta, float scale, const float* h0, float* ht, float* o, int dtype, int B, int T,
                     int H, int dk, int dv, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
-  return kda_fwd_chunked_stages(q, k, v, g, gcum, beta, scale, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace,
-                                workspace_bytes, 3, stream);
+  const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace, 3);
+  if (st != KDA_OK) return st;
+  if (workspace_bytes < kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
+  hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
+                                       workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                           const void* beta, float scale, const float* h0, float* ht, float* o, int dtype, int B,
+                           int T, int H, int dk, int dv, int chunk, void* workspace, size_t workspace_bytes,
+                           int stages, void* stream) {
+  const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace, stages);
+  if (st != KDA_OK) return st;
+  if (workspace_bytes < kda_fwd_stages_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
+  hipError_t e = kda::launch_fwd_stages(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
+                                        workspace, stages, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,

@@ -157,12 +157,14 @@ struct IntraLds {
 __constant__ signed char kTileA[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
 __constant__ signed char kTileB[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
 
+// Builds the record of chunk `ch` of head (b, h) at `rec`.  Called by a
+// whole work-group of 256 threads; `smem` holds IntraLds::BYTES.
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void intra_chunk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                                          const TIn* __restrict__ v, const TIn* __restrict__ g,
-                                                          const float* __restrict__ gcum,
-                                                          const TIn* __restrict__ beta, float scale,
-                                                          char* __restrict__ ws, int T_len, int H, int nchunks) {
+__device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                              const TIn* __restrict__ v, const TIn* __restrict__ g,
+                                              const float* __restrict__ gcum, const TIn* __restrict__ beta,
+                                              float scale, int b, int h, int T_len, int H, int ch,
+                                              char* __restrict__ rec) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using Gm = typename P::Gram;
@@ -171,7 +173,6 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(const TIn* __restrict_
   constexpr int VE = 16 / sizeof(TIn);   // input elements per 16-byte vector
   constexpr int NQT = (DK / 16) * 4;     // Q'^T / W^T tiles
   constexpr int NQW = NQT / kNW;         // ... per wave
-  __shared__ __align__(16) char smem[L::BYTES];
   float* sG = reinterpret_cast<float*>(smem + L::G);
   TIn* sK = reinterpret_cast<TIn*>(smem + L::R1);
   Op* sKbt = reinterpret_cast<Op*>(smem + L::R1);
@@ -188,14 +189,12 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(const TIn* __restrict_
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g4 = 4 * (lane >> 4);
-  const int ch = blockIdx.x % nchunks, bh = blockIdx.x / nchunks;
-  const int b = bh / H, h = bh % H;
   const int t0 = ch * kC;
   const int Lrows = min(kC, T_len - t0);
   const size_t tokk = (size_t)H * DK, tokv = (size_t)H * DV;
   const size_t base_k = ((size_t)b * T_len + t0) * tokk + (size_t)h * DK;
   const size_t base_v = ((size_t)b * T_len + t0) * tokv + (size_t)h * DV;
-  char* rec = ws + ((size_t)bh * nchunks + ch) * R::BYTES;
+  __syncthreads();   // a previous call's LDS readers are done
   Op* rW = reinterpret_cast<Op*>(rec) + R::W;
   Op* rQ = reinterpret_cast<Op*>(rec) + R::Q;
   Op* rK = reinterpret_cast<Op*>(rec) + R::K;
@@ -451,39 +450,109 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(const TIn* __restrict_
   }
 }
 
+// Two-stage schedule, stage 1: one work-group per (b*h, chunk), records for
+// every chunk of every head in the workspace.
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(256) void intra_chunk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                          const TIn* __restrict__ v, const TIn* __restrict__ g,
+                                                          const float* __restrict__ gcum,
+                                                          const TIn* __restrict__ beta, float scale,
+                                                          char* __restrict__ ws, int T_len, int H, int nchunks) {
+  __shared__ __align__(16) char smem[IntraLds<TIn, DK, DV>::BYTES];
+  const int ch = blockIdx.x % nchunks, bh = blockIdx.x / nchunks;
+  produce_chunk<TIn, DK, DV>(smem, q, k, v, g, gcum, beta, scale, bh / H, bh % H, T_len, H, ch,
+                             ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES);
+}
+
 // ---------------------------------------------------------------------------
-// State pass: one work-group per (b*h, 64 value columns); each of its 4
-// waves owns 16 value columns and keeps that dk x 16 slice of S in fp32
-// accumulators for the whole sequence.  The chunk's shared operands
+// State pass over one head's chunks, 64 value columns (block vb): each of
+// the 4 waves owns 16 value columns and keeps that dk x 16 slice of S in
+// fp32 accumulators for the whole sequence.  The chunk's shared operands
 // (W, Q', Khat, dec) are staged once in LDS for the four waves; the next
 // chunk's copy is prefetched into registers during the current one.
+//
+// kRing = false: records of every chunk are stored one after another at
+//   recbase (two-stage schedule).
+// kRing = true : chunk c is in slot c % R of a ring at recbase, published by a
+//   producer work-group through ready[c % R] == c + 1; after the chunk has
+//   been read, done[0] = c + 1 hands the slot back.
 // ---------------------------------------------------------------------------
+struct Ring {
+  int* ready;   // this head's R slot flags
+  int* done;    // this consumer's progress counter
+  int* err;     // set on a wait that exceeded its bound
+  int R;
+};
+
+constexpr int kSpinLimit = 1 << 20;   // about a second of polling before giving up
+
+// Polls *p >= target.  Executed by every lane of one whole wave: all lanes
+// load the same word and the loop condition goes through readfirstlane, so
+// the loop is wave-uniform (no lane-divergent loop inside code that also
+// holds barriers).  Returns false after kSpinLimit polls, or as soon as
+// another work-group reported an error; sets *err on a timeout.
+__device__ __forceinline__ bool spin_until_geq(const int* p, int target, int* err) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (v >= target) return true;
+    const int e = __builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (e != 0) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void state_pass_kernel(const char* __restrict__ ws, const float* __restrict__ h0,
-                                                         float* __restrict__ ht, float* __restrict__ o, int T_len,
-                                                         int H, int nchunks) {
+struct ConsumerLds {
+  static constexpr size_t BYTES = Rec<TIn, DK, DV>::SHARED_BYTES + 16;   // + abort word
+};
+
+template <typename TIn, int DK, int DV, bool kRing>
+__device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
+                                              const float* __restrict__ h0, float* __restrict__ ht,
+                                              float* __restrict__ o, int b, int h, int T_len, int H,
+                                              int nchunks) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using R = Rec<TIn, DK, DV>;
   constexpr int NCT = DK / 16;
   constexpr int NV16 = R::SHARED_BYTES / 16;
   constexpr int PPT = (NV16 + 255) / 256;
-  constexpr int NVB = DV / 64;   // value-column blocks per head
-  __shared__ __align__(16) char smem[R::SHARED_BYTES];
   const Op* sW = reinterpret_cast<const Op*>(smem) + R::W;
   const Op* sQ = reinterpret_cast<const Op*>(smem) + R::Q;
   const Op* sK = reinterpret_cast<const Op*>(smem) + R::K;
   const float* sDec = reinterpret_cast<const float*>(smem + R::DEC_OFF_BYTES);
+  int* sAbort = reinterpret_cast<int*>(smem + R::SHARED_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g4 = 4 * (lane >> 4);
-  const int bh = blockIdx.x / NVB, b = bh / H, h = bh % H;
-  const int jt = (blockIdx.x % NVB) * 4 + w;
+  const int jt = vb * 4 + w;
   const int j = 16 * jt + l16;
-  const char* rec0 = ws + (size_t)bh * nchunks * R::BYTES;
+  const size_t bh = (size_t)b * H + h;
+  auto rec_of = [&](int c) { return recbase + (size_t)(kRing ? c % ring.R : c) * R::BYTES; };
+
+  // Ring: wait until chunk c is published; true = go on, false = abort.
+  // The verdict is read back with readfirstlane so that every branch and
+  // loop exit that depends on it is wave-uniform for the compiler: a
+  // lane-divergent exit from a loop that contains barriers lets the
+  // structurizer run the lane-0 block and the other lanes' next iteration in
+  // either order, which breaks the barrier protocol.
+  auto wait_ready = [&](int c) -> bool {
+    if (!kRing) return true;
+    if (w == 0) {   // wave 0 polls, uniformly
+      const bool ok = spin_until_geq(ring.ready + c % ring.R, c + 1, ring.err);
+      if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (lane == 0) *sAbort = ok ? 0 : 1;
+    }
+    __syncthreads();
+    const int abort_now = __builtin_amdgcn_readfirstlane(*sAbort);
+    __syncthreads();   // the word is rewritten by the next wait
+    return abort_now == 0;
+  };
 
   f32x4 S[NCT];
-  const size_t sbase = (size_t)bh * DK * DV;
+  const size_t sbase = bh * DK * DV;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -492,7 +561,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(const char* __restrict_
   raw16 pre[PPT];
   f32x4 preU[4], preO[4];
   auto prefetch = [&](int c) {
-    const char* rec = rec0 + (size_t)c * R::BYTES;
+    const char* rec = rec_of(c);
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int n = tid + 256 * i;
@@ -506,6 +575,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(const char* __restrict_
       preO[t] = *reinterpret_cast<const f32x4*>(rO + (t * (DV / 16) + jt) * 256 + 4 * lane);
     }
   };
+  if (!wait_ready(0)) return;
   prefetch(0);
 
   for (int c = 0; c < nchunks; ++c) {
@@ -522,7 +592,12 @@ __global__ __launch_bounds__(256) void state_pass_kernel(const char* __restrict_
       Ot[t] = preO[t];
     }
     __syncthreads();
-    if (c + 1 < nchunks) prefetch(c + 1);
+    // chunk c has been read completely: hand its slot back
+    if (kRing && tid == 0) __hip_atomic_store(ring.done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c + 1 < nchunks) {
+      if (!wait_ready(c + 1)) return;
+      prefetch(c + 1);
+    }
 
     // S as an operand, range-scaled by a power of two
     float smax = 0.f;
@@ -591,11 +666,170 @@ __global__ __launch_bounds__(256) void state_pass_kernel(const char* __restrict_
   }
 }
 
+// Two-stage schedule, stage 2: one work-group per (b*h, 64 value columns).
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(256) void state_pass_kernel(const char* __restrict__ ws, const float* __restrict__ h0,
+                                                         float* __restrict__ ht, float* __restrict__ o, int T_len,
+                                                         int H, int nchunks) {
+  __shared__ __align__(16) char smem[ConsumerLds<TIn, DK, DV>::BYTES];
+  constexpr int NVB = DV / 64;
+  const int bh = blockIdx.x / NVB;
+  consume_chain<TIn, DK, DV, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
+                                    Ring{nullptr, nullptr, nullptr, 1}, blockIdx.x % NVB, h0, ht, o, bh / H, bh % H,
+                                    T_len, H, nchunks);
+}
+
+// ---------------------------------------------------------------------------
+// Fused single-pass schedule: one persistent work-group per CU.  Heads are
+// dealt to the 8 XCDs (work-group i runs on XCD i % 8); on each XCD the
+// first work-groups are state-pass consumers (one per head and 64-column
+// block, resident for the whole call) and the rest are producers that take
+// (chunk, head) items of that XCD's heads in chunk-major order from a queue
+// and write each chunk's record into the head's ring of R slots.  Records
+// therefore live only in L2 / Infinity Cache between producer and consumer.
+// Ordering: producer stores, then an agent-scope release fence in every
+// wave, then ready[slot] = c + 1; the consumer polls ready, then an
+// agent-scope acquire fence, then reads.  A slot is reused only after every
+// consumer of the head stored done >= c + 1 for the chunk that held it.
+// Every wait is bounded (kSpinLimit); on a timeout the work-group sets the
+// error word and leaves, so the grid always drains.
+//
+// ctrl layout (ints, zeroed before the launch):
+//   [0..7]   per-XCD item counters      [8] error word
+//   [16 ..)  ready[nheads][R], then done[nheads][NVB]
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
-static hipError_t go_fwd(const void* q, const void* k, const void* v, const void* g, const float* gcum,
-                         const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                         int H, void* ws, int stages, hipStream_t st) {
+struct FusedLds {
+  static constexpr size_t A = IntraLds<TIn, DK, DV>::BYTES, B = ConsumerLds<TIn, DK, DV>::BYTES;
+  static constexpr size_t BYTES = (A > B ? A : B) + 16;
+};
+
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(256) void fused_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                        const TIn* __restrict__ v, const TIn* __restrict__ g,
+                                                        const float* __restrict__ gcum, const TIn* __restrict__ beta,
+                                                        float scale, const float* __restrict__ h0,
+                                                        float* __restrict__ ht, float* __restrict__ o, int T_len,
+                                                        int H, int nchunks, int head0, int nheads,
+                                                        char* __restrict__ ring, int* __restrict__ ctrl, int R) {
+  using Rc = Rec<TIn, DK, DV>;
+  constexpr int NVB = DV / 64;
+  __shared__ __align__(16) char smem[FusedLds<TIn, DK, DV>::BYTES];
+  int* sWord = reinterpret_cast<int*>(smem + FusedLds<TIn, DK, DV>::BYTES - 16);
+  const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
+  const int nloc = nheads > xcd ? (nheads - xcd + 7) / 8 : 0;   // heads j = xcd + 8m of this launch
+  int* err = ctrl + 8;
+  int* ready = ctrl + 16;
+  int* done = ready + nheads * R;
+
+  if (li < nloc * NVB) {   // consumer
+    const int m = li / NVB, vb = li % NVB, jh = xcd + 8 * m, bh = head0 + jh;
+    consume_chain<TIn, DK, DV, true>(smem, ring + (size_t)jh * R * Rc::BYTES,
+                                     Ring{ready + jh * R, done + jh * NVB + vb, err, R}, vb, h0, ht, o, bh / H,
+                                     bh % H, T_len, H, nchunks);
+    return;
+  }
+  // producer
+  const int total = nloc * nchunks;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (;;) {
+    if (w == 0) {   // wave 0 takes the next item and waits for its slot, uniformly
+      int it = 0;
+      if (lane == 0) it = __hip_atomic_fetch_add(ctrl + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      it = __builtin_amdgcn_readfirstlane(it);
+      if (it < total) {
+        const int c = it / nloc, jh = xcd + 8 * (it % nloc);
+        // the slot of chunk c held chunk c - R: wait until every consumer has read it
+        for (int vb = 0; vb < NVB && c >= R; ++vb)
+          if (!spin_until_geq(done + jh * NVB + vb, c - R + 1, err)) {
+            it = total;
+            break;
+          }
+      }
+      if (lane == 0) *sWord = it;
+    }
+    __syncthreads();
+    // wave-uniform copy (see consume_chain): the loop exit below must not be
+    // lane-divergent for the compiler, the loop body holds barriers
+    const int it = __builtin_amdgcn_readfirstlane(*sWord);
+    if (it >= total) return;
+    const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
+    produce_chunk<TIn, DK, DV>(smem, q, k, v, g, gcum, beta, scale, bh / H, bh % H, T_len, H, c,
+                               ring + ((size_t)jh * R + c % R) * Rc::BYTES);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (w == 0 && lane == 0)
+      __hip_atomic_store(ready + jh * R + c % R, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ void clear_ints_kernel(int* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+constexpr int kRingSlots = 4;         // ring slots per head (fused schedule)
+constexpr int kMaxWgPerXcd = 32;      // MI355X: 256 CUs in 8 XCDs
+
+// Heads one fused launch can serve with `per_xcd` work-groups per XCD:
+// keep at least a quarter of each XCD (and >= 2 work-groups) as producers.
+static int fused_heads_per_launch(int per_xcd, int nvb) {
+  const int prod = per_xcd / 4 > 2 ? per_xcd / 4 : 2;
+  const int hx = (per_xcd - prod) / nvb;
+  return hx > 0 ? 8 * hx : 0;
+}
+
+template <typename TIn, int DK, int DV>
+static size_t fused_ctrl_bytes(int nheads) {
+  return ((size_t)(16 + nheads * kRingSlots + nheads * (DV / 64)) * 4 + 255) / 256 * 256;
+}
+
+template <typename TIn, int DK, int DV>
+static size_t fused_ws_bytes(int nbh) {
+  const int cap = fused_heads_per_launch(kMaxWgPerXcd, DV / 64);
+  const int nh = nbh < cap ? nbh : cap;
+  return fused_ctrl_bytes<TIn, DK, DV>(nh) + (size_t)nh * kRingSlots * Rec<TIn, DK, DV>::BYTES;
+}
+
+template <typename TIn, int DK, int DV>
+static hipError_t go_fused(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                           const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
+                           int H, void* ws, size_t ws_bytes, hipStream_t st) {
+  const int nchunks = (T_len + kC - 1) / kC;
+  const int nbh = B * H;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  int per_xcd = cus / 8;
+  if (per_xcd > kMaxWgPerXcd) per_xcd = kMaxWgPerXcd;
+  int batch = fused_heads_per_launch(per_xcd, DV / 64);
+  if (batch <= 0) return hipErrorInvalidConfiguration;
+  // what the workspace can hold
+  while (batch > 0 && fused_ctrl_bytes<TIn, DK, DV>(batch) + (size_t)batch * kRingSlots * Rec<TIn, DK, DV>::BYTES > ws_bytes)
+    --batch;
+  if (batch <= 0) return hipErrorInvalidValue;
+  int* ctrl = reinterpret_cast<int*>(ws);
+  char* ring = reinterpret_cast<char*>(ws) + fused_ctrl_bytes<TIn, DK, DV>(batch);
+  for (int head0 = 0; head0 < nbh; head0 += batch) {
+    const int nh = nbh - head0 < batch ? nbh - head0 : batch;
+    const int nctrl = 16 + nh * kRingSlots + nh * (DV / 64);
+    hipLaunchKernelGGL(clear_ints_kernel, dim3((nctrl + 255) / 256), dim3(256), 0, st, ctrl, nctrl);
+    hipLaunchKernelGGL((fused_fwd_kernel<TIn, DK, DV>), dim3(8 * per_xcd), dim3(256), 0, st, (const TIn*)q,
+                       (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len,
+                       H, nchunks, head0, nh, ring, ctrl, kRingSlots);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename TIn, int DK, int DV>
+static hipError_t go_stages(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                            const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
+                            int H, void* ws, int stages, hipStream_t st) {
   const int nchunks = (T_len + kC - 1) / kC;
   const unsigned nbh = (unsigned)B * (unsigned)H;
   if (stages & 1) {
@@ -613,8 +847,18 @@ static hipError_t go_fwd(const void* q, const void* k, const void* v, const void
   return hipSuccess;
 }
 
+#define KDA_DISPATCH_D(FN, ...)                                   \
+  do {                                                            \
+    if (dk == 128 && dv == 128) return FN<TIn, 128, 128>(__VA_ARGS__); \
+    if (dk == 128 && dv == 64) return FN<TIn, 128, 64>(__VA_ARGS__);   \
+    if (dk == 64 && dv == 128) return FN<TIn, 64, 128>(__VA_ARGS__);   \
+    return FN<TIn, 64, 64>(__VA_ARGS__);                          \
+  } while (0)
+
 template <typename TIn>
-static size_t rec_bytes(int dk, int dv) {
+static size_t ws_fused_t(int nbh, int dk, int dv) { KDA_DISPATCH_D(fused_ws_bytes, nbh); }
+template <typename TIn>
+static size_t rec_bytes_t(int dk, int dv) {
   if (dk == 128 && dv == 128) return Rec<TIn, 128, 128>::BYTES;
   if (dk == 128 && dv == 64) return Rec<TIn, 128, 64>::BYTES;
   if (dk == 64 && dv == 128) return Rec<TIn, 64, 128>::BYTES;
@@ -622,29 +866,37 @@ static size_t rec_bytes(int dk, int dv) {
 }
 
 size_t fwd_record_bytes(int is_bf16, int dk, int dv) {
-  return is_bf16 ? rec_bytes<bf16>(dk, dv) : rec_bytes<float>(dk, dv);
+  return is_bf16 ? rec_bytes_t<bf16>(dk, dv) : rec_bytes_t<float>(dk, dv);
+}
+size_t fwd_fused_workspace_bytes(int is_bf16, int nbh, int dk, int dv) {
+  return is_bf16 ? ws_fused_t<bf16>(nbh, dk, dv) : ws_fused_t<float>(nbh, dk, dv);
 }
 
 template <typename TIn>
-static hipError_t dispatch_fwd(const void* q, const void* k, const void* v, const void* g, const float* gcum,
-                               const void* beta, float scale, const float* h0, float* ht, float* o, int B,
-                               int T_len, int H, int dk, int dv, void* ws, int stages, hipStream_t st) {
-  if (dk == 128 && dv == 128)
-    return go_fwd<TIn, 128, 128>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
-  if (dk == 128 && dv == 64)
-    return go_fwd<TIn, 128, 64>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
-  if (dk == 64 && dv == 128)
-    return go_fwd<TIn, 64, 128>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
-  return go_fwd<TIn, 64, 64>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
+static hipError_t fused_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                          const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
+                          int H, int dk, int dv, void* ws, size_t wsb, hipStream_t st) {
+  KDA_DISPATCH_D(go_fused, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, wsb, st);
+}
+template <typename TIn>
+static hipError_t stages_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                           const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
+                           int H, int dk, int dv, void* ws, int stages, hipStream_t st) {
+  KDA_DISPATCH_D(go_stages, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
 }
 
-hipError_t launch_fwd_chunked(int is_bf16, const void* q, const void* k, const void* v, const void* g,
-                              const float* gcum, const void* beta, float scale, const float* h0, float* ht,
-                              float* o, int B, int T_len, int H, int dk, int dv, void* ws, int stages,
-                              hipStream_t st) {
-  if (is_bf16)
-    return dispatch_fwd<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, st);
-  return dispatch_fwd<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, st);
+hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const void* v, const void* g,
+                            const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
+                            int B, int T_len, int H, int dk, int dv, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (is_bf16) return fused_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, st);
+  return fused_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, st);
+}
+
+hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,
+                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
+                             int B, int T_len, int H, int dk, int dv, void* ws, int stages, hipStream_t st) {
+  if (is_bf16) return stages_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, st);
+  return stages_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, st);
 }
 
 }  // namespace kda

@@ -14,12 +14,19 @@ hipError_t launch_prepare_decay(int is_bf16, const void* z, const float* A, floa
 
 // Bytes of one per-chunk record of the prefill workspace.
 size_t fwd_record_bytes(int is_bf16, int dk, int dv);
+// Workspace of the fused single-pass schedule (ring buffers + control words).
+size_t fwd_fused_workspace_bytes(int is_bf16, int nbh, int dk, int dv);
 
-// Chunked prefill: intra-chunk kernel then the sequential state pass.
-hipError_t launch_fwd_chunked(int is_bf16, const void* q, const void* k, const void* v,
-                              const void* g, const float* gcum, const void* beta, float scale,
-                              const float* h0, float* ht, float* o, int B, int T, int H, int dk,
-                              int dv, void* workspace, int stages, hipStream_t stream);
+// Chunked prefill, fused schedule (one persistent kernel per batch of heads).
+hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const void* v, const void* g,
+                            const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
+                            int B, int T, int H, int dk, int dv, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+// Chunked prefill, two-stage schedule: bit 0 intra-chunk kernel, bit 1 state pass.
+hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,
+                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
+                             int B, int T, int H, int dk, int dv, void* workspace, int stages, hipStream_t stream);
 
 // One decode token per (b, h), state updated in place.
 hipError_t launch_decode_step(int is_bf16, const void* q, const void* k, const void* v,

@@ -46,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L.kda_prepare_decay.argtypes = [P, P, F, P, P, I, I, I, I, I, I, P]
         L.kda_fwd_workspace_bytes.restype = S
         L.kda_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.kda_fwd_stages_workspace_bytes.restype = S
+        L.kda_fwd_stages_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kda_fwd_chunked.restype = I
         L.kda_fwd_chunked.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, P]
         L.kda_fwd_chunked_stages.restype = I
@@ -113,23 +115,33 @@ def prepare_decay(z=None, A=None, g=None, *, want_g=True, want_gcum=True, gmin=G
     return gcum
 
 
-def fwd_workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16, chunk=CHUNK) -> int:
+def fwd_workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16, chunk=CHUNK, stages=False) -> int:
+    """Workspace bytes of kda_fwd_chunked (stages=False) or kda_fwd_chunked_stages."""
     code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
-    return int(lib().kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, code))
+    f = lib().kda_fwd_stages_workspace_bytes if stages else lib().kda_fwd_workspace_bytes
+    return int(f(B, T, H, dk, dv, chunk, code))
 
 
-def alloc_workspace(B, T, H, dk, dv, dtype=torch.bfloat16, device="cuda", chunk=CHUNK) -> torch.Tensor:
-    n = fwd_workspace_bytes(B, T, H, dk, dv, dtype, chunk)
+def alloc_workspace(B, T, H, dk, dv, dtype=torch.bfloat16, device="cuda", chunk=CHUNK, stages=False) -> torch.Tensor:
+    n = fwd_workspace_bytes(B, T, H, dk, dv, dtype, chunk, stages)
     if n == 0:
         raise ValueError("unsupported sizes")
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def workspace_error(workspace: torch.Tensor) -> int:
+    """Error word of a kda_fwd_chunked workspace (non-zero: a hand-off wait
+    timed out and the outputs are incomplete).  Synchronises the stream."""
+    return int(workspace[32:36].view(torch.int32).item())
+
+
 def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state=True, ht=None,
-                workspace=None, out=None, chunk=CHUNK, stages=3):
+                workspace=None, out=None, chunk=CHUNK, stages=None):
     """o, ht = fwd_chunked(q, k, v, g, beta, h0).  q,k,g [B,T,H,dk]; v [B,T,H,dv];
     beta [B,T,H] (bf16 or fp32); h0/ht [B,H,dk,dv] fp32; o [B,T,H,dv] fp32.
-    ht may be h0 itself (in-place carry)."""
+    ht may be h0 itself (in-place carry).  stages=None runs the fused
+    single-pass schedule (kda_fwd_chunked); stages in {1, 2, 3} runs the
+    two-kernel schedule (kda_fwd_chunked_stages) with that stage mask."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q)
@@ -139,7 +151,7 @@ def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state
     if scale is None:
         scale = 1.0 / math.sqrt(dk)
     if workspace is None:
-        workspace = alloc_workspace(B, T, H, dk, dv, q.dtype, q.device, chunk)
+        workspace = alloc_workspace(B, T, H, dk, dv, q.dtype, q.device, chunk, stages is not None)
     o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device) if out is None else out
     if o.dtype != torch.float32 or o.shape != (B, T, H, dv):
         raise ValueError("out must be fp32 [B, T, H, dv]")
@@ -148,11 +160,13 @@ def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state
     for t in (h0, ht):
         if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
             raise ValueError("states must be fp32 [B, H, dk, dv]")
-    _check(lib().kda_fwd_chunked_stages(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gcum), _ptr(beta),
-                                        float(scale), _ptr(h0), _ptr(ht if final_state else None), _ptr(o), dt,
-                                        B, T, H, dk, dv, chunk, _ptr(workspace), workspace.numel(), int(stages),
-                                        _stream(q.device)),
-           "kda_fwd_chunked")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gcum), _ptr(beta), float(scale), _ptr(h0),
+            _ptr(ht if final_state else None), _ptr(o), dt, B, T, H, dk, dv, chunk, _ptr(workspace),
+            workspace.numel())
+    if stages is None:
+        _check(lib().kda_fwd_chunked(*args, _stream(q.device)), "kda_fwd_chunked")
+    else:
+        _check(lib().kda_fwd_chunked_stages(*args, int(stages), _stream(q.device)), "kda_fwd_chunked_stages")
     return o, (ht if final_state else None)
 
 

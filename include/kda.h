@@ -90,9 +90,15 @@ const char* kda_status_str(int status);
 int kda_prepare_decay(const void* z, const float* A, float gmin, void* g, float* gcum,
                       int dtype, int B, int T, int H, int dk, int chunk, void* stream);
 
-/* Bytes of device workspace kda_fwd_chunked needs for these sizes
- * (0 if the sizes are invalid or unsupported). */
+/* Bytes of device workspace kda_fwd_chunked needs for these sizes (0 if
+ * the sizes are invalid or unsupported): ring buffers of a few chunk
+ * records per head for at most one launch's batch of heads plus control
+ * words, independent of T (about 45 MiB at B*H >= 84, dk = dv = 128, bf16). */
 size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
+
+/* Bytes of device workspace kda_fwd_chunked_stages needs: one record per
+ * (b, h, chunk), i.e. proportional to B*H*T (0 if invalid). */
+size_t kda_fwd_stages_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
 
 /*
  * Chunked prefill ("Method", section 2.1): o[b,t,h,:] = scale * S_t^T q_t
@@ -102,7 +108,15 @@ size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, i
  * next).  g is the log-decay input; if gcum != NULL (fp32, from
  * kda_prepare_decay with the same chunk) it is used instead and g may be
  * NULL.  workspace (device, >= kda_fwd_workspace_bytes, 256-byte aligned)
- * holds per-chunk intermediates; its contents on entry are ignored.
+ * holds per-chunk intermediates in flight; its contents on entry are
+ * ignored.  Calls that share one workspace must not overlap on the device
+ * (one stream, or synchronised streams).  Schedule: one persistent kernel
+ * per batch of heads, whose work-groups hand chunk records from producers
+ * to the state pass through the workspace; the kernel needs every one of
+ * its work-groups resident at once (one per CU), so it must not share the
+ * GPU with other work that holds CUs for long; if a hand-off wait exceeds
+ * its bound (about a second) the kernel stops early and sets the first error word
+ * of the workspace (ints [8]), leaving the outputs incomplete.
  * Precondition, not checked: g in [gmin, 0] with gmin = -5.
  * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN,
  *         KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP.
@@ -113,12 +127,15 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g,
                     int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Same as kda_fwd_chunked, with the two device stages selectable: bit 0 =
- * the intra-chunk stage (reads q, k, v, g/gcum, beta; writes workspace),
- * bit 1 = the state pass (reads workspace, h0; writes o, ht).  stages == 3
- * is kda_fwd_chunked.  Running stage 2 alone requires a workspace filled by
- * stage 1 with the same sizes, inputs and scale.  For profiling each stage
- * and for callers that schedule the stages on their own.
+ * The same computation as kda_fwd_chunked on a two-kernel schedule with
+ * every chunk record stored in the workspace (>= kda_fwd_stages_workspace_bytes):
+ * bit 0 of `stages` = the intra-chunk kernel (reads q, k, v, g/gcum, beta;
+ * writes the workspace), bit 1 = the state pass (reads the workspace and h0;
+ * writes o and ht).  Running stage 2 alone requires a workspace filled by
+ * stage 1 with the same sizes, inputs and scale.  No inter-work-group
+ * waits; for profiling each stage and for callers that schedule the stages
+ * themselves.  Same results as kda_fwd_chunked up to nothing: both
+ * schedules run the same per-chunk arithmetic.
  * Errors: as kda_fwd_chunked, plus KDA_ERR_SHAPE for stages outside 1..3.
  */
 int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const void* g,

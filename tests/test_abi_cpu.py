@@ -21,7 +21,7 @@ def declared_functions():
 def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("kda_prepare_decay", "kda_fwd_chunked", "kda_decode_step", "kda_fwd_workspace_bytes",
-              "kda_status_str", "kda_abi_version"):
+              "kda_fwd_chunked_stages", "kda_fwd_stages_workspace_bytes", "kda_status_str", "kda_abi_version"):
         assert n in names
 
 
@@ -66,9 +66,16 @@ def test_fwd_validation(kw, code):
 def test_workspace_bytes():
     n = kda.fwd_workspace_bytes(1, 65536, 32, 128, 128)
     assert n > 0 and n % 256 == 0
-    assert kda.fwd_workspace_bytes(1, 65, 1, 128, 128) == 2 * kda.fwd_workspace_bytes(1, 64, 1, 128, 128)
-    assert kda.lib().kda_fwd_workspace_bytes(1, 64, 1, 96, 128, 64, 1) == 0
-    assert kda.lib().kda_fwd_workspace_bytes(1, 64, 1, 128, 128, 32, 1) == 0
+    # fused schedule: ring buffers, independent of T, capped at one launch's heads
+    assert kda.fwd_workspace_bytes(1, 65536, 32, 128, 128) == kda.fwd_workspace_bytes(1, 64, 32, 128, 128)
+    assert kda.fwd_workspace_bytes(8, 64, 64, 128, 128) == kda.fwd_workspace_bytes(4, 64, 64, 128, 128)
+    assert n < 64 << 20
+    # two-stage schedule: one record per chunk
+    s = lambda T: kda.fwd_workspace_bytes(1, T, 1, 128, 128, stages=True)
+    assert s(65) == 2 * s(64) and s(64) % 256 == 0
+    for f in (kda.lib().kda_fwd_workspace_bytes, kda.lib().kda_fwd_stages_workspace_bytes):
+        assert f(1, 64, 1, 96, 128, 64, 1) == 0
+        assert f(1, 64, 1, 128, 128, 32, 1) == 0
 
 
 def test_decode_validation():

@@ -213,3 +213,30 @@ def test_fwd_is_deterministic():
     r2 = kda.fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"])
     torch.cuda.synchronize()
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
+def test_fused_and_two_stage_schedules_agree_bitwise():
+    say("fused vs two-stage schedule")
+    d = to_dev(prefill_case(2, 333, 3, 128, 128, seed=14, dtype=torch.bfloat16))
+    o1, h1 = kda.fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"])
+    o2, h2 = kda.fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], stages=3)
+    ws = kda.alloc_workspace(2, 333, 3, 128, 128, torch.bfloat16, "cuda", stages=True)
+    kda.fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], stages=1, workspace=ws)
+    o3, h3 = kda.fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], stages=2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    assert torch.equal(o1, o3) and torch.equal(h1, h3)
+
+
+@pytest.mark.parametrize("B,H", [(2, 64), (1, 3), (3, 1)])
+def test_fused_head_batching(B, H):
+    """More heads than one persistent launch serves (B*H = 128 > 96), and
+    fewer heads than XCDs."""
+    say(f"fused head batching B={B} H={H}")
+    c = prefill_case(B, 130, H, 128, 128, seed=15, dtype=torch.bfloat16)
+    d = to_dev(c)
+    ws = kda.alloc_workspace(B, 130, H, 128, 128, torch.bfloat16, "cuda")
+    o, ht = kda.fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], workspace=ws)
+    assert kda.workspace_error(ws) == 0
+    o_ref, h_ref = _oracle(c, c["h0"])
+    assert err_ratio(f32(o), o_ref) <= 2e-2 and err_ratio(ht.cpu().numpy(), h_ref) <= 2e-2
