@@ -1,6 +1,6 @@
 // Chunked KDA prefill on gfx950: an intra-chunk kernel (parallel over every
 // chunk of every head) followed by a state pass (sequential over chunks,
-// parallel over heads and value-column blocks).
+// parallel over heads), or both fused into one persistent kernel.
 //
 // Method (Kimi K3 technical report summary, page "Kimi K3 Technical Report -
 // Open Frontier Intelligence"): "Key claims" section 2.1 (delta-rule state
@@ -58,7 +58,8 @@
 namespace kda {
 
 constexpr int kC = 64;   // chunk rows
-constexpr int kNW = 4;   // waves per intra-chunk work-group
+constexpr int kNW = 8;                // waves per work-group (every kernel here)
+constexpr int kThreads = 64 * kNW;
 
 template <typename TIn> struct Policy;
 template <> struct Policy<float> {
@@ -124,8 +125,66 @@ __device__ __forceinline__ float block_max(float x, float* sred) {
   return m;
 }
 
+// Tiles (x, r) of a 64-row x (16 * nx) output split over the 8 waves, j-th
+// tile of wave w: with 4 tiles per wave, wave w takes column-tile x = w and
+// every row block r; with 2, the pairs of row blocks {0,3} and {1,2}.  The
+// lower-triangular products cost r + 1 units, so every wave gets the same.
+__device__ __forceinline__ void wave_tile(int w, int j, int per_wave, int& x, int& r) {
+  if (per_wave == 4) {
+    x = w;
+    r = j;
+  } else {
+    x = w >> 1;
+    r = (w & 1) ? 1 + j : (j ? 3 : 0);
+  }
+}
+
+// One chunk's raw inputs in registers (rows past the end of the sequence
+// are zero): 16-byte vectors of k, q, g and v rows, and beta.
+template <typename TIn, int DK, int DV>
+struct InRegs {
+  static constexpr int VE = 16 / sizeof(TIn);
+  static constexpr int NK = kC * DK / VE / kThreads;
+  static constexpr int NV = kC * DV / VE / kThreads;
+  static_assert(NK * kThreads * VE == kC * DK && NV * kThreads * VE == kC * DV, "shape");
+  raw16 k[NK], q[NK], g[NK], v[NV];
+  float beta;
+};
+
+template <typename TIn, int DK, int DV>
+__device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* __restrict__ q,
+                                            const TIn* __restrict__ k, const TIn* __restrict__ v,
+                                            const TIn* __restrict__ g, const TIn* __restrict__ beta, int b, int h,
+                                            int T_len, int H, int ch) {
+  using IR = InRegs<TIn, DK, DV>;
+  constexpr int VE = IR::VE;
+  const int tid = threadIdx.x;
+  const int t0 = ch * kC;
+  const int Lrows = min(kC, T_len - t0);
+  const size_t tokk = (size_t)H * DK, tokv = (size_t)H * DV;
+  const size_t base_k = ((size_t)b * T_len + t0) * tokk + (size_t)h * DK;
+  const size_t base_v = ((size_t)b * T_len + t0) * tokv + (size_t)h * DV;
+  const raw16 zero16 = raw16{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < IR::NK; ++i) {
+    const int n = tid + kThreads * i;
+    const int r = n / (DK / VE), c = (n % (DK / VE)) * VE;
+    const bool ok = r < Lrows;
+    in.k[i] = ok ? *reinterpret_cast<const raw16*>(k + base_k + r * tokk + c) : zero16;
+    in.q[i] = ok ? *reinterpret_cast<const raw16*>(q + base_k + r * tokk + c) : zero16;
+    in.g[i] = (ok && g) ? *reinterpret_cast<const raw16*>(g + base_k + r * tokk + c) : zero16;
+  }
+#pragma unroll
+  for (int i = 0; i < IR::NV; ++i) {
+    const int n = tid + kThreads * i;
+    const int r = n / (DV / VE), c = (n % (DV / VE)) * VE;
+    in.v[i] = r < Lrows ? *reinterpret_cast<const raw16*>(v + base_v + r * tokv + c) : zero16;
+  }
+  in.beta = (tid < kC && tid < Lrows) ? to_f32(beta[((size_t)b * T_len + t0 + tid) * H + h]) : 0.f;
+}
+
 // ---------------------------------------------------------------------------
-// Intra-chunk kernel: one work-group (4 waves) per (b*h, chunk).
+// Intra-chunk kernel: one work-group (8 waves) per (b*h, chunk).
 // LDS regions are reused across phases (lifetimes in brackets):
 //   G  : fp32 Gamma*log2(e) [C][DK+4]                          [all]
 //   R1 : k [C][DK] (in)  | Kbar^T [DK][C] (Op) | V^T [DV][C] (Op)
@@ -158,13 +217,14 @@ __constant__ signed char kTileA[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
 __constant__ signed char kTileB[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
 
 // Builds the record of chunk `ch` of head (b, h) at `rec`.  Called by a
-// whole work-group of 256 threads; `smem` holds IntraLds::BYTES.
-template <typename TIn, int DK, int DV>
-__device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                              const TIn* __restrict__ v, const TIn* __restrict__ g,
-                                              const float* __restrict__ gcum, const TIn* __restrict__ beta,
+// whole work-group of kThreads threads; `smem` holds IntraLds::BYTES.
+// `in` holds the chunk's inputs (load_inputs); right after they are staged
+// in LDS, `after_stage()` runs with every thread (it may reuse `in`, e.g. to
+// prefetch the next chunk); if it returns false nothing is written.
+template <typename TIn, int DK, int DV, typename AfterStage>
+__device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& in, const float* __restrict__ gcum,
                                               float scale, int b, int h, int T_len, int H, int ch,
-                                              char* __restrict__ rec) {
+                                              char* __restrict__ rec, AfterStage after_stage) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using Gm = typename P::Gram;
@@ -187,13 +247,12 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sRed = reinterpret_cast<float*>(smem + L::RED);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = 4 * (lane >> 4);
   const int t0 = ch * kC;
   const int Lrows = min(kC, T_len - t0);
-  const size_t tokk = (size_t)H * DK, tokv = (size_t)H * DV;
+  const size_t tokk = (size_t)H * DK;
   const size_t base_k = ((size_t)b * T_len + t0) * tokk + (size_t)h * DK;
-  const size_t base_v = ((size_t)b * T_len + t0) * tokv + (size_t)h * DV;
   __syncthreads();   // a previous call's LDS readers are done
   Op* rW = reinterpret_cast<Op*>(rec) + R::W;
   Op* rQ = reinterpret_cast<Op*>(rec) + R::Q;
@@ -201,46 +260,35 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
   float* rDec = reinterpret_cast<float*>(rec + R::DEC_OFF_BYTES);
   float* rU = reinterpret_cast<float*>(rec + R::U_OFF_BYTES);
   float* rO = reinterpret_cast<float*>(rec + R::O_OFF_BYTES);
-  const raw16 zero16 = raw16{0.f, 0.f, 0.f, 0.f};
 
-  // ---- phase 0: stage k, q (rows >= Lrows are zero), beta, Gamma; v to registers
-  constexpr int NVK = kC * DK / VE;
-  for (int n = tid; n < NVK; n += 256) {
-    const int r = n / (DK / VE), c = (n % (DK / VE)) * VE;
-    raw16 kv = zero16, qv = zero16;
-    if (r < Lrows) {
-      kv = *reinterpret_cast<const raw16*>(k + base_k + r * tokk + c);
-      qv = *reinterpret_cast<const raw16*>(q + base_k + r * tokk + c);
-    }
-    *reinterpret_cast<raw16*>(sK + r * L::LK + c) = kv;
-    *reinterpret_cast<raw16*>(sQ + r * L::LK + c) = qv;
-  }
-  constexpr int NVV = kC * DV / VE;
-  constexpr int VPT = (NVV + 255) / 256;
-  raw16 vreg[VPT];
+  // ---- phase 0: stage k, q, beta, Gamma from the input registers
+  using IR = InRegs<TIn, DK, DV>;
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int n = tid + 256 * i;
-    const int r = n / (DV / VE), c = (n % (DV / VE)) * VE;
-    vreg[i] = (n < NVV && r < Lrows) ? *reinterpret_cast<const raw16*>(v + base_v + r * tokv + c) : zero16;
+  for (int i = 0; i < IR::NK; ++i) {
+    const int n = tid + kThreads * i;
+    const int r = n / (DK / VE), c = (n % (DK / VE)) * VE;
+    *reinterpret_cast<raw16*>(sK + r * L::LK + c) = in.k[i];
+    *reinterpret_cast<raw16*>(sQ + r * L::LK + c) = in.q[i];
+    if (!gcum) {
+#pragma unroll
+      for (int x = 0; x < VE; ++x) sG[r * L::LG + c + x] = raw_elem<TIn>(in.g[i], x);
+    }
   }
-  if (tid < kC) sBeta[tid] = tid < Lrows ? to_f32(beta[((size_t)b * T_len + t0 + tid) * H + h]) : 0.f;
+  if (tid < kC) sBeta[tid] = in.beta;
+  raw16 vreg[IR::NV];
+#pragma unroll
+  for (int i = 0; i < IR::NV; ++i) vreg[i] = in.v[i];
+  constexpr int NVV = kC * DV / VE;
+  constexpr int VPT = IR::NV;
   if (gcum) {
-    for (int n = tid; n < kC * DK / 4; n += 256) {
+    for (int n = tid; n < kC * DK / 4; n += kThreads) {
       const int r = n / (DK / 4), c = (n % (DK / 4)) * 4;
       const int rr = min(r, Lrows - 1);
       const f32x4 gv = *reinterpret_cast<const f32x4*>(gcum + base_k + rr * tokk + c);
       *reinterpret_cast<f32x4*>(sG + r * L::LG + c) = gv * kLog2e;
     }
   } else {
-    // stage g (vector loads, rows >= Lrows are zero), then scan each channel
-    // from registers in row order
-    for (int n = tid; n < NVK; n += 256) {
-      const int r = n / (DK / VE), c = (n % (DK / VE)) * VE;
-      const raw16 gv = r < Lrows ? *reinterpret_cast<const raw16*>(g + base_k + r * tokk + c) : zero16;
-#pragma unroll
-      for (int x = 0; x < VE; ++x) sG[r * L::LG + c + x] = raw_elem<TIn>(gv, x);
-    }
+    // inclusive scan of each channel over the chunk's rows, in row order
     __syncthreads();
     if (tid < DK) {
       float gr[kC];
@@ -255,10 +303,11 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
     }
   }
   __syncthreads();
+  if (!after_stage()) return false;
 
   // ---- phase 1: Gram tiles (A -> LDS, M kept in registers), Khat, dec, Qbar
-  f32x4 mreg[3];
-  for (int ti = 0; ti < 3; ++ti) {
+  f32x4 mreg[2];
+  for (int ti = 0; ti < 2; ++ti) {
     const int idx = w + kNW * ti;
     if (idx >= 10) break;
     const int a = kTileA[idx], bb = kTileB[idx];
@@ -305,7 +354,7 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
     mreg[ti] = mrow;
   }
   // Khat tiles (st, ct) and dec
-  for (int n = tid; n < DK * 16; n += 256) {
+  for (int n = tid; n < DK * 16; n += kThreads) {
     const int tile = n >> 6, ln = n & 63;
     const int st = tile / (DK / 16), ct = tile % (DK / 16);
     const int col = 16 * ct + (ln & 15), row0 = 16 * st + 4 * (ln >> 4);
@@ -321,14 +370,15 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
   f32x4 qbar[NQW];
 #pragma unroll
   for (int j = 0; j < NQW; ++j) {
-    const int n = w + kNW * j, ct = n >> 2, rt = (n + ct) & 3;
+    int ct, rt;
+    wave_tile(w, j, NQW, ct, rt);
     const int row = 16 * rt + l16, col = 16 * ct + g4;
     qbar[j] = widen4(load4(sQ + row * L::LK + col)) * exp2v(*reinterpret_cast<const f32x4*>(sG + row * L::LG + col));
   }
   __syncthreads();   // sQ is dead from here on; R2 becomes M + Tm
 
   // M (Op) into R2, zero above the diagonal inside diagonal tiles
-  for (int ti = 0; ti < 3; ++ti) {
+  for (int ti = 0; ti < 2; ++ti) {
     const int idx = w + kNW * ti;
     if (idx >= 10) break;
     const int a = kTileA[idx], bb = kTileB[idx];
@@ -366,28 +416,30 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
     __syncthreads();
   }
   // Tm = X Diag(beta), lower triangle
-  for (int n = tid; n < kC * kC; n += 256) {
+  for (int n = tid; n < kC * kC; n += kThreads) {
     const int r = n >> 6, s = n & 63;
     sTm[r * L::LB + s] = from_f32<Op>(s <= r ? sX[r * L::LA + s] * sBeta[s] : 0.f);
   }
 
   // ---- phase 3a: Kbar^T = (e^Gamma k)^T into R1 (through registers), then W^T
-  constexpr int NKB = kC * DK / 256;
+  constexpr int NKB = kC * DK / kThreads;
   Op kb[NKB];
 #pragma unroll
   for (int i = 0; i < NKB; ++i) {
-    const int n = tid + 256 * i, s = n & 63, c = n >> 6;
+    const int n = tid + kThreads * i, s = n & 63, c = n >> 6;
     kb[i] = from_f32<Op>(to_f32(sK[s * L::LK + c]) * exp2_fast(sG[s * L::LG + c]));
   }
   __syncthreads();   // sK and sX dead; sTm complete
 #pragma unroll
   for (int i = 0; i < NKB; ++i) {
-    const int n = tid + 256 * i, s = n & 63, c = n >> 6;
+    const int n = tid + kThreads * i, s = n & 63, c = n >> 6;
     sKbt[c * L::LB + s] = kb[i];
   }
   __syncthreads();
-  for (int n = w; n < NQT; n += kNW) {   // W^T tile (ct, rt)
-    const int ct = n >> 2, rt = (n + ct) & 3;
+#pragma unroll
+  for (int j = 0; j < NQW; ++j) {   // W^T tile (ct, rt)
+    int ct, rt;
+    wave_tile(w, j, NQW, ct, rt);
     const f32x4 acc = tri_mma(sKbt + (16 * ct + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
     store4<Op>(rW + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(acc));
 #pragma unroll
@@ -398,7 +450,8 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
   // ---- phase 4a: Q'^T = scale (Qbar^T - W^T M^T)
 #pragma unroll
   for (int j = 0; j < NQW; ++j) {
-    const int n = w + kNW * j, ct = n >> 2, rt = (n + ct) & 3;
+    int ct, rt;
+    wave_tile(w, j, NQW, ct, rt);
     const f32x4 mw = tri_mma(sWt + (16 * ct + l16) * L::LB, sM + (16 * rt + l16) * L::LB, rt + 1);
     store4<Op>(rQ + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>((qbar[j] - mw) * scale));
   }
@@ -413,7 +466,7 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
   if (!P::kMixed) __syncthreads();   // R1 (Kbar^T) and X (W^T) readers done
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const int n = tid + 256 * i;
+    const int n = tid + kThreads * i;
     if (n < NVV) {
       const int r = n / (DV / VE), c = (n % (DV / VE)) * VE;
 #pragma unroll
@@ -427,7 +480,8 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
   float umax = 0.f;
 #pragma unroll
   for (int j = 0; j < NUW; ++j) {   // Ut tile (st, jt)
-    const int n = w + kNW * j, jt = n >> 2, st = (n + jt) & 3;
+    int jt, st;
+    wave_tile(w, j, NUW, jt, st);
     ut[j] = tri_mma(sTm + (16 * st + l16) * L::LB, sVt + (16 * jt + l16) * L::LB, st + 1) * (1.f / sv);
     *reinterpret_cast<f32x4*>(rU + (st * (DV / 16) + jt) * 256 + 4 * lane) = ut[j];
     umax = fmaxf(umax, absmax4(ut[j]));
@@ -436,7 +490,8 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
   if (!P::kMixed) __syncthreads();
 #pragma unroll
   for (int j = 0; j < NUW; ++j) {   // Ut^T (range-scaled) into X
-    const int n = w + kNW * j, jt = n >> 2, st = (n + jt) & 3;
+    int jt, st;
+    wave_tile(w, j, NUW, jt, st);
     store4<Op>(sUt + (16 * jt + l16) * L::LB + 16 * st + g4, narrow4<Op>(ut[j] * su));
   }
   __syncthreads();
@@ -444,32 +499,37 @@ __device__ __forceinline__ void produce_chunk(char* smem, const TIn* __restrict_
   // ---- phase 4b: Ot = scale M Ut
 #pragma unroll
   for (int j = 0; j < NUW; ++j) {   // Ot tile (rt, jt)
-    const int n = w + kNW * j, jt = n >> 2, rt = (n + jt) & 3;
+    int jt, rt;
+    wave_tile(w, j, NUW, jt, rt);
     const f32x4 acc = tri_mma(sM + (16 * rt + l16) * L::LB, sUt + (16 * jt + l16) * L::LB, rt + 1);
     *reinterpret_cast<f32x4*>(rO + (rt * (DV / 16) + jt) * 256 + 4 * lane) = acc * (scale / su);
   }
+  return true;
 }
 
 // Two-stage schedule, stage 1: one work-group per (b*h, chunk), records for
 // every chunk of every head in the workspace.
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void intra_chunk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                                          const TIn* __restrict__ v, const TIn* __restrict__ g,
-                                                          const float* __restrict__ gcum,
-                                                          const TIn* __restrict__ beta, float scale,
-                                                          char* __restrict__ ws, int T_len, int H, int nchunks) {
+__global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                               const TIn* __restrict__ v, const TIn* __restrict__ g,
+                                                               const float* __restrict__ gcum,
+                                                               const TIn* __restrict__ beta, float scale,
+                                                               char* __restrict__ ws, int T_len, int H, int nchunks) {
   __shared__ __align__(16) char smem[IntraLds<TIn, DK, DV>::BYTES];
   const int ch = blockIdx.x % nchunks, bh = blockIdx.x / nchunks;
-  produce_chunk<TIn, DK, DV>(smem, q, k, v, g, gcum, beta, scale, bh / H, bh % H, T_len, H, ch,
-                             ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES);
+  InRegs<TIn, DK, DV> in;
+  load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, ch);
+  produce_chunk<TIn, DK, DV>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, ch,
+                             ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [] { return true; });
 }
 
 // ---------------------------------------------------------------------------
-// State pass over one head's chunks, 64 value columns (block vb): each of
-// the 4 waves owns 16 value columns and keeps that dk x 16 slice of S in
-// fp32 accumulators for the whole sequence.  The chunk's shared operands
-// (W, Q', Khat, dec) are staged once in LDS for the four waves; the next
-// chunk's copy is prefetched into registers during the current one.
+// State pass over one head's chunks: wave w < dv/16 owns the 16 value
+// columns 16w..16w+15 and keeps that dk x 16 slice of S in fp32
+// accumulators for the whole sequence (with dv = 64 the upper four waves
+// only help stage the operands).  The chunk's shared operands (W, Q', Khat,
+// dec) are staged once in LDS for all waves; the next chunk's copy is
+// prefetched into registers during the current one.
 //
 // kRing = false: records of every chunk are stored one after another at
 //   recbase (two-stage schedule).
@@ -509,7 +569,7 @@ struct ConsumerLds {
 };
 
 template <typename TIn, int DK, int DV, bool kRing>
-__device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
+__device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring,
                                               const float* __restrict__ h0, float* __restrict__ ht,
                                               float* __restrict__ o, int b, int h, int T_len, int H,
                                               int nchunks) {
@@ -517,17 +577,19 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   using Op = typename P::Op;
   using R = Rec<TIn, DK, DV>;
   constexpr int NCT = DK / 16;
+  constexpr int NCW = DV / 16;   // waves that own value columns
   constexpr int NV16 = R::SHARED_BYTES / 16;
-  constexpr int PPT = (NV16 + 255) / 256;
+  constexpr int PPT = (NV16 + kThreads - 1) / kThreads;
   const Op* sW = reinterpret_cast<const Op*>(smem) + R::W;
   const Op* sQ = reinterpret_cast<const Op*>(smem) + R::Q;
   const Op* sK = reinterpret_cast<const Op*>(smem) + R::K;
   const float* sDec = reinterpret_cast<const float*>(smem + R::DEC_OFF_BYTES);
   int* sAbort = reinterpret_cast<int*>(smem + R::SHARED_BYTES);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = 4 * (lane >> 4);
-  const int jt = vb * 4 + w;
+  const bool owner = w < NCW;                 // wave-uniform
+  const int jt = owner ? w : 0;
   const int j = 16 * jt + l16;
   const size_t bh = (size_t)b * H + h;
   auto rec_of = [&](int c) { return recbase + (size_t)(kRing ? c % ring.R : c) * R::BYTES; };
@@ -556,7 +618,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[ct][i] = h0 ? h0[sbase + (size_t)(16 * ct + g4 + i) * DV + j] : 0.f;
+    for (int i = 0; i < 4; ++i) S[ct][i] = (h0 && owner) ? h0[sbase + (size_t)(16 * ct + g4 + i) * DV + j] : 0.f;
 
   raw16 pre[PPT];
   f32x4 preU[4], preO[4];
@@ -564,15 +626,17 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     const char* rec = rec_of(c);
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int n = tid + 256 * i;
+      const int n = tid + kThreads * i;
       if (n < NV16) pre[i] = reinterpret_cast<const raw16*>(rec)[n];
     }
     const float* rU = reinterpret_cast<const float*>(rec + R::U_OFF_BYTES);
     const float* rO = reinterpret_cast<const float*>(rec + R::O_OFF_BYTES);
+    if (owner) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      preU[t] = *reinterpret_cast<const f32x4*>(rU + (t * (DV / 16) + jt) * 256 + 4 * lane);
-      preO[t] = *reinterpret_cast<const f32x4*>(rO + (t * (DV / 16) + jt) * 256 + 4 * lane);
+      for (int t = 0; t < 4; ++t) {
+        preU[t] = *reinterpret_cast<const f32x4*>(rU + (t * (DV / 16) + jt) * 256 + 4 * lane);
+        preO[t] = *reinterpret_cast<const f32x4*>(rO + (t * (DV / 16) + jt) * 256 + 4 * lane);
+      }
     }
   };
   if (!wait_ready(0)) return;
@@ -582,7 +646,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     __syncthreads();   // every wave is done with the previous chunk's LDS copy
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int n = tid + 256 * i;
+      const int n = tid + kThreads * i;
       if (n < NV16) reinterpret_cast<raw16*>(smem)[n] = pre[i];
     }
     f32x4 Ut[4], Ot[4];
@@ -591,6 +655,9 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       Ut[t] = preU[t];
       Ot[t] = preO[t];
     }
+    // every load of chunk c has returned its data (in every wave) before the
+    // slot is handed back below
+    if (kRing) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // chunk c has been read completely: hand its slot back
     if (kRing && tid == 0) __hip_atomic_store(ring.done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -598,6 +665,8 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       if (!wait_ready(c + 1)) return;
       prefetch(c + 1);
     }
+
+    if (!owner) continue;   // wave-uniform; no barriers below in this iteration
 
     // S as an operand, range-scaled by a power of two
     float smax = 0.f;
@@ -658,7 +727,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     }
   }
 
-  if (ht) {
+  if (ht && owner) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -666,37 +735,37 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   }
 }
 
-// Two-stage schedule, stage 2: one work-group per (b*h, 64 value columns).
+// Two-stage schedule, stage 2: one work-group per head.
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void state_pass_kernel(const char* __restrict__ ws, const float* __restrict__ h0,
-                                                         float* __restrict__ ht, float* __restrict__ o, int T_len,
-                                                         int H, int nchunks) {
+__global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __restrict__ ws,
+                                                              const float* __restrict__ h0, float* __restrict__ ht,
+                                                              float* __restrict__ o, int T_len, int H, int nchunks) {
   __shared__ __align__(16) char smem[ConsumerLds<TIn, DK, DV>::BYTES];
-  constexpr int NVB = DV / 64;
-  const int bh = blockIdx.x / NVB;
+  const int bh = blockIdx.x;
   consume_chain<TIn, DK, DV, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
-                                    Ring{nullptr, nullptr, nullptr, 1}, blockIdx.x % NVB, h0, ht, o, bh / H, bh % H,
-                                    T_len, H, nchunks);
+                                    Ring{nullptr, nullptr, nullptr, 1}, h0, ht, o, bh / H, bh % H, T_len, H, nchunks);
 }
 
 // ---------------------------------------------------------------------------
 // Fused single-pass schedule: one persistent work-group per CU.  Heads are
 // dealt to the 8 XCDs (work-group i runs on XCD i % 8); on each XCD the
-// first work-groups are state-pass consumers (one per head and 64-column
-// block, resident for the whole call) and the rest are producers that take
+// first work-groups are state-pass consumers (one per head, resident for
+// the whole call) and the rest are producers that take
 // (chunk, head) items of that XCD's heads in chunk-major order from a queue
 // and write each chunk's record into the head's ring of R slots.  Records
 // therefore live only in L2 / Infinity Cache between producer and consumer.
 // Ordering: producer stores, then an agent-scope release fence in every
 // wave, then ready[slot] = c + 1; the consumer polls ready, then an
 // agent-scope acquire fence, then reads.  A slot is reused only after every
-// consumer of the head stored done >= c + 1 for the chunk that held it.
+// consumer of the head stored done >= c + 1 for the chunk that held it.  A
+// producer takes its next item and starts loading that item's inputs as soon
+// as the current item's inputs are staged, so loads overlap the compute.
 // Every wait is bounded (kSpinLimit); on a timeout the work-group sets the
 // error word and leaves, so the grid always drains.
 //
 // ctrl layout (ints, zeroed before the launch):
 //   [0..7]   per-XCD item counters      [8] error word
-//   [16 ..)  ready[nheads][R], then done[nheads][NVB]
+//   [16 ..)  ready[nheads][R], then done[nheads]
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct FusedLds {
@@ -705,15 +774,15 @@ struct FusedLds {
 };
 
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void fused_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                                        const TIn* __restrict__ v, const TIn* __restrict__ g,
-                                                        const float* __restrict__ gcum, const TIn* __restrict__ beta,
-                                                        float scale, const float* __restrict__ h0,
-                                                        float* __restrict__ ht, float* __restrict__ o, int T_len,
-                                                        int H, int nchunks, int head0, int nheads,
-                                                        char* __restrict__ ring, int* __restrict__ ctrl, int R) {
+__global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                             const TIn* __restrict__ v, const TIn* __restrict__ g,
+                                                             const float* __restrict__ gcum,
+                                                             const TIn* __restrict__ beta, float scale,
+                                                             const float* __restrict__ h0, float* __restrict__ ht,
+                                                             float* __restrict__ o, int T_len, int H, int nchunks,
+                                                             int head0, int nheads, char* __restrict__ ring,
+                                                             int* __restrict__ ctrl, int R) {
   using Rc = Rec<TIn, DK, DV>;
-  constexpr int NVB = DV / 64;
   __shared__ __align__(16) char smem[FusedLds<TIn, DK, DV>::BYTES];
   int* sWord = reinterpret_cast<int*>(smem + FusedLds<TIn, DK, DV>::BYTES - 16);
   const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
@@ -722,44 +791,67 @@ __global__ __launch_bounds__(256) void fused_fwd_kernel(const TIn* __restrict__ 
   int* ready = ctrl + 16;
   int* done = ready + nheads * R;
 
-  if (li < nloc * NVB) {   // consumer
-    const int m = li / NVB, vb = li % NVB, jh = xcd + 8 * m, bh = head0 + jh;
-    consume_chain<TIn, DK, DV, true>(smem, ring + (size_t)jh * R * Rc::BYTES,
-                                     Ring{ready + jh * R, done + jh * NVB + vb, err, R}, vb, h0, ht, o, bh / H,
-                                     bh % H, T_len, H, nchunks);
+  if (li < nloc) {   // consumer of head jh
+    const int jh = xcd + 8 * li, bh = head0 + jh;
+    consume_chain<TIn, DK, DV, true>(smem, ring + (size_t)jh * R * Rc::BYTES, Ring{ready + jh * R, done + jh, err, R},
+                                     h0, ht, o, bh / H, bh % H, T_len, H, nchunks);
     return;
   }
-  // producer
+
+  // producer: items of this XCD's heads in chunk-major order
   const int total = nloc * nchunks;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (;;) {
-    if (w == 0) {   // wave 0 takes the next item and waits for its slot, uniformly
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // next item, taken by wave 0 and broadcast (wave-uniform result)
+  auto take = [&]() -> int {
+    if (w == 0) {
       int it = 0;
       if (lane == 0) it = __hip_atomic_fetch_add(ctrl + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       it = __builtin_amdgcn_readfirstlane(it);
-      if (it < total) {
-        const int c = it / nloc, jh = xcd + 8 * (it % nloc);
-        // the slot of chunk c held chunk c - R: wait until every consumer has read it
-        for (int vb = 0; vb < NVB && c >= R; ++vb)
-          if (!spin_until_geq(done + jh * NVB + vb, c - R + 1, err)) {
-            it = total;
-            break;
-          }
-      }
       if (lane == 0) *sWord = it;
     }
     __syncthreads();
-    // wave-uniform copy (see consume_chain): the loop exit below must not be
-    // lane-divergent for the compiler, the loop body holds barriers
     const int it = __builtin_amdgcn_readfirstlane(*sWord);
-    if (it >= total) return;
+    __syncthreads();
+    return it;
+  };
+  InRegs<TIn, DK, DV> in;
+  int it = take();
+  if (it >= total) return;
+  {
+    const int jh = xcd + 8 * (it % nloc), bh = head0 + jh;
+    load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, it / nloc);
+  }
+  for (;;) {
     const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
-    produce_chunk<TIn, DK, DV>(smem, q, k, v, g, gcum, beta, scale, bh / H, bh % H, T_len, H, c,
-                               ring + ((size_t)jh * R + c % R) * Rc::BYTES);
+    int nxt = total;
+    // Runs once this chunk's inputs are in LDS: take the next item and start
+    // loading its inputs, then wait until the ring slot of chunk c is free
+    // (it held chunk c - R, which every consumer must have read).
+    auto after_stage = [&]() -> bool {
+      nxt = take();
+      if (nxt < total) {
+        const int jn = xcd + 8 * (nxt % nloc), bn = head0 + jn;
+        load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bn / H, bn % H, T_len, H, nxt / nloc);
+      }
+      if (c < R) return true;
+      if (w == 0) {
+        const bool ok = spin_until_geq(done + jh, c - R + 1, err);
+        if (lane == 0) *sWord = ok ? 1 : 0;
+      }
+      __syncthreads();
+      const int ok = __builtin_amdgcn_readfirstlane(*sWord);
+      __syncthreads();
+      return ok != 0;
+    };
+    if (!produce_chunk<TIn, DK, DV>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
+                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage))
+      return;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (w == 0 && lane == 0)
       __hip_atomic_store(ready + jh * R + c % R, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (nxt >= total) return;
+    it = nxt;
   }
 }
 
@@ -775,20 +867,20 @@ constexpr int kMaxWgPerXcd = 32;      // MI355X: 256 CUs in 8 XCDs
 
 // Heads one fused launch can serve with `per_xcd` work-groups per XCD:
 // keep at least a quarter of each XCD (and >= 2 work-groups) as producers.
-static int fused_heads_per_launch(int per_xcd, int nvb) {
+static int fused_heads_per_launch(int per_xcd) {
   const int prod = per_xcd / 4 > 2 ? per_xcd / 4 : 2;
-  const int hx = (per_xcd - prod) / nvb;
+  const int hx = per_xcd - prod;
   return hx > 0 ? 8 * hx : 0;
 }
 
 template <typename TIn, int DK, int DV>
 static size_t fused_ctrl_bytes(int nheads) {
-  return ((size_t)(16 + nheads * kRingSlots + nheads * (DV / 64)) * 4 + 255) / 256 * 256;
+  return ((size_t)(16 + nheads * kRingSlots + nheads) * 4 + 255) / 256 * 256;
 }
 
 template <typename TIn, int DK, int DV>
 static size_t fused_ws_bytes(int nbh) {
-  const int cap = fused_heads_per_launch(kMaxWgPerXcd, DV / 64);
+  const int cap = fused_heads_per_launch(kMaxWgPerXcd);
   const int nh = nbh < cap ? nbh : cap;
   return fused_ctrl_bytes<TIn, DK, DV>(nh) + (size_t)nh * kRingSlots * Rec<TIn, DK, DV>::BYTES;
 }
@@ -805,7 +897,7 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   int per_xcd = cus / 8;
   if (per_xcd > kMaxWgPerXcd) per_xcd = kMaxWgPerXcd;
-  int batch = fused_heads_per_launch(per_xcd, DV / 64);
+  int batch = fused_heads_per_launch(per_xcd);
   if (batch <= 0) return hipErrorInvalidConfiguration;
   // what the workspace can hold
   while (batch > 0 && fused_ctrl_bytes<TIn, DK, DV>(batch) + (size_t)batch * kRingSlots * Rec<TIn, DK, DV>::BYTES > ws_bytes)
@@ -815,9 +907,9 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   char* ring = reinterpret_cast<char*>(ws) + fused_ctrl_bytes<TIn, DK, DV>(batch);
   for (int head0 = 0; head0 < nbh; head0 += batch) {
     const int nh = nbh - head0 < batch ? nbh - head0 : batch;
-    const int nctrl = 16 + nh * kRingSlots + nh * (DV / 64);
+    const int nctrl = 16 + nh * kRingSlots + nh;
     hipLaunchKernelGGL(clear_ints_kernel, dim3((nctrl + 255) / 256), dim3(256), 0, st, ctrl, nctrl);
-    hipLaunchKernelGGL((fused_fwd_kernel<TIn, DK, DV>), dim3(8 * per_xcd), dim3(256), 0, st, (const TIn*)q,
+    hipLaunchKernelGGL((fused_fwd_kernel<TIn, DK, DV>), dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q,
                        (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len,
                        H, nchunks, head0, nh, ring, ctrl, kRingSlots);
     e = hipGetLastError();
@@ -833,14 +925,14 @@ static hipError_t go_stages(const void* q, const void* k, const void* v, const v
   const int nchunks = (T_len + kC - 1) / kC;
   const unsigned nbh = (unsigned)B * (unsigned)H;
   if (stages & 1) {
-    hipLaunchKernelGGL((intra_chunk_kernel<TIn, DK, DV>), dim3(nchunks * nbh), dim3(256), 0, st, (const TIn*)q,
+    hipLaunchKernelGGL((intra_chunk_kernel<TIn, DK, DV>), dim3(nchunks * nbh), dim3(kThreads), 0, st, (const TIn*)q,
                        (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, (char*)ws,
                        T_len, H, nchunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
-    hipLaunchKernelGGL((state_pass_kernel<TIn, DK, DV>), dim3((DV / 64) * nbh), dim3(256), 0, st,
+    hipLaunchKernelGGL((state_pass_kernel<TIn, DK, DV>), dim3(nbh), dim3(kThreads), 0, st,
                        (const char*)ws, h0, ht, o, T_len, H, nchunks);
     return hipGetLastError();
   }
