@@ -534,34 +534,43 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __rest
 // kRing = false: records of every chunk are stored one after another at
 //   recbase (two-stage schedule).
 // kRing = true : chunk c is in slot c % R of a ring at recbase, published by a
-//   producer work-group through ready[c % R] == c + 1; after the chunk has
-//   been read, done[0] = c + 1 hands the slot back.
+//   producer work-group through ready[c % R] = ((c + 1) << 4) | (producer's
+//   XCD); after the chunk has been read, done[0] = c + 1 hands the slot back.
 // ---------------------------------------------------------------------------
 struct Ring {
   int* ready;   // this head's R slot flags
   int* done;    // this consumer's progress counter
   int* err;     // set on a wait that exceeded its bound
+  int* cxcc;    // this consumer's XCD + 1, published at its start
   int R;
 };
 
 constexpr int kSpinLimit = 1 << 20;   // about a second of polling before giving up
 
-// Polls *p >= target.  Executed by every lane of one whole wave: all lanes
-// load the same word and the loop condition goes through readfirstlane, so
-// the loop is wave-uniform (no lane-divergent loop inside code that also
-// holds barriers).  Returns false after kSpinLimit polls, or as soon as
-// another work-group reported an error; sets *err on a timeout.
-__device__ __forceinline__ bool spin_until_geq(const int* p, int target, int* err) {
+// The XCD (accelerator complex die, each with its own L2) this wave runs on.
+__device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xf; }
+
+// Polls *p until it is >= target and returns the value seen.  Executed by
+// every lane of one whole wave: all lanes load the same word and the loop
+// condition goes through readfirstlane, so the loop is wave-uniform (no
+// lane-divergent loop inside code that also holds barriers).  Returns -1
+// after kSpinLimit polls, or as soon as another work-group reported an
+// error; sets *err on a timeout.
+__device__ __forceinline__ int spin_until_geq(const int* p, int target, int* err) {
   for (int it = 0; it < kSpinLimit; ++it) {
     const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (v >= target) return true;
+    if (v >= target) return v;
     const int e = __builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (e != 0) return false;
+    if (e != 0) return -1;
     __builtin_amdgcn_s_sleep(2);
   }
   if ((threadIdx.x & 63) == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return false;
+  return -1;
 }
+
+// Waits until every vector memory access this wave issued has completed
+// (stores acknowledged by the L2, loads returned); also a compiler barrier.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <typename TIn, int DK, int DV>
 struct ConsumerLds {
@@ -600,12 +609,20 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   // lane-divergent exit from a loop that contains barriers lets the
   // structurizer run the lane-0 block and the other lanes' next iteration in
   // either order, which breaks the barrier protocol.
+  // A producer on this XCD wrote the chunk into the L2 this work-group
+  // reads through, so only the CU's L1 may hold stale lines of the slot: an
+  // L1 invalidate suffices.  Otherwise an agent-scope acquire.
+  const int my_xcc = xcc_id();
+  if (kRing && tid == 0) __hip_atomic_store(ring.cxcc, my_xcc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   auto wait_ready = [&](int c) -> bool {
     if (!kRing) return true;
     if (w == 0) {   // wave 0 polls, uniformly
-      const bool ok = spin_until_geq(ring.ready + c % ring.R, c + 1, ring.err);
-      if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      if (lane == 0) *sAbort = ok ? 0 : 1;
+      const int v = spin_until_geq(ring.ready + c % ring.R, (c + 1) << 4, ring.err);
+      if (v >= 0) {
+        if ((v & 15) == my_xcc) asm volatile("buffer_inv sc0" ::: "memory");
+        else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      if (lane == 0) *sAbort = v >= 0 ? 0 : 1;
     }
     __syncthreads();
     const int abort_now = __builtin_amdgcn_readfirstlane(*sAbort);
@@ -657,7 +674,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     }
     // every load of chunk c has returned its data (in every wave) before the
     // slot is handed back below
-    if (kRing) __builtin_amdgcn_s_waitcnt(0);
+    if (kRing) wait_vmem();
     __syncthreads();
     // chunk c has been read completely: hand its slot back
     if (kRing && tid == 0) __hip_atomic_store(ring.done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -743,7 +760,8 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
   __shared__ __align__(16) char smem[ConsumerLds<TIn, DK, DV>::BYTES];
   const int bh = blockIdx.x;
   consume_chain<TIn, DK, DV, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
-                                    Ring{nullptr, nullptr, nullptr, 1}, h0, ht, o, bh / H, bh % H, T_len, H, nchunks);
+                                    Ring{nullptr, nullptr, nullptr, nullptr, 1}, h0, ht, o, bh / H, bh % H, T_len,
+                                    H, nchunks);
 }
 
 // ---------------------------------------------------------------------------
@@ -754,9 +772,14 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
 // (chunk, head) items of that XCD's heads in chunk-major order from a queue
 // and write each chunk's record into the head's ring of R slots.  Records
 // therefore live only in L2 / Infinity Cache between producer and consumer.
-// Ordering: producer stores, then an agent-scope release fence in every
-// wave, then ready[slot] = c + 1; the consumer polls ready, then an
-// agent-scope acquire fence, then reads.  A slot is reused only after every
+// Ordering: producer stores, then a release in every wave, then
+// ready[slot] = (c + 1) << 4 | XCD; the consumer polls ready, then an
+// acquire, then reads.  Work-group i is dispatched to XCD i % 8, so a head's
+// producers and its consumer normally share one L2: then the release is a
+// wait for the stores to reach the L2 and the acquire an L1 invalidate.
+// Both sides check where they actually run (the XCC_ID hardware register;
+// the consumer publishes its XCD, the producer tags the flag with its own)
+// and use agent-scope fences whenever the two differ.  A slot is reused only after every
 // consumer of the head stored done >= c + 1 for the chunk that held it.  A
 // producer takes its next item and starts loading that item's inputs as soon
 // as the current item's inputs are staged, so loads overlap the compute.
@@ -765,7 +788,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
 //
 // ctrl layout (ints, zeroed before the launch):
 //   [0..7]   per-XCD item counters      [8] error word
-//   [16 ..)  ready[nheads][R], then done[nheads]
+//   [16 ..)  ready[nheads][R], then done[nheads], then cxcc[nheads]
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct FusedLds {
@@ -790,17 +813,20 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   int* err = ctrl + 8;
   int* ready = ctrl + 16;
   int* done = ready + nheads * R;
+  int* cxcc = done + nheads;
 
   if (li < nloc) {   // consumer of head jh
     const int jh = xcd + 8 * li, bh = head0 + jh;
-    consume_chain<TIn, DK, DV, true>(smem, ring + (size_t)jh * R * Rc::BYTES, Ring{ready + jh * R, done + jh, err, R},
-                                     h0, ht, o, bh / H, bh % H, T_len, H, nchunks);
+    consume_chain<TIn, DK, DV, true>(smem, ring + (size_t)jh * R * Rc::BYTES,
+                                     Ring{ready + jh * R, done + jh, err, cxcc + jh, R}, h0, ht, o, bh / H, bh % H,
+                                     T_len, H, nchunks);
     return;
   }
 
   // producer: items of this XCD's heads in chunk-major order
   const int total = nloc * nchunks;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int my_xcc = xcc_id();
   // next item, taken by wave 0 and broadcast (wave-uniform result)
   auto take = [&]() -> int {
     if (w == 0) {
@@ -835,7 +861,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
       }
       if (c < R) return true;
       if (w == 0) {
-        const bool ok = spin_until_geq(done + jh, c - R + 1, err);
+        const bool ok = spin_until_geq(done + jh, c - R + 1, err) >= 0;
         if (lane == 0) *sWord = ok ? 1 : 0;
       }
       __syncthreads();
@@ -846,10 +872,17 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     if (!produce_chunk<TIn, DK, DV>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
                                     ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage))
       return;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // Release.  If the head's consumer runs on this XCD it reads through the
+    // same L2, so it is enough that every wave's record stores have reached
+    // the L2; otherwise an agent-scope release (L2 write-back).
+    const int cx = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(cxcc + jh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (cx == my_xcc + 1) wait_vmem();
+    else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (w == 0 && lane == 0)
-      __hip_atomic_store(ready + jh * R + c % R, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ready + jh * R + c % R, ((c + 1) << 4) | my_xcc, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     if (nxt >= total) return;
     it = nxt;
   }
@@ -875,7 +908,7 @@ static int fused_heads_per_launch(int per_xcd) {
 
 template <typename TIn, int DK, int DV>
 static size_t fused_ctrl_bytes(int nheads) {
-  return ((size_t)(16 + nheads * kRingSlots + nheads) * 4 + 255) / 256 * 256;
+  return ((size_t)(16 + nheads * kRingSlots + 2 * nheads) * 4 + 255) / 256 * 256;
 }
 
 template <typename TIn, int DK, int DV>
@@ -907,7 +940,7 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   char* ring = reinterpret_cast<char*>(ws) + fused_ctrl_bytes<TIn, DK, DV>(batch);
   for (int head0 = 0; head0 < nbh; head0 += batch) {
     const int nh = nbh - head0 < batch ? nbh - head0 : batch;
-    const int nctrl = 16 + nh * kRingSlots + nh;
+    const int nctrl = 16 + nh * kRingSlots + 2 * nh;
     hipLaunchKernelGGL(clear_ints_kernel, dim3((nctrl + 255) / 256), dim3(256), 0, st, ctrl, nctrl);
     hipLaunchKernelGGL((fused_fwd_kernel<TIn, DK, DV>), dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q,
                        (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len,
