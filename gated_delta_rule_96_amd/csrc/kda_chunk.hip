@@ -51,7 +51,7 @@
 //   K  : tile (st, ct) lane l = Khat[16st + 4(l/16) + i][16ct + l%16]  (Op)
 //   dec: fp32 [dk] = e^{Gamma_C}
 //   U  : tile (st, jt) lane l = Ut[16st + 4(l/16) + i][16jt + l%16]    (fp32)
-//   O  : tile (rt, jt) lane l = Ot[16rt + 4(l/16) + i][16jt + l%16]    (fp32)
+//   O  : tile (rt, jt) lane l = Ot[16rt + l%16][16jt + 4(l/16) + i]    (fp32)
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -98,12 +98,16 @@ template <> __device__ __forceinline__ float raw_elem<bf16>(raw16 v, int x) {
 
 // acc = sum over the first 16*n16 reduction indices of pa-row . pb-row
 // (both rows k-contiguous): the lower-triangular ranges of the chunk.
+// The odd 16 of the range goes through a half-width MFMA into an
+// accumulator of its own, added with a VALU op: the result of one MFMA shape
+// is never fed to an MFMA of another shape as its accumulator (with such a
+// hand-off, rows of the result came out wrong, differently from run to run).
 template <typename T>
 __device__ __forceinline__ f32x4 tri_mma(const T* pa, const T* pb, int n16) {
   f32x4 acc = zero4();
   int k = 0;
   for (; k + 2 <= n16; k += 2) acc = mma(load_slab(pa + 16 * k), load_slab(pb + 16 * k), acc);
-  if (k < n16) acc = mma(load_half(pa + 16 * k), load_half(pb + 16 * k), acc);
+  if (k < n16) acc = acc + mma(load_half(pa + 16 * k), load_half(pb + 16 * k), zero4());
   return acc;
 }
 
@@ -496,12 +500,12 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   }
   __syncthreads();
 
-  // ---- phase 4b: Ot = scale M Ut
+  // ---- phase 4b: Ot = scale M Ut, as Ot^T tiles (lane: one row, 4 columns)
 #pragma unroll
   for (int j = 0; j < NUW; ++j) {   // Ot tile (rt, jt)
     int jt, rt;
     wave_tile(w, j, NUW, jt, rt);
-    const f32x4 acc = tri_mma(sM + (16 * rt + l16) * L::LB, sUt + (16 * jt + l16) * L::LB, rt + 1);
+    const f32x4 acc = tri_mma(sUt + (16 * jt + l16) * L::LB, sM + (16 * rt + l16) * L::LB, rt + 1);
     *reinterpret_cast<f32x4*>(rO + (rt * (DV / 16) + jt) * 256 + 4 * lane) = acc * (scale / su);
   }
   return true;
@@ -524,12 +528,13 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __rest
 }
 
 // ---------------------------------------------------------------------------
-// State pass over one head's chunks: wave w < dv/16 owns the 16 value
-// columns 16w..16w+15 and keeps that dk x 16 slice of S in fp32
-// accumulators for the whole sequence (with dv = 64 the upper four waves
-// only help stage the operands).  The chunk's shared operands (W, Q', Khat,
-// dec) are staged once in LDS for all waves; the next chunk's copy is
-// prefetched into registers during the current one.
+// State pass over one head's chunks.  Waves 0..3 (one per SIMD) own the
+// value columns: wave w keeps the dk x (dv/4) slice S[:, w*dv/4 ...] in fp32
+// accumulators for the whole sequence; waves 4..7 stage the records: each
+// chunk's record is copied into LDS once, and the next chunk's copy is
+// prefetched into their registers while the owners compute the current one.  With the whole record in LDS every operand tile read from LDS
+// feeds dv/64 MFMAs.  When the record does not fit (fp32 inputs with
+// dk = dv = 128), Ut and Ot stay in global memory and are read where used.
 //
 // kRing = false: records of every chunk are stored one after another at
 //   recbase (two-stage schedule).
@@ -572,9 +577,15 @@ __device__ __forceinline__ int spin_until_geq(const int* p, int target, int* err
 // (stores acknowledged by the L2, loads returned); also a compiler barrier.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+constexpr size_t kLdsMax = 160 * 1024;
+constexpr int kOwners = 4;   // waves that own value columns
+
 template <typename TIn, int DK, int DV>
 struct ConsumerLds {
-  static constexpr size_t BYTES = Rec<TIn, DK, DV>::SHARED_BYTES + 16;   // + abort word
+  using R = Rec<TIn, DK, DV>;
+  static constexpr bool kWhole = R::BYTES + 16 <= kLdsMax;   // Ut, Ot staged too
+  static constexpr size_t STAGED = kWhole ? R::BYTES : R::SHARED_BYTES;
+  static constexpr size_t BYTES = STAGED + 16;   // + abort word
 };
 
 template <typename TIn, int DK, int DV, bool kRing>
@@ -585,149 +596,197 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using R = Rec<TIn, DK, DV>;
+  using CL = ConsumerLds<TIn, DK, DV>;
   constexpr int NCT = DK / 16;
-  constexpr int NCW = DV / 16;   // waves that own value columns
-  constexpr int NV16 = R::SHARED_BYTES / 16;
-  constexpr int PPT = (NV16 + kThreads - 1) / kThreads;
+  constexpr int NJ = DV / 16 / kOwners;   // column tiles per owner wave
+  constexpr int NJT = DV / 16;
+  constexpr int NV16 = CL::STAGED / 16;
+  constexpr int kHelpers = kThreads - 64 * kOwners;   // threads of the staging waves
+  constexpr int PPT = (NV16 + kHelpers - 1) / kHelpers;
+  static_assert(NJ >= 1 && NJ * kOwners * 16 == DV, "dv must be a multiple of 64");
   const Op* sW = reinterpret_cast<const Op*>(smem) + R::W;
   const Op* sQ = reinterpret_cast<const Op*>(smem) + R::Q;
   const Op* sK = reinterpret_cast<const Op*>(smem) + R::K;
   const float* sDec = reinterpret_cast<const float*>(smem + R::DEC_OFF_BYTES);
-  int* sAbort = reinterpret_cast<int*>(smem + R::SHARED_BYTES);
+  int* sAbort = reinterpret_cast<int*>(smem + CL::STAGED);
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = 4 * (lane >> 4);
-  const bool owner = w < NCW;                 // wave-uniform
-  const int jt = owner ? w : 0;
-  const int j = 16 * jt + l16;
+  const bool owner = w < kOwners;   // wave-uniform
+  const int jt0 = (owner ? w : 0) * NJ;
   const size_t bh = (size_t)b * H + h;
   auto rec_of = [&](int c) { return recbase + (size_t)(kRing ? c % ring.R : c) * R::BYTES; };
 
-  // Ring: wait until chunk c is published; true = go on, false = abort.
-  // The verdict is read back with readfirstlane so that every branch and
-  // loop exit that depends on it is wave-uniform for the compiler: a
-  // lane-divergent exit from a loop that contains barriers lets the
-  // structurizer run the lane-0 block and the other lanes' next iteration in
-  // either order, which breaks the barrier protocol.
   // A producer on this XCD wrote the chunk into the L2 this work-group
   // reads through, so only the CU's L1 may hold stale lines of the slot: an
   // L1 invalidate suffices.  Otherwise an agent-scope acquire.
   const int my_xcc = xcc_id();
   if (kRing && tid == 0) __hip_atomic_store(ring.cxcc, my_xcc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  auto wait_ready = [&](int c) -> bool {
-    if (!kRing) return true;
-    if (w == 0) {   // wave 0 polls, uniformly
-      const int v = spin_until_geq(ring.ready + c % ring.R, (c + 1) << 4, ring.err);
-      if (v >= 0) {
-        if ((v & 15) == my_xcc) asm volatile("buffer_inv sc0" ::: "memory");
-        else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      }
-      if (lane == 0) *sAbort = v >= 0 ? 0 : 1;
-    }
-    __syncthreads();
-    const int abort_now = __builtin_amdgcn_readfirstlane(*sAbort);
-    __syncthreads();   // the word is rewritten by the next wait
-    return abort_now == 0;
-  };
+  if (tid == 0) *sAbort = 0;
+  __syncthreads();   // B0
 
-  f32x4 S[NCT];
+  // Owners and staging waves run separate loops (so that their registers
+  // are allocated separately) with the same barriers per chunk c:
+  //   B1  chunk c - 1 no longer read from LDS; then every wave reads the
+  //       abort word and leaves if it is set
+  //   B2  chunk c staged in LDS (+ B2b: Ut, Ot read, when not staged)
+  // Each staging wave polls the ring by itself while the owners compute (a
+  // wave-uniform bounded spin) and sets the abort word before B1 if the wait
+  // failed; the word is only ever set, so every wave sees the same verdict
+  // after B1.
+  if (!owner) {
+    const int htid = tid - 64 * kOwners;
+    raw16 pre[PPT];
+    // true once chunk c is published and may be read
+    auto ready_wait = [&](int c) -> bool {
+      if (!kRing) return true;
+      const int v = spin_until_geq(ring.ready + c % ring.R, (c + 1) << 4, ring.err);
+      if (v < 0) return false;
+      if ((v & 15) == my_xcc) asm volatile("buffer_inv sc0" ::: "memory");
+      else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      return true;
+    };
+    auto prefetch = [&](int c) {
+      const char* rec = rec_of(c);
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int n = htid + kHelpers * i;
+        if (n < NV16) pre[i] = reinterpret_cast<const raw16*>(rec)[n];
+      }
+    };
+    if (ready_wait(0)) prefetch(0);
+    else if (lane == 0) *sAbort = 1;
+    for (int c = 0; c < nchunks; ++c) {
+      __syncthreads();   // B1
+      if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int n = htid + kHelpers * i;
+        if (n < NV16) reinterpret_cast<raw16*>(smem)[n] = pre[i];
+      }
+      // every load of chunk c has returned its data before the slot is
+      // handed back below
+      if (kRing) wait_vmem();
+      __syncthreads();   // B2
+      if (!CL::kWhole) __syncthreads();   // B2b
+      // chunk c has been read completely: hand its slot back
+      if (kRing && htid == 0) __hip_atomic_store(ring.done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c + 1 < nchunks) {
+        if (ready_wait(c + 1)) prefetch(c + 1);
+        else if (lane == 0) *sAbort = 1;
+      }
+    }
+    return;
+  }
+
+  f32x4 S[NCT][NJ];
   const size_t sbase = bh * DK * DV;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[ct][i] = (h0 && owner) ? h0[sbase + (size_t)(16 * ct + g4 + i) * DV + j] : 0.f;
-
-  raw16 pre[PPT];
-  f32x4 preU[4], preO[4];
-  auto prefetch = [&](int c) {
-    const char* rec = rec_of(c);
+    for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int n = tid + kThreads * i;
-      if (n < NV16) pre[i] = reinterpret_cast<const raw16*>(rec)[n];
-    }
-    const float* rU = reinterpret_cast<const float*>(rec + R::U_OFF_BYTES);
-    const float* rO = reinterpret_cast<const float*>(rec + R::O_OFF_BYTES);
-    if (owner) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        preU[t] = *reinterpret_cast<const f32x4*>(rU + (t * (DV / 16) + jt) * 256 + 4 * lane);
-        preO[t] = *reinterpret_cast<const f32x4*>(rO + (t * (DV / 16) + jt) * 256 + 4 * lane);
-      }
-    }
-  };
-  if (!wait_ready(0)) return;
-  prefetch(0);
+      for (int i = 0; i < 4; ++i)
+        S[ct][jj][i] = h0 ? h0[sbase + (size_t)(16 * ct + g4 + i) * DV + 16 * (jt0 + jj) + l16] : 0.f;
 
+  const bool mixed = P::kMixed;
   for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();   // every wave is done with the previous chunk's LDS copy
+    __syncthreads();   // B1
+    if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
+    __syncthreads();   // B2
+    const char* rec = rec_of(c);
+    const float* uBase = CL::kWhole ? reinterpret_cast<const float*>(smem + R::U_OFF_BYTES)
+                                    : reinterpret_cast<const float*>(rec + R::U_OFF_BYTES);
+    const float* oBase = CL::kWhole ? reinterpret_cast<const float*>(smem + R::O_OFF_BYTES)
+                                    : reinterpret_cast<const float*>(rec + R::O_OFF_BYTES);
+    f32x4 Ut[CL::kWhole ? 1 : 4][NJ], Ot[CL::kWhole ? 1 : 4][NJ];   // read before the slot is handed back
+    if (!CL::kWhole) {
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int n = tid + kThreads * i;
-      if (n < NV16) reinterpret_cast<raw16*>(smem)[n] = pre[i];
-    }
-    f32x4 Ut[4], Ot[4];
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      Ut[t] = preU[t];
-      Ot[t] = preO[t];
+        for (int jj = 0; jj < NJ; ++jj) {
+          Ut[t][jj] = *reinterpret_cast<const f32x4*>(uBase + (t * NJT + jt0 + jj) * 256 + 4 * lane);
+          Ot[t][jj] = *reinterpret_cast<const f32x4*>(oBase + (t * NJT + jt0 + jj) * 256 + 4 * lane);
+        }
+      if (kRing) wait_vmem();
+      __syncthreads();   // B2b
     }
-    // every load of chunk c has returned its data (in every wave) before the
-    // slot is handed back below
-    if (kRing) wait_vmem();
-    __syncthreads();
-    // chunk c has been read completely: hand its slot back
-    if (kRing && tid == 0) __hip_atomic_store(ring.done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (c + 1 < nchunks) {
-      if (!wait_ready(c + 1)) return;
-      prefetch(c + 1);
-    }
-
-    if (!owner) continue;   // wave-uniform; no barriers below in this iteration
+    // Ut / Ot tile t of column tile jj: from LDS where staged, else from the
+    // registers read above
+    auto ut_of = [&](int t, int jj) -> f32x4 {
+      if (CL::kWhole) return *reinterpret_cast<const f32x4*>(uBase + (t * NJT + jt0 + jj) * 256 + 4 * lane);
+      return Ut[CL::kWhole ? 0 : t][jj];
+    };
+    auto ot_of = [&](int t, int jj) -> f32x4 {
+      if (CL::kWhole) return *reinterpret_cast<const f32x4*>(oBase + (t * NJT + jt0 + jj) * 256 + 4 * lane);
+      return Ot[CL::kWhole ? 0 : t][jj];
+    };
 
     // S as an operand, range-scaled by a power of two
     float smax = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) smax = fmaxf(smax, absmax4(S[ct]));
-    const float ss = P::kMixed ? fp16_range_scale(wave_max(smax)) : 1.f;
-    const float iss = 1.f / ss;
-    V4<Op> Sb[NCT];
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) Sb[ct] = narrow4<Op>(S[ct] * ss);
+      for (int jj = 0; jj < NJ; ++jj) smax = fmaxf(smax, absmax4(S[ct][jj]));
+    float ss = 1.f, iss = 1.f;
+    if (mixed) fp16_range_scale2(wave_max_dpp(smax), ss, iss);
+    V4<Op> Sb[NCT][NJ];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) Sb[ct][jj] = narrow4<Op>(S[ct][jj] * ss);
 
     // U = Ut - W S
-    f32x4 U[4];
+    f32x4 U[4][NJ];
     float umax = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      f32x4 Pv = zero4();
+      f32x4 Pv[NJ];
 #pragma unroll
-      for (int sl = 0; sl < DK / 32; ++sl)
-        Pv = mma(slab_of<Op>(load4(sW + ((2 * sl) * 4 + st) * 256 + 4 * lane), load4(sW + ((2 * sl + 1) * 4 + st) * 256 + 4 * lane)),
-                 slab_of<Op>(Sb[2 * sl], Sb[2 * sl + 1]), Pv);
-      U[st] = Ut[st] - Pv * iss;
-      umax = fmaxf(umax, absmax4(U[st]));
+      for (int jj = 0; jj < NJ; ++jj) Pv[jj] = zero4();
+#pragma unroll
+      for (int sl = 0; sl < DK / 32; ++sl) {
+        const Slab<Op> Wa = slab_of<Op>(load4(sW + ((2 * sl) * 4 + st) * 256 + 4 * lane),
+                                        load4(sW + ((2 * sl + 1) * 4 + st) * 256 + 4 * lane));
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) Pv[jj] = mma(Wa, slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]), Pv[jj]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        U[st][jj] = ut_of(st, jj) - Pv[jj] * iss;
+        umax = fmaxf(umax, absmax4(U[st][jj]));
+      }
     }
-    const float us = P::kMixed ? fp16_range_scale(wave_max(umax)) : 1.f;
-    const float ius = 1.f / us;
-    V4<Op> Ub[4];
+    float us = 1.f, ius = 1.f;
+    if (mixed) fp16_range_scale2(wave_max_dpp(umax), us, ius);
+    V4<Op> Ub[4][NJ];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) Ub[st] = narrow4<Op>(U[st] * us);
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) Ub[st][jj] = narrow4<Op>(U[st][jj] * us);
 
-    // O = Q' S + Ot
+    // O = Q' S + Ot, as O^T tiles: lane l holds row 16rt + l%16, columns
+    // 16jt + 4(l/16) .. +3, stored as one 16-byte vector
     const int t0 = c * kC;
+    const bool full = t0 + kC <= T_len;   // uniform; only the last chunk is partial
+    float* orow = o + (((size_t)b * T_len + t0 + l16) * H + h) * DV + 16 * jt0 + g4;
+    const size_t ors = (size_t)16 * H * DV;   // 16 rows
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc = zero4();
+      f32x4 acc[NJ];
 #pragma unroll
-      for (int sl = 0; sl < DK / 32; ++sl)
-        acc = mma(slab_of<Op>(load4(sQ + ((2 * sl) * 4 + rt) * 256 + 4 * lane), load4(sQ + ((2 * sl + 1) * 4 + rt) * 256 + 4 * lane)),
-                  slab_of<Op>(Sb[2 * sl], Sb[2 * sl + 1]), acc);
-      acc = acc * iss + Ot[rt];
+      for (int jj = 0; jj < NJ; ++jj) acc[jj] = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * rt + g4 + i;
-        if (t < T_len) o[(((size_t)b * T_len + t) * H + h) * DV + j] = acc[i];
+      for (int sl = 0; sl < DK / 32; ++sl) {
+        const Slab<Op> Qa = slab_of<Op>(load4(sQ + ((2 * sl) * 4 + rt) * 256 + 4 * lane),
+                                        load4(sQ + ((2 * sl + 1) * 4 + rt) * 256 + 4 * lane));
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) acc[jj] = mma(slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]), Qa, acc[jj]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        const f32x4 r = acc[jj] * iss + ot_of(rt, jj);
+        if (full || t0 + 16 * rt + l16 < T_len) *reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj) = r;
       }
     }
 
@@ -735,20 +794,29 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
-      f32x4 acc = zero4();
+      f32x4 acc[NJ];
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
-        acc = mma(slab_of<Op>(load4(sK + ((2 * sl) * NCT + ct) * 256 + 4 * lane), load4(sK + ((2 * sl + 1) * NCT + ct) * 256 + 4 * lane)),
-                  slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), acc);
-      S[ct] = S[ct] * d + acc * ius;
+      for (int jj = 0; jj < NJ; ++jj) acc[jj] = zero4();
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const Slab<Op> Ka = slab_of<Op>(load4(sK + ((2 * sl) * NCT + ct) * 256 + 4 * lane),
+                                        load4(sK + ((2 * sl + 1) * NCT + ct) * 256 + 4 * lane));
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) acc[jj] = mma(Ka, slab_of<Op>(Ub[2 * sl][jj], Ub[2 * sl + 1][jj]), acc[jj]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) S[ct][jj] = S[ct][jj] * d + acc[jj] * ius;
     }
   }
 
-  if (ht && owner) {
+  if (ht) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ht[sbase + (size_t)(16 * ct + g4 + i) * DV + j] = S[ct][i];
+      for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ht[sbase + (size_t)(16 * ct + g4 + i) * DV + 16 * (jt0 + jj) + l16] = S[ct][jj][i];
   }
 }
 

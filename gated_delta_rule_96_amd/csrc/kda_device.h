@@ -139,6 +139,28 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// x from lane (l ^ ...) as selected by DPP control `ctrl` within the rows
+// enabled by `row_mask`; lanes outside them (or with no source) keep x.
+template <int ctrl, int row_mask = 0xf>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                               ctrl, row_mask, 0xf, false));
+}
+
+// Maximum over the wave's 64 lanes with DPP moves (no LDS round trips),
+// returned wave-uniform: pairs, quads, half rows and rows of 16 by lane
+// permutations, then rows 0-1 and 2-3 by broadcasting lane 15 of a row into
+// the next, then row 3 gets lane 31; lane 63 holds the result.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));        // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));        // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));       // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));       // row_mirror
+  x = fmaxf(x, dpp_f<0x142, 0xA>(x));  // row_bcast:15 into rows 1 and 3
+  x = fmaxf(x, dpp_f<0x143, 0xC>(x));  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // Power-of-two factor s with s * mx in [2^14, 2^15) (mx > 0 finite), so
 // values scaled by s fit the fp16 range with their full precision; 1 for
 // mx == 0 or non-finite mx.  Multiplying and dividing by s is exact.
@@ -149,6 +171,16 @@ __device__ __forceinline__ float fp16_range_scale(float mx) {
   int k = 14 - (ex - 127);
   k = k < -100 ? -100 : (k > 100 ? 100 : k);
   return ldexpf(1.f, k);
+}
+// The same factor and its exact reciprocal.
+__device__ __forceinline__ void fp16_range_scale2(float mx, float& s, float& inv) {
+  const unsigned bits = __float_as_uint(mx);
+  const int ex = (int)((bits >> 23) & 0xffu);
+  int k = 14 - (ex - 127);
+  k = k < -100 ? -100 : (k > 100 ? 100 : k);
+  if (mx <= 0.f || ex == 0xff) k = 0;
+  s = ldexpf(1.f, k);
+  inv = ldexpf(1.f, -k);
 }
 
 }  // namespace kda
