@@ -15,12 +15,11 @@
 //   M[r,s]  =        sum_c q_rc k_sc e^{Gamma_rc - Gamma_sc}      s <= r
 //   Tm      = (I + A)^-1 Diag(beta)
 //   W       = Tm (e^Gamma * K)          Ut = Tm V
-//   Q'      = scale (e^Gamma * Q - M W) Ot = scale M Ut
 //   U       = Ut - W S
-//   O       = Q' S + Ot                 (= scale (e^Gamma Q) S + scale M U)
+//   O       = scale (e^Gamma * Q) S + scale M U
 //   S      <- e^{Gamma_C} * S + (e^{Gamma_C - Gamma} * K)^T U
-// Everything that does not depend on S (A, M, Tm, W, Ut, Q', Ot) is built by
-// the intra-chunk kernel; the state pass only does three products per chunk.
+// Everything that does not depend on S (A, M, Tm, W, Ut) is built by the
+// intra-chunk kernel; the state pass does the four S-dependent products.
 //
 // Rescaling (the point of the bounded decay): a tile of A or M whose rows
 // lie in 16-row sub-chunk a is a plain product of
@@ -40,18 +39,20 @@
 //     fp32 accumulation.  Quantities whose range is not bounded by the
 //     normalised inputs (V, Ut, S, U) are first scaled by a power of two
 //     chosen from their current maximum (exact), so fp16 never overflows.
-//   * Ut and Ot are kept in fp32.
 // With fp32 inputs every operand is fp32 (v_mfma_f32_16x16x4_f32).
 //
 // Workspace record per (b, h, chunk), every matrix stored as 16x16 tiles in
 // MFMA lane order (tile = 64 lanes x 4 consecutive values), so the state
 // pass reads each operand with one contiguous vector load per lane:
-//   W  : tile (ct, rt) lane l = W[16rt + l%16][16ct + 4(l/16) + i]     (Op)
-//   Q  : tile (ct, rt) lane l = Q'[16rt + l%16][16ct + 4(l/16) + i]    (Op)
-//   K  : tile (st, ct) lane l = Khat[16st + 4(l/16) + i][16ct + l%16]  (Op)
-//   dec: fp32 [dk] = e^{Gamma_C}
-//   U  : tile (st, jt) lane l = Ut[16st + 4(l/16) + i][16jt + l%16]    (fp32)
-//   O  : tile (rt, jt) lane l = Ot[16rt + l%16][16jt + 4(l/16) + i]    (fp32)
+//   W  : tile (ct, rt) lane l = W[16rt + l%16][16ct + 4(l/16) + i]       (Op)
+//   Q  : tile (ct, rt) lane l = Qbar[16rt + l%16][16ct + 4(l/16) + i]    (Op)
+//        with Qbar = scale e^Gamma * Q
+//   K  : tile (st, ct) lane l = Khat[16st + 4(l/16) + i][16ct + l%16]    (Op)
+//   M  : tile (kt, rt) lane l = scale M[16rt + l%16][16kt + 4(l/16) + i] (Op)
+//        (tiles above the diagonal are zero)
+//   dec: fp32 [dk] = e^{Gamma_C};  uinv: fp32, 1 / (scale factor of U)
+//   U  : tile (st, jt) lane l = Ut[16st + 4(l/16) + i][16jt + l%16] * su (Op),
+//        tiles column-block major (index 4 jt + st)
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -79,12 +80,12 @@ struct Rec {
   static constexpr size_t W = 0;                               // Op elements
   static constexpr size_t Q = (size_t)DK * kC;
   static constexpr size_t K = 2 * (size_t)DK * kC;
-  static constexpr size_t DEC_OFF_BYTES = 3 * (size_t)DK * kC * sizeof(Op);
-  static constexpr size_t SHARED_BYTES = DEC_OFF_BYTES + 4 * (size_t)DK;   // staged in LDS
-  static constexpr size_t U_OFF_BYTES = SHARED_BYTES;                      // fp32 [C*DV]
-  static constexpr size_t O_OFF_BYTES = U_OFF_BYTES + 4 * (size_t)kC * DV; // fp32 [C*DV]
-  static constexpr size_t BYTES = (O_OFF_BYTES + 4 * (size_t)kC * DV + 255) / 256 * 256;
-  static_assert(SHARED_BYTES % 16 == 0, "record alignment");
+  static constexpr size_t M = 3 * (size_t)DK * kC;
+  static constexpr size_t DEC_OFF_BYTES = (M + (size_t)kC * kC) * sizeof(Op);   // fp32 [DK]
+  static constexpr size_t UINV_OFF_BYTES = DEC_OFF_BYTES + 4 * (size_t)DK;      // fp32, 16 bytes
+  static constexpr size_t U_OFF_BYTES = UINV_OFF_BYTES + 16;                    // Op [C*DV]
+  static constexpr size_t BYTES = (U_OFF_BYTES + (size_t)kC * DV * sizeof(Op) + 255) / 256 * 256;
+  static_assert(U_OFF_BYTES % 16 == 0, "record alignment");
 };
 
 typedef float raw16 __attribute__((ext_vector_type(4)));   // 16 raw bytes
@@ -192,8 +193,8 @@ __device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* 
 // LDS regions are reused across phases (lifetimes in brackets):
 //   G  : fp32 Gamma*log2(e) [C][DK+4]                          [all]
 //   R1 : k [C][DK] (in)  | Kbar^T [DK][C] (Op) | V^T [DV][C] (Op)
-//   X  : A, X fp32 [C][C+4] each | W^T [DK][C] (Op) | Ut^T [DV][C] (Op)
-//   R2 : q [C][DK] (in)  | M [C][C] (Op) + Tm [C][C] (Op)
+//   X  : A, X fp32 [C][C+4] each
+//   R2 : q [C][DK] (in)  | Tm [C][C] (Op)
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct IntraLds {
@@ -208,9 +209,9 @@ struct IntraLds {
   static constexpr size_t R1 = G + (size_t)kC * LG * 4;
   static constexpr size_t R1_SIZE = mx((size_t)kC * LK * sizeof(TIn), mx((size_t)DK, (size_t)DV) * LB * sizeof(Op));
   static constexpr size_t X = R1 + R1_SIZE;
-  static constexpr size_t X_SIZE = mx(2 * (size_t)kC * LA * 4, mx((size_t)DK, (size_t)DV) * LB * sizeof(Op));
+  static constexpr size_t X_SIZE = 2 * (size_t)kC * LA * 4;
   static constexpr size_t R2 = X + X_SIZE;
-  static constexpr size_t R2_SIZE = mx((size_t)kC * LK * sizeof(TIn), 2 * (size_t)kC * LB * sizeof(Op));
+  static constexpr size_t R2_SIZE = mx((size_t)kC * LK * sizeof(TIn), (size_t)kC * LB * sizeof(Op));
   static constexpr size_t BETA = R2 + R2_SIZE;
   static constexpr size_t RED = BETA + kC * 4;
   static constexpr size_t BYTES = RED + 16 * 4;
@@ -243,11 +244,8 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   Op* sVt = reinterpret_cast<Op*>(smem + L::R1);
   float* sA = reinterpret_cast<float*>(smem + L::X);
   float* sX = sA + kC * L::LA;
-  Op* sWt = reinterpret_cast<Op*>(smem + L::X);
-  Op* sUt = reinterpret_cast<Op*>(smem + L::X);
   TIn* sQ = reinterpret_cast<TIn*>(smem + L::R2);
-  Op* sM = reinterpret_cast<Op*>(smem + L::R2);
-  Op* sTm = sM + kC * L::LB;
+  Op* sTm = reinterpret_cast<Op*>(smem + L::R2);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sRed = reinterpret_cast<float*>(smem + L::RED);
 
@@ -262,8 +260,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   Op* rQ = reinterpret_cast<Op*>(rec) + R::Q;
   Op* rK = reinterpret_cast<Op*>(rec) + R::K;
   float* rDec = reinterpret_cast<float*>(rec + R::DEC_OFF_BYTES);
-  float* rU = reinterpret_cast<float*>(rec + R::U_OFF_BYTES);
-  float* rO = reinterpret_cast<float*>(rec + R::O_OFF_BYTES);
+  Op* rM = reinterpret_cast<Op*>(rec) + R::M;
+  Op* rU = reinterpret_cast<Op*>(rec + R::U_OFF_BYTES);
+  float* rUinv = reinterpret_cast<float*>(rec + R::UINV_OFF_BYTES);
 
   // ---- phase 0: stage k, q, beta, Gamma from the input registers
   using IR = InRegs<TIn, DK, DV>;
@@ -309,8 +308,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   __syncthreads();
   if (!after_stage()) return false;
 
-  // ---- phase 1: Gram tiles (A -> LDS, M kept in registers), Khat, dec, Qbar
-  f32x4 mreg[2];
+  // ---- phase 1: Gram tiles (A -> LDS, scale M -> record), Khat, dec, Qbar
   for (int ti = 0; ti < 2; ++ti) {
     const int idx = w + kNW * ti;
     if (idx >= 10) break;
@@ -355,7 +353,12 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       mrow[i] = sc <= r ? accM[i] : 0.f;
     }
     *reinterpret_cast<f32x4*>(sA + r * L::LA + 16 * bb + g4) = arow;
-    mreg[ti] = mrow;
+    store4<Op>(rM + (bb * 4 + a) * 256 + 4 * lane, narrow4<Op>(mrow * scale));
+  }
+  if (w >= 2) {   // the six tiles above the diagonal of the record's M are zero
+    // (the mirror of lower tile (a, b): row block b, column block a)
+    const int zt = w - 2, kt = kTileA[4 + zt], rt = kTileB[4 + zt];
+    store4<Op>(rM + (kt * 4 + rt) * 256 + 4 * lane, narrow4<Op>(zero4()));
   }
   // Khat tiles (st, ct) and dec
   for (int n = tid; n < DK * 16; n += kThreads) {
@@ -370,24 +373,16 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     store4<Op>(rK + tile * 256 + 4 * ln, narrow4<Op>(val));
   }
   if (tid < DK) rDec[tid] = exp2_fast(sG[(kC - 1) * L::LG + tid]);
-  // Qbar = e^Gamma q for this wave's Q'^T tiles (ct, rt): lane holds Qbar[16rt + l16][16ct + g4 + i]
-  f32x4 qbar[NQW];
+  // Qbar = scale e^Gamma q, tiles (ct, rt): lane holds Qbar[16rt + l16][16ct + g4 + i]
 #pragma unroll
   for (int j = 0; j < NQW; ++j) {
     int ct, rt;
     wave_tile(w, j, NQW, ct, rt);
     const int row = 16 * rt + l16, col = 16 * ct + g4;
-    qbar[j] = widen4(load4(sQ + row * L::LK + col)) * exp2v(*reinterpret_cast<const f32x4*>(sG + row * L::LG + col));
+    const f32x4 qb = widen4(load4(sQ + row * L::LK + col)) * exp2v(*reinterpret_cast<const f32x4*>(sG + row * L::LG + col));
+    store4<Op>(rQ + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(qb * scale));
   }
-  __syncthreads();   // sQ is dead from here on; R2 becomes M + Tm
-
-  // M (Op) into R2, zero above the diagonal inside diagonal tiles
-  for (int ti = 0; ti < 2; ++ti) {
-    const int idx = w + kNW * ti;
-    if (idx >= 10) break;
-    const int a = kTileA[idx], bb = kTileB[idx];
-    store4<Op>(sM + (16 * a + l16) * L::LB + 16 * bb + g4, narrow4<Op>(mreg[ti]));
-  }
+  __syncthreads();   // sQ is dead from here on; R2 becomes Tm
 
   // ---- phase 2: X = (I + A)^-1 by 16x16 blocks, fp32
   if (w == 0) {   // diagonal blocks by forward substitution; lane = (block, column)
@@ -446,18 +441,6 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     wave_tile(w, j, NQW, ct, rt);
     const f32x4 acc = tri_mma(sKbt + (16 * ct + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
     store4<Op>(rW + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(acc));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sWt[(16 * ct + g4 + i) * L::LB + 16 * rt + l16] = from_f32<Op>(acc[i]);
-  }
-  __syncthreads();
-
-  // ---- phase 4a: Q'^T = scale (Qbar^T - W^T M^T)
-#pragma unroll
-  for (int j = 0; j < NQW; ++j) {
-    int ct, rt;
-    wave_tile(w, j, NQW, ct, rt);
-    const f32x4 mw = tri_mma(sWt + (16 * ct + l16) * L::LB, sM + (16 * rt + l16) * L::LB, rt + 1);
-    store4<Op>(rQ + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>((qbar[j] - mw) * scale));
   }
 
   // ---- phase 3b: V^T (range-scaled) into R1, then Ut = Tm V
@@ -467,7 +450,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
 #pragma unroll
     for (int x = 0; x < VE; ++x) vmax = fmaxf(vmax, fabsf(raw_elem<TIn>(vreg[i], x)));
   const float sv = P::kMixed ? fp16_range_scale(block_max(vmax, sRed)) : 1.f;   // barriers inside
-  if (!P::kMixed) __syncthreads();   // R1 (Kbar^T) and X (W^T) readers done
+  if (!P::kMixed) __syncthreads();   // R1 (Kbar^T) readers done
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int n = tid + kThreads * i;
@@ -487,27 +470,18 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     int jt, st;
     wave_tile(w, j, NUW, jt, st);
     ut[j] = tri_mma(sTm + (16 * st + l16) * L::LB, sVt + (16 * jt + l16) * L::LB, st + 1) * (1.f / sv);
-    *reinterpret_cast<f32x4*>(rU + (st * (DV / 16) + jt) * 256 + 4 * lane) = ut[j];
     umax = fmaxf(umax, absmax4(ut[j]));
   }
-  const float su = P::kMixed ? fp16_range_scale(block_max(umax, sRed)) : 1.f;   // X (W^T) readers done too
-  if (!P::kMixed) __syncthreads();
+  // Ut into the record as Op, range-scaled by su (exact power of two)
+  float su = 1.f, suinv = 1.f;
+  if (P::kMixed) fp16_range_scale2(block_max(umax, sRed), su, suinv);
 #pragma unroll
-  for (int j = 0; j < NUW; ++j) {   // Ut^T (range-scaled) into X
+  for (int j = 0; j < NUW; ++j) {
     int jt, st;
     wave_tile(w, j, NUW, jt, st);
-    store4<Op>(sUt + (16 * jt + l16) * L::LB + 16 * st + g4, narrow4<Op>(ut[j] * su));
+    store4<Op>(rU + (jt * 4 + st) * 256 + 4 * lane, narrow4<Op>(ut[j] * su));
   }
-  __syncthreads();
-
-  // ---- phase 4b: Ot = scale M Ut, as Ot^T tiles (lane: one row, 4 columns)
-#pragma unroll
-  for (int j = 0; j < NUW; ++j) {   // Ot tile (rt, jt)
-    int jt, rt;
-    wave_tile(w, j, NUW, jt, rt);
-    const f32x4 acc = tri_mma(sUt + (16 * jt + l16) * L::LB, sM + (16 * rt + l16) * L::LB, rt + 1);
-    *reinterpret_cast<f32x4*>(rO + (rt * (DV / 16) + jt) * 256 + 4 * lane) = acc * (scale / su);
-  }
+  if (tid == 0) *rUinv = suinv;
   return true;
 }
 
@@ -580,16 +554,28 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 constexpr size_t kLdsMax = 160 * 1024;
 constexpr int kOwners = 4;   // waves that own value columns
 
+// The state pass of one head runs on NS work-groups (value-column blocks
+// of dv / NS), each staging the record's shared part (W, Qbar, Khat, M,
+// dec, uinv) and its own Ut columns.  LDS: NBUF such buffers (two when they
+// fit, so that the next chunk is staged while the current one is computed)
+// + abort word.
 template <typename TIn, int DK, int DV>
 struct ConsumerLds {
   using R = Rec<TIn, DK, DV>;
-  static constexpr bool kWhole = R::BYTES + 16 <= kLdsMax;   // Ut, Ot staged too
-  static constexpr size_t STAGED = kWhole ? R::BYTES : R::SHARED_BYTES;
-  static constexpr size_t BYTES = STAGED + 16;   // + abort word
+  using Op = typename Policy<TIn>::Op;
+  static constexpr int NS = DV >= 128 ? 2 : 1;
+  static constexpr size_t SH = R::U_OFF_BYTES;
+  static constexpr size_t UPART = (size_t)kC * (DV / NS) * sizeof(Op);
+  static constexpr size_t USED = SH + UPART;
+  static constexpr size_t BUF = (USED + 255) / 256 * 256;
+  static constexpr int NBUF = 2 * BUF + 16 <= kLdsMax ? 2 : 1;
+  static constexpr size_t BYTES = NBUF * BUF + 16;
+  static_assert(BUF + 16 <= kLdsMax, "record does not fit in LDS");
+  static_assert(SH % 16 == 0 && UPART % 16 == 0, "16-byte staging");
 };
 
 template <typename TIn, int DK, int DV, bool kRing>
-__device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring,
+__device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
                                               const float* __restrict__ h0, float* __restrict__ ht,
                                               float* __restrict__ o, int b, int h, int T_len, int H,
                                               int nchunks) {
@@ -597,25 +583,24 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   using Op = typename P::Op;
   using R = Rec<TIn, DK, DV>;
   using CL = ConsumerLds<TIn, DK, DV>;
+  constexpr int NBUF = CL::NBUF;
   constexpr int NCT = DK / 16;
-  constexpr int NJ = DV / 16 / kOwners;   // column tiles per owner wave
-  constexpr int NJT = DV / 16;
-  constexpr int NV16 = CL::STAGED / 16;
+  constexpr int NJ = DV / CL::NS / 16 / kOwners;   // column tiles per owner wave
+  constexpr int NV16 = CL::USED / 16;
+  constexpr int NSH16 = CL::SH / 16;
   constexpr int kHelpers = kThreads - 64 * kOwners;   // threads of the staging waves
   constexpr int PPT = (NV16 + kHelpers - 1) / kHelpers;
-  static_assert(NJ >= 1 && NJ * kOwners * 16 == DV, "dv must be a multiple of 64");
-  const Op* sW = reinterpret_cast<const Op*>(smem) + R::W;
-  const Op* sQ = reinterpret_cast<const Op*>(smem) + R::Q;
-  const Op* sK = reinterpret_cast<const Op*>(smem) + R::K;
-  const float* sDec = reinterpret_cast<const float*>(smem + R::DEC_OFF_BYTES);
-  int* sAbort = reinterpret_cast<int*>(smem + CL::STAGED);
+  static_assert(NJ >= 1 && NJ * kOwners * 16 * CL::NS == DV, "dv must be a multiple of 64");
+  int* sAbort = reinterpret_cast<int*>(smem + NBUF * CL::BUF);
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = 4 * (lane >> 4);
   const bool owner = w < kOwners;   // wave-uniform
-  const int jt0 = (owner ? w : 0) * NJ;
+  const int jl0 = (owner ? w : 0) * NJ;           // first local column tile
+  const int jt0 = vb * NJ * kOwners + jl0;        // first column tile of the head
   const size_t bh = (size_t)b * H + h;
   auto rec_of = [&](int c) { return recbase + (size_t)(kRing ? c % ring.R : c) * R::BYTES; };
+  auto buf_of = [&](int c) { return smem + (size_t)(NBUF == 2 ? (c & 1) : 0) * CL::BUF; };
 
   // A producer on this XCD wrote the chunk into the L2 this work-group
   // reads through, so only the CU's L1 may hold stale lines of the slot: an
@@ -627,16 +612,19 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 
   // Owners and staging waves run separate loops (so that their registers
   // are allocated separately) with the same barriers per chunk c:
-  //   B1  chunk c - 1 no longer read from LDS; then every wave reads the
-  //       abort word and leaves if it is set
-  //   B2  chunk c staged in LDS (+ B2b: Ut, Ot read, when not staged)
-  // Each staging wave polls the ring by itself while the owners compute (a
-  // wave-uniform bounded spin) and sets the abort word before B1 if the wait
-  // failed; the word is only ever set, so every wave sees the same verdict
-  // after B1.
+  //   X_c  chunk c is staged in its buffer; every wave then reads the abort
+  //        word and leaves if it is set
+  //   Y_c  (one buffer only) the owners are done with chunk c
+  // With two buffers, chunk c + 1 is staged into the other buffer while the
+  // owners compute chunk c: the owners passed X_c only after finishing chunk
+  // c - 1, the buffer's previous content.  Each staging wave polls the ring
+  // by itself (a wave-uniform bounded spin) and sets the abort word before
+  // the next X if the wait failed; the word is only ever set, so every wave
+  // sees the same verdict after X.
   if (!owner) {
     const int htid = tid - 64 * kOwners;
     raw16 pre[PPT];
+    bool ok = true;
     // true once chunk c is published and may be read
     auto ready_wait = [&](int c) -> bool {
       if (!kRing) return true;
@@ -646,34 +634,47 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       return true;
     };
-    auto prefetch = [&](int c) {
-      const char* rec = rec_of(c);
+    // staged vector n: the shared part, then this work-group's Ut columns
+    const int uoff16 = (int)((R::U_OFF_BYTES + (size_t)vb * CL::UPART) / 16) - NSH16;
+    auto load = [&](int c) {
+      const raw16* rec = reinterpret_cast<const raw16*>(rec_of(c));
 #pragma unroll
       for (int i = 0; i < PPT; ++i) {
         const int n = htid + kHelpers * i;
-        if (n < NV16) pre[i] = reinterpret_cast<const raw16*>(rec)[n];
+        if (n < NV16) pre[i] = rec[n < NSH16 ? n : n + uoff16];
       }
     };
-    if (ready_wait(0)) prefetch(0);
-    else if (lane == 0) *sAbort = 1;
-    for (int c = 0; c < nchunks; ++c) {
-      __syncthreads();   // B1
-      if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
+    auto stage = [&](int c) {
+      char* buf = buf_of(c);
 #pragma unroll
       for (int i = 0; i < PPT; ++i) {
         const int n = htid + kHelpers * i;
-        if (n < NV16) reinterpret_cast<raw16*>(smem)[n] = pre[i];
+        if (n < NV16) reinterpret_cast<raw16*>(buf)[n] = pre[i];
       }
-      // every load of chunk c has returned its data before the slot is
-      // handed back below
+      // every load of chunk c has returned its data before its slot is
+      // handed back (after the next X)
       if (kRing) wait_vmem();
-      __syncthreads();   // B2
-      if (!CL::kWhole) __syncthreads();   // B2b
+    };
+    ok = ready_wait(0);
+    if (ok) {
+      load(0);
+      stage(0);
+    } else if (lane == 0) {
+      *sAbort = 1;
+    }
+    for (int c = 0; c < nchunks; ++c) {
+      __syncthreads();   // X_c
+      if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
       // chunk c has been read completely: hand its slot back
       if (kRing && htid == 0) __hip_atomic_store(ring.done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (c + 1 < nchunks) {
-        if (ready_wait(c + 1)) prefetch(c + 1);
+        ok = ready_wait(c + 1);
+        if (ok) load(c + 1);
         else if (lane == 0) *sAbort = 1;
+        if (NBUF == 1) __syncthreads();   // Y_c
+        if (ok) stage(c + 1);
+      } else if (NBUF == 1) {
+        __syncthreads();   // Y_c
       }
     }
     return;
@@ -691,36 +692,16 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 
   const bool mixed = P::kMixed;
   for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();   // B1
+    __syncthreads();   // X_c
     if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
-    __syncthreads();   // B2
-    const char* rec = rec_of(c);
-    const float* uBase = CL::kWhole ? reinterpret_cast<const float*>(smem + R::U_OFF_BYTES)
-                                    : reinterpret_cast<const float*>(rec + R::U_OFF_BYTES);
-    const float* oBase = CL::kWhole ? reinterpret_cast<const float*>(smem + R::O_OFF_BYTES)
-                                    : reinterpret_cast<const float*>(rec + R::O_OFF_BYTES);
-    f32x4 Ut[CL::kWhole ? 1 : 4][NJ], Ot[CL::kWhole ? 1 : 4][NJ];   // read before the slot is handed back
-    if (!CL::kWhole) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          Ut[t][jj] = *reinterpret_cast<const f32x4*>(uBase + (t * NJT + jt0 + jj) * 256 + 4 * lane);
-          Ot[t][jj] = *reinterpret_cast<const f32x4*>(oBase + (t * NJT + jt0 + jj) * 256 + 4 * lane);
-        }
-      if (kRing) wait_vmem();
-      __syncthreads();   // B2b
-    }
-    // Ut / Ot tile t of column tile jj: from LDS where staged, else from the
-    // registers read above
-    auto ut_of = [&](int t, int jj) -> f32x4 {
-      if (CL::kWhole) return *reinterpret_cast<const f32x4*>(uBase + (t * NJT + jt0 + jj) * 256 + 4 * lane);
-      return Ut[CL::kWhole ? 0 : t][jj];
-    };
-    auto ot_of = [&](int t, int jj) -> f32x4 {
-      if (CL::kWhole) return *reinterpret_cast<const f32x4*>(oBase + (t * NJT + jt0 + jj) * 256 + 4 * lane);
-      return Ot[CL::kWhole ? 0 : t][jj];
-    };
+    const char* buf = buf_of(c);
+    const Op* sW = reinterpret_cast<const Op*>(buf) + R::W;
+    const Op* sQ = reinterpret_cast<const Op*>(buf) + R::Q;
+    const Op* sK = reinterpret_cast<const Op*>(buf) + R::K;
+    const Op* sM = reinterpret_cast<const Op*>(buf) + R::M;
+    const float* sDec = reinterpret_cast<const float*>(buf + R::DEC_OFF_BYTES);
+    const float uinv = *reinterpret_cast<const float*>(buf + R::UINV_OFF_BYTES);
+    const Op* sU = reinterpret_cast<const Op*>(buf + CL::SH);   // local column tiles, 4 jl + st
 
     // S as an operand, range-scaled by a power of two
     float smax = 0.f;
@@ -737,6 +718,8 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       for (int jj = 0; jj < NJ; ++jj) Sb[ct][jj] = narrow4<Op>(S[ct][jj] * ss);
 
     // U = Ut - W S
+    // (each stage reads all its LDS operands of one row block before the
+    // products, so that one LDS latency is paid per block, not per product)
     f32x4 U[4][NJ];
     float umax = 0.f;
 #pragma unroll
@@ -744,16 +727,19 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       f32x4 Pv[NJ];
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) Pv[jj] = zero4();
+      Slab<Op> Wa[DK / 32];
+#pragma unroll
+      for (int sl = 0; sl < DK / 32; ++sl)
+        Wa[sl] = slab_of<Op>(load4(sW + ((2 * sl) * 4 + st) * 256 + 4 * lane),
+                             load4(sW + ((2 * sl + 1) * 4 + st) * 256 + 4 * lane));
 #pragma unroll
       for (int sl = 0; sl < DK / 32; ++sl) {
-        const Slab<Op> Wa = slab_of<Op>(load4(sW + ((2 * sl) * 4 + st) * 256 + 4 * lane),
-                                        load4(sW + ((2 * sl + 1) * 4 + st) * 256 + 4 * lane));
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) Pv[jj] = mma(Wa, slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]), Pv[jj]);
+        for (int jj = 0; jj < NJ; ++jj) Pv[jj] = mma(Wa[sl], slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]), Pv[jj]);
       }
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
-        U[st][jj] = ut_of(st, jj) - Pv[jj] * iss;
+        U[st][jj] = widen4(load4(sU + ((jl0 + jj) * 4 + st) * 256 + 4 * lane)) * uinv - Pv[jj] * iss;
         umax = fmaxf(umax, absmax4(U[st][jj]));
       }
     }
@@ -765,48 +751,79 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) Ub[st][jj] = narrow4<Op>(U[st][jj] * us);
 
-    // O = Q' S + Ot, as O^T tiles: lane l holds row 16rt + l%16, columns
-    // 16jt + 4(l/16) .. +3, stored as one 16-byte vector
+    // O = Qbar S + (scale M) U, as O^T tiles (O^T = S^T Qbar^T + U^T (scale
+    // M)^T): lane l holds row 16rt + l%16, columns 16jt + 4(l/16) .. +3,
+    // stored as one 16-byte vector
     const int t0 = c * kC;
     const bool full = t0 + kC <= T_len;   // uniform; only the last chunk is partial
     float* orow = o + (((size_t)b * T_len + t0 + l16) * H + h) * DV + 16 * jt0 + g4;
     const size_t ors = (size_t)16 * H * DV;   // 16 rows
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      f32x4 acc[NJ];
+      f32x4 accQ[NJ], accM[NJ];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) acc[jj] = zero4();
+      for (int jj = 0; jj < NJ; ++jj) {
+        accQ[jj] = zero4();
+        accM[jj] = zero4();
+      }
+      Slab<Op> Qa[DK / 32], Ma[2];
+#pragma unroll
+      for (int sl = 0; sl < DK / 32; ++sl)
+        Qa[sl] = slab_of<Op>(load4(sQ + ((2 * sl) * 4 + rt) * 256 + 4 * lane),
+                             load4(sQ + ((2 * sl + 1) * 4 + rt) * 256 + 4 * lane));
+      const int nms = rt < 2 ? 1 : 2;   // slabs of M's row block rt that are not all zero
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+        if (sl < nms)
+          Ma[sl] = slab_of<Op>(load4(sM + ((2 * sl) * 4 + rt) * 256 + 4 * lane),
+                               load4(sM + ((2 * sl + 1) * 4 + rt) * 256 + 4 * lane));
 #pragma unroll
       for (int sl = 0; sl < DK / 32; ++sl) {
-        const Slab<Op> Qa = slab_of<Op>(load4(sQ + ((2 * sl) * 4 + rt) * 256 + 4 * lane),
-                                        load4(sQ + ((2 * sl + 1) * 4 + rt) * 256 + 4 * lane));
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) acc[jj] = mma(slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]), Qa, acc[jj]);
+        for (int jj = 0; jj < NJ; ++jj) accQ[jj] = mma(slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]), Qa[sl], accQ[jj]);
+      }
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        if (sl < nms) {
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+            accM[jj] = mma(slab_of<Op>(Ub[2 * sl][jj], Ub[2 * sl + 1][jj]), Ma[sl], accM[jj]);
+        }
       }
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
-        const f32x4 r = acc[jj] * iss + ot_of(rt, jj);
+        const f32x4 r = accQ[jj] * iss + accM[jj] * ius;
         if (full || t0 + 16 * rt + l16 < T_len) *reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj) = r;
       }
     }
 
     // S <- e^{Gamma_C} S + Khat^T U
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
-      f32x4 acc[NJ];
+    for (int cp = 0; cp < NCT; cp += 2) {   // two column tiles of S per LDS batch
+      Slab<Op> Ka[2][2];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) acc[jj] = zero4();
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const Slab<Op> Ka = slab_of<Op>(load4(sK + ((2 * sl) * NCT + ct) * 256 + 4 * lane),
-                                        load4(sK + ((2 * sl + 1) * NCT + ct) * 256 + 4 * lane));
+        for (int sl = 0; sl < 2; ++sl)
+          Ka[cc][sl] = slab_of<Op>(load4(sK + ((2 * sl) * NCT + cp + cc) * 256 + 4 * lane),
+                                   load4(sK + ((2 * sl + 1) * NCT + cp + cc) * 256 + 4 * lane));
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) acc[jj] = mma(Ka, slab_of<Op>(Ub[2 * sl][jj], Ub[2 * sl + 1][jj]), acc[jj]);
+      for (int cc = 0; cc < 2; ++cc) {
+        const int ct = cp + cc;
+        const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
+        f32x4 acc[NJ];
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) acc[jj] = zero4();
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) acc[jj] = mma(Ka[cc][sl], slab_of<Op>(Ub[2 * sl][jj], Ub[2 * sl + 1][jj]), acc[jj]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) S[ct][jj] = S[ct][jj] * d + acc[jj] * ius;
       }
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) S[ct][jj] = S[ct][jj] * d + acc[jj] * ius;
     }
+    if (NBUF == 1) __syncthreads();   // Y_c
   }
 
   if (ht) {
@@ -820,25 +837,26 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   }
 }
 
-// Two-stage schedule, stage 2: one work-group per head.
+// Two-stage schedule, stage 2: NS work-groups per head.
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __restrict__ ws,
                                                               const float* __restrict__ h0, float* __restrict__ ht,
                                                               float* __restrict__ o, int T_len, int H, int nchunks) {
-  __shared__ __align__(16) char smem[ConsumerLds<TIn, DK, DV>::BYTES];
-  const int bh = blockIdx.x;
+  using CL = ConsumerLds<TIn, DK, DV>;
+  __shared__ __align__(16) char smem[CL::BYTES];
+  const int bh = blockIdx.x / CL::NS, vb = blockIdx.x % CL::NS;
   consume_chain<TIn, DK, DV, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
-                                    Ring{nullptr, nullptr, nullptr, nullptr, 1}, h0, ht, o, bh / H, bh % H, T_len,
-                                    H, nchunks);
+                                    Ring{nullptr, nullptr, nullptr, nullptr, 1}, vb, h0, ht, o, bh / H, bh % H,
+                                    T_len, H, nchunks);
 }
 
 // ---------------------------------------------------------------------------
 // Fused single-pass schedule: one persistent work-group per CU.  Heads are
 // dealt to the 8 XCDs (work-group i runs on XCD i % 8); on each XCD the
-// first work-groups are state-pass consumers (one per head, resident for
-// the whole call) and the rest are producers that take
-// (chunk, head) items of that XCD's heads in chunk-major order from a queue
-// and write each chunk's record into the head's ring of R slots.  Records
+// first work-groups are state-pass consumers (NS per head, resident for
+// the whole call) and the rest are producers that share the (chunk, head)
+// items of that XCD's heads, in chunk-major order, round robin, and write
+// each chunk's record into the head's ring of R slots.  Records
 // therefore live only in L2 / Infinity Cache between producer and consumer.
 // Ordering: producer stores, then a release in every wave, then
 // ready[slot] = (c + 1) << 4 | XCD; the consumer polls ready, then an
@@ -849,14 +867,14 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
 // the consumer publishes its XCD, the producer tags the flag with its own)
 // and use agent-scope fences whenever the two differ.  A slot is reused only after every
 // consumer of the head stored done >= c + 1 for the chunk that held it.  A
-// producer takes its next item and starts loading that item's inputs as soon
-// as the current item's inputs are staged, so loads overlap the compute.
+// producer starts loading its next item's inputs as soon as the current
+// item's inputs are staged, so loads overlap the compute.
 // Every wait is bounded (kSpinLimit); on a timeout the work-group sets the
 // error word and leaves, so the grid always drains.
 //
 // ctrl layout (ints, zeroed before the launch):
-//   [0..7]   per-XCD item counters      [8] error word
-//   [16 ..)  ready[nheads][R], then done[nheads], then cxcc[nheads]
+//   [0..7]   unused                     [8] error word
+//   [16 ..)  ready[nheads][R], then done[nheads][NS], then cxcc[nheads][NS]
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct FusedLds {
@@ -878,38 +896,31 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   int* sWord = reinterpret_cast<int*>(smem + FusedLds<TIn, DK, DV>::BYTES - 16);
   const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
   const int nloc = nheads > xcd ? (nheads - xcd + 7) / 8 : 0;   // heads j = xcd + 8m of this launch
+  constexpr int NS = ConsumerLds<TIn, DK, DV>::NS;
   int* err = ctrl + 8;
   int* ready = ctrl + 16;
   int* done = ready + nheads * R;
-  int* cxcc = done + nheads;
+  int* cxcc = done + nheads * NS;
 
-  if (li < nloc) {   // consumer of head jh
-    const int jh = xcd + 8 * li, bh = head0 + jh;
+  if (li < nloc * NS) {   // consumer vb of head jh
+    const int jh = xcd + 8 * (li / NS), vb = li % NS, bh = head0 + jh;
     consume_chain<TIn, DK, DV, true>(smem, ring + (size_t)jh * R * Rc::BYTES,
-                                     Ring{ready + jh * R, done + jh, err, cxcc + jh, R}, h0, ht, o, bh / H, bh % H,
-                                     T_len, H, nchunks);
+                                     Ring{ready + jh * R, done + jh * NS + vb, err, cxcc + jh * NS + vb, R}, vb, h0,
+                                     ht, o, bh / H, bh % H, T_len, H, nchunks);
     return;
   }
 
-  // producer: items of this XCD's heads in chunk-major order
+  // producer p of this XCD's P producers: items p, p + P, p + 2P, ... of
+  // this XCD's heads in chunk-major order (item = chunk * nloc + local head).
+  // No deadlock: the smallest item any producer waits on only needs chunks
+  // of smaller items, and every smaller item is finished because each
+  // producer handles its items in increasing order.
   const int total = nloc * nchunks;
+  const int P = (int)(gridDim.x >> 3) - nloc * NS;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int my_xcc = xcc_id();
-  // next item, taken by wave 0 and broadcast (wave-uniform result)
-  auto take = [&]() -> int {
-    if (w == 0) {
-      int it = 0;
-      if (lane == 0) it = __hip_atomic_fetch_add(ctrl + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      it = __builtin_amdgcn_readfirstlane(it);
-      if (lane == 0) *sWord = it;
-    }
-    __syncthreads();
-    const int it = __builtin_amdgcn_readfirstlane(*sWord);
-    __syncthreads();
-    return it;
-  };
   InRegs<TIn, DK, DV> in;
-  int it = take();
+  int it = li - nloc * NS;
   if (it >= total) return;
   {
     const int jh = xcd + 8 * (it % nloc), bh = head0 + jh;
@@ -917,19 +928,19 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   }
   for (;;) {
     const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
-    int nxt = total;
-    // Runs once this chunk's inputs are in LDS: take the next item and start
-    // loading its inputs, then wait until the ring slot of chunk c is free
-    // (it held chunk c - R, which every consumer must have read).
+    const int nxt = it + P;
+    // Runs once this chunk's inputs are in LDS: start loading the next
+    // item's inputs, then wait until the ring slot of chunk c is free (it
+    // held chunk c - R, which the head's consumer must have read).
     auto after_stage = [&]() -> bool {
-      nxt = take();
       if (nxt < total) {
         const int jn = xcd + 8 * (nxt % nloc), bn = head0 + jn;
         load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bn / H, bn % H, T_len, H, nxt / nloc);
       }
       if (c < R) return true;
       if (w == 0) {
-        const bool ok = spin_until_geq(done + jh, c - R + 1, err) >= 0;
+        bool ok = true;
+        for (int vb = 0; vb < NS && ok; ++vb) ok = spin_until_geq(done + jh * NS + vb, c - R + 1, err) >= 0;
         if (lane == 0) *sWord = ok ? 1 : 0;
       }
       __syncthreads();
@@ -940,12 +951,14 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     if (!produce_chunk<TIn, DK, DV>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
                                     ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage))
       return;
-    // Release.  If the head's consumer runs on this XCD it reads through the
-    // same L2, so it is enough that every wave's record stores have reached
-    // the L2; otherwise an agent-scope release (L2 write-back).
-    const int cx = __builtin_amdgcn_readfirstlane(
-        __hip_atomic_load(cxcc + jh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (cx == my_xcc + 1) wait_vmem();
+    // Release.  If the head's consumers run on this XCD they read through
+    // the same L2, so it is enough that every wave's record stores have
+    // reached the L2; otherwise an agent-scope release (L2 write-back).
+    bool same = true;
+    for (int vb = 0; vb < NS; ++vb)
+      same = same && __builtin_amdgcn_readfirstlane(__hip_atomic_load(cxcc + jh * NS + vb, __ATOMIC_RELAXED,
+                                                                      __HIP_MEMORY_SCOPE_AGENT)) == my_xcc + 1;
+    if (same) wait_vmem();
     else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (w == 0 && lane == 0)
@@ -963,25 +976,26 @@ __global__ void clear_ints_kernel(int* p, int n) {
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-constexpr int kRingSlots = 4;         // ring slots per head (fused schedule)
+constexpr int kRingSlots = 8;         // ring slots per head (fused schedule)
 constexpr int kMaxWgPerXcd = 32;      // MI355X: 256 CUs in 8 XCDs
 
 // Heads one fused launch can serve with `per_xcd` work-groups per XCD:
 // keep at least a quarter of each XCD (and >= 2 work-groups) as producers.
-static int fused_heads_per_launch(int per_xcd) {
+static int fused_heads_per_launch(int per_xcd, int ns) {
   const int prod = per_xcd / 4 > 2 ? per_xcd / 4 : 2;
-  const int hx = per_xcd - prod;
+  const int hx = (per_xcd - prod) / ns;
   return hx > 0 ? 8 * hx : 0;
 }
 
 template <typename TIn, int DK, int DV>
 static size_t fused_ctrl_bytes(int nheads) {
-  return ((size_t)(16 + nheads * kRingSlots + 2 * nheads) * 4 + 255) / 256 * 256;
+  constexpr int NS = ConsumerLds<TIn, DK, DV>::NS;
+  return ((size_t)(16 + nheads * kRingSlots + 2 * NS * nheads) * 4 + 255) / 256 * 256;
 }
 
 template <typename TIn, int DK, int DV>
 static size_t fused_ws_bytes(int nbh) {
-  const int cap = fused_heads_per_launch(kMaxWgPerXcd);
+  const int cap = fused_heads_per_launch(kMaxWgPerXcd, ConsumerLds<TIn, DK, DV>::NS);
   const int nh = nbh < cap ? nbh : cap;
   return fused_ctrl_bytes<TIn, DK, DV>(nh) + (size_t)nh * kRingSlots * Rec<TIn, DK, DV>::BYTES;
 }
@@ -998,7 +1012,8 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   int per_xcd = cus / 8;
   if (per_xcd > kMaxWgPerXcd) per_xcd = kMaxWgPerXcd;
-  int batch = fused_heads_per_launch(per_xcd);
+  constexpr int NS = ConsumerLds<TIn, DK, DV>::NS;
+  int batch = fused_heads_per_launch(per_xcd, NS);
   if (batch <= 0) return hipErrorInvalidConfiguration;
   // what the workspace can hold
   while (batch > 0 && fused_ctrl_bytes<TIn, DK, DV>(batch) + (size_t)batch * kRingSlots * Rec<TIn, DK, DV>::BYTES > ws_bytes)
@@ -1008,7 +1023,7 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   char* ring = reinterpret_cast<char*>(ws) + fused_ctrl_bytes<TIn, DK, DV>(batch);
   for (int head0 = 0; head0 < nbh; head0 += batch) {
     const int nh = nbh - head0 < batch ? nbh - head0 : batch;
-    const int nctrl = 16 + nh * kRingSlots + 2 * nh;
+    const int nctrl = 16 + nh * kRingSlots + 2 * NS * nh;
     hipLaunchKernelGGL(clear_ints_kernel, dim3((nctrl + 255) / 256), dim3(256), 0, st, ctrl, nctrl);
     hipLaunchKernelGGL((fused_fwd_kernel<TIn, DK, DV>), dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q,
                        (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len,
@@ -1033,7 +1048,7 @@ static hipError_t go_stages(const void* q, const void* k, const void* v, const v
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
-    hipLaunchKernelGGL((state_pass_kernel<TIn, DK, DV>), dim3(nbh), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((state_pass_kernel<TIn, DK, DV>), dim3(ConsumerLds<TIn, DK, DV>::NS * nbh), dim3(kThreads), 0, st,
                        (const char*)ws, h0, ht, o, T_len, H, nchunks);
     return hipGetLastError();
   }
