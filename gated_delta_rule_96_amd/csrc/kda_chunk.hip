@@ -120,7 +120,7 @@ __device__ __forceinline__ Half<float> load_half_col(const float* p, int ld) {
 }
 
 __device__ __forceinline__ float block_max(float x, float* sred) {
-  x = wave_max(x);
+  x = wave_max_dpp(x);
   if ((threadIdx.x & 63) == 0) sred[threadIdx.x >> 6] = x;
   __syncthreads();
   float m = sred[0];
@@ -220,6 +220,11 @@ struct IntraLds {
 // The 10 tiles (a, b) of the lower 4x4 block triangle: diagonal first.
 __constant__ signed char kTileA[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
 __constant__ signed char kTileB[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
+// Gram tiles of wave w (-1: none): a diagonal tile (the costlier kind, with
+// split operands) for waves 0-3, two off-diagonal tiles for waves 4 and 5,
+// one for waves 6 and 7.  The Khat / Qbar tile work is spread over the
+// waves with lighter Gram shares (see kTaskBegin).
+__constant__ signed char kWaveTile[8][2] = {{0, -1}, {1, -1}, {2, -1}, {3, -1}, {4, 5}, {6, 7}, {8, -1}, {9, -1}};
 
 // Builds the record of chunk `ch` of head (b, h) at `rec`.  Called by a
 // whole work-group of kThreads threads; `smem` holds IntraLds::BYTES.
@@ -310,8 +315,8 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
 
   // ---- phase 1: Gram tiles (A -> LDS, scale M -> record), Khat, dec, Qbar
   for (int ti = 0; ti < 2; ++ti) {
-    const int idx = w + kNW * ti;
-    if (idx >= 10) break;
+    const int idx = kWaveTile[w][ti];
+    if (idx < 0) break;
     const int a = kTileA[idx], bb = kTileB[idx];
     const bool diag = a == bb;
     const int p = 16 * a - 1;
@@ -360,28 +365,34 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     const int zt = w - 2, kt = kTileA[4 + zt], rt = kTileB[4 + zt];
     store4<Op>(rM + (kt * 4 + rt) * 256 + 4 * lane, narrow4<Op>(zero4()));
   }
-  // Khat tiles (st, ct) and dec
-  for (int n = tid; n < DK * 16; n += kThreads) {
-    const int tile = n >> 6, ln = n & 63;
-    const int st = tile / (DK / 16), ct = tile % (DK / 16);
-    const int col = 16 * ct + (ln & 15), row0 = 16 * st + 4 * (ln >> 4);
-    const float gC = sG[(kC - 1) * L::LG + col];
-    f32x4 val;
+  // Khat tiles and Qbar tiles: NTK = DK / 4 tasks of each kind, task t of
+  // wave w in [kTaskBegin(w), kTaskBegin(w + 1)); a Khat task is one 16x16
+  // tile (st, ct), a Qbar task one tile (ct, rt)
+  constexpr int NTK = DK / 4;
+  auto task_begin = [](int wv) -> int {
+    // waves 0-3 take 5/32 of the tasks each, 4-5 none, 6-7 6/32 each
+    constexpr int T = 2 * NTK;
+    return wv <= 4 ? wv * (5 * T / 32) : (wv <= 6 ? 4 * (5 * T / 32) : 4 * (5 * T / 32) + (T - 4 * (5 * T / 32)) / 2);
+  };
+  const int tb = task_begin(w), te = w == kNW - 1 ? 2 * NTK : task_begin(w + 1);
+  for (int t = tb; t < te; ++t) {
+    if (t < NTK) {   // Khat tile t: lane holds Khat[16st + g4 + i][16ct + l16]
+      const int st = t / (DK / 16), ct = t % (DK / 16);
+      const int col = 16 * ct + l16, row0 = 16 * st + g4;
+      const float gC = sG[(kC - 1) * L::LG + col];
+      f32x4 val;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      val[i] = to_f32(sK[(row0 + i) * L::LK + col]) * exp2_fast(gC - sG[(row0 + i) * L::LG + col]);
-    store4<Op>(rK + tile * 256 + 4 * ln, narrow4<Op>(val));
+      for (int i = 0; i < 4; ++i)
+        val[i] = to_f32(sK[(row0 + i) * L::LK + col]) * exp2_fast(gC - sG[(row0 + i) * L::LG + col]);
+      store4<Op>(rK + t * 256 + 4 * lane, narrow4<Op>(val));
+    } else {         // Qbar = scale e^Gamma q, tile (ct, rt): lane holds Qbar[16rt + l16][16ct + g4 + i]
+      const int qt = t - NTK, ct = qt / 4, rt = qt % 4;
+      const int row = 16 * rt + l16, col = 16 * ct + g4;
+      const f32x4 qb = widen4(load4(sQ + row * L::LK + col)) * exp2v(*reinterpret_cast<const f32x4*>(sG + row * L::LG + col));
+      store4<Op>(rQ + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(qb * scale));
+    }
   }
-  if (tid < DK) rDec[tid] = exp2_fast(sG[(kC - 1) * L::LG + tid]);
-  // Qbar = scale e^Gamma q, tiles (ct, rt): lane holds Qbar[16rt + l16][16ct + g4 + i]
-#pragma unroll
-  for (int j = 0; j < NQW; ++j) {
-    int ct, rt;
-    wave_tile(w, j, NQW, ct, rt);
-    const int row = 16 * rt + l16, col = 16 * ct + g4;
-    const f32x4 qb = widen4(load4(sQ + row * L::LK + col)) * exp2v(*reinterpret_cast<const f32x4*>(sG + row * L::LG + col));
-    store4<Op>(rQ + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(qb * scale));
-  }
+  if (tid >= kThreads - DK) rDec[tid - (kThreads - DK)] = exp2_fast(sG[(kC - 1) * L::LG + tid - (kThreads - DK)]);
   __syncthreads();   // sQ is dead from here on; R2 becomes Tm
 
   // ---- phase 2: X = (I + A)^-1 by 16x16 blocks, fp32
@@ -926,13 +937,33 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     const int jh = xcd + 8 * (it % nloc), bh = head0 + jh;
     load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, it / nloc);
   }
+  // Publishes item `pi` (its record stores were issued by every wave).
+  // Release: if the head's consumers run on this XCD they read through the
+  // same L2, so it is enough that every wave's record stores have reached
+  // the L2; otherwise an agent-scope release (L2 write-back).
+  auto publish = [&](int pi) {
+    const int pc = pi / nloc, pj = xcd + 8 * (pi % nloc);
+    bool same = true;
+    for (int vb = 0; vb < NS; ++vb)
+      same = same && __builtin_amdgcn_readfirstlane(__hip_atomic_load(cxcc + pj * NS + vb, __ATOMIC_RELAXED,
+                                                                      __HIP_MEMORY_SCOPE_AGENT)) == my_xcc + 1;
+    if (same) wait_vmem();
+    else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (w == 0 && lane == 0)
+      __hip_atomic_store(ready + pj * R + pc % R, ((pc + 1) << 4) | my_xcc, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  };
+  int pending = -1;   // item whose record is written but not yet published
   for (;;) {
     const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
     const int nxt = it + P;
-    // Runs once this chunk's inputs are in LDS: start loading the next
-    // item's inputs, then wait until the ring slot of chunk c is free (it
-    // held chunk c - R, which the head's consumer must have read).
+    // Runs once this chunk's inputs are in LDS: publish the previous item
+    // (its record stores drained while this item was staged), start loading
+    // the next item's inputs, then wait until the ring slot of chunk c is
+    // free (it held chunk c - R, which the head's consumers must have read).
     auto after_stage = [&]() -> bool {
+      if (pending >= 0) publish(pending);
       if (nxt < total) {
         const int jn = xcd + 8 * (nxt % nloc), bn = head0 + jn;
         load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bn / H, bn % H, T_len, H, nxt / nloc);
@@ -951,20 +982,11 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     if (!produce_chunk<TIn, DK, DV>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
                                     ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage))
       return;
-    // Release.  If the head's consumers run on this XCD they read through
-    // the same L2, so it is enough that every wave's record stores have
-    // reached the L2; otherwise an agent-scope release (L2 write-back).
-    bool same = true;
-    for (int vb = 0; vb < NS; ++vb)
-      same = same && __builtin_amdgcn_readfirstlane(__hip_atomic_load(cxcc + jh * NS + vb, __ATOMIC_RELAXED,
-                                                                      __HIP_MEMORY_SCOPE_AGENT)) == my_xcc + 1;
-    if (same) wait_vmem();
-    else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (w == 0 && lane == 0)
-      __hip_atomic_store(ready + jh * R + c % R, ((c + 1) << 4) | my_xcc, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    if (nxt >= total) return;
+    pending = it;
+    if (nxt >= total) {
+      publish(pending);
+      return;
+    }
     it = nxt;
   }
 }
