@@ -145,7 +145,8 @@ __device__ __forceinline__ void wave_tile(int w, int j, int per_wave, int& x, in
 }
 
 // One chunk's raw inputs in registers (rows past the end of the sequence
-// are zero): 16-byte vectors of k, q, g and v rows, and beta.
+// are zero): 16-byte vectors of k, q, g and v rows (k, q, g row-major over
+// the threads, v column-block-major), and beta.
 template <typename TIn, int DK, int DV>
 struct InRegs {
   static constexpr int VE = 16 / sizeof(TIn);
@@ -179,19 +180,50 @@ __device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* 
     in.q[i] = ok ? *reinterpret_cast<const raw16*>(q + base_k + r * tokk + c) : zero16;
     in.g[i] = (ok && g) ? *reinterpret_cast<const raw16*>(g + base_k + r * tokk + c) : zero16;
   }
+  // v: consecutive lanes take consecutive rows of one column block, so that
+  // the transposed LDS staging of V is free of bank conflicts
 #pragma unroll
   for (int i = 0; i < IR::NV; ++i) {
     const int n = tid + kThreads * i;
-    const int r = n / (DV / VE), c = (n % (DV / VE)) * VE;
+    const int r = n % kC, c = (n / kC) * VE;
     in.v[i] = r < Lrows ? *reinterpret_cast<const raw16*>(v + base_v + r * tokv + c) : zero16;
   }
   in.beta = (tid < kC && tid < Lrows) ? to_f32(beta[((size_t)b * T_len + t0 + tid) * H + h]) : 0.f;
 }
 
+// The BLK rows of channel c from the chunk's block starts bs[a] = Gamma_p(a)
+// (a = 0..3) and bs[4] = Gamma_C, in fp64 (natural log units): every
+// exponent that involves a block start is formed in fp64 and rounded once,
+// so its fp32 error is set by its own size, not by the size of Gamma.
+template <int DK>
+__device__ __forceinline__ void block_exponents(float* sBlk, int c, const double* bs) {
+  constexpr double l2e = 1.4426950408889634;
+  const int pa[6] = {1, 2, 3, 2, 3, 3}, pb[6] = {0, 0, 0, 1, 1, 2};
+#pragma unroll
+  for (int i = 0; i < 6; ++i) sBlk[i * DK + c] = (float)((bs[pa[i]] - bs[pb[i]]) * l2e);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    sBlk[(6 + a) * DK + c] = (float)((bs[4] - bs[a]) * l2e);
+    const double x = bs[a] * l2e;
+    const float hi = (float)x;
+    sBlk[(10 + a) * DK + c] = hi;
+    sBlk[(14 + a) * DK + c] = (float)(x - (double)hi);
+  }
+  sBlk[18 * DK + c] = (float)(bs[4] * l2e);
+}
+
 // ---------------------------------------------------------------------------
 // Intra-chunk kernel: one work-group (8 waves) per (b*h, chunk).
 // LDS regions are reused across phases (lifetimes in brackets):
-//   G  : fp32 Gamma*log2(e) [C][DK+4]                          [all]
+//   G  : fp32 (Gamma - Gamma_p)*log2(e) [C][DK+4], p = the row before the
+//        row's 16-row block (sums local to the block)              [all]
+//   BLK: fp32 [19][DK], exponents built from the block starts Gamma_p,
+//        p = 16a - 1, summed in fp64 (times log2(e)):               [phase 1]
+//        rows 0-5   Gamma_p(a) - Gamma_p(b) for the off-diagonal tiles
+//                   (a, b) in kTileA/kTileB order 4..9
+//        rows 6-9   Gamma_C - Gamma_p(a), a = 0..3 (C = the chunk's last row)
+//        rows 10-13 Gamma_p(a) rounded to fp32, rows 14-17 the remainder
+//        row 18     Gamma_C
 //   R1 : k [C][DK] (in)  | Kbar^T [DK][C] (Op) | V^T [DV][C] (Op)
 //   X  : A, X fp32 [C][C+4] each
 //   R2 : q [C][DK] (in)  | Tm [C][C] (Op)
@@ -212,7 +244,8 @@ struct IntraLds {
   static constexpr size_t X_SIZE = 2 * (size_t)kC * LA * 4;
   static constexpr size_t R2 = X + X_SIZE;
   static constexpr size_t R2_SIZE = mx((size_t)kC * LK * sizeof(TIn), (size_t)kC * LB * sizeof(Op));
-  static constexpr size_t BETA = R2 + R2_SIZE;
+  static constexpr size_t BLK = R2 + R2_SIZE;   // fp32 [19][DK], see above
+  static constexpr size_t BETA = BLK + 19 * (size_t)DK * 4;
   static constexpr size_t RED = BETA + kC * 4;
   static constexpr size_t BYTES = RED + 16 * 4;
 };
@@ -221,10 +254,10 @@ struct IntraLds {
 __constant__ signed char kTileA[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
 __constant__ signed char kTileB[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
 // Gram tiles of wave w (-1: none): a diagonal tile (the costlier kind, with
-// split operands) for waves 0-3, two off-diagonal tiles for waves 4 and 5,
-// one for waves 6 and 7.  The Khat / Qbar tile work is spread over the
-// waves with lighter Gram shares (see kTaskBegin).
-__constant__ signed char kWaveTile[8][2] = {{0, -1}, {1, -1}, {2, -1}, {3, -1}, {4, 5}, {6, 7}, {8, -1}, {9, -1}};
+// split operands) for waves 0-3; two off-diagonal tiles of one row block for
+// waves 4 and 5 (they share the row operand); one for waves 6 and 7.  The
+// Khat tile work goes to the waves with lighter Gram shares.
+__constant__ signed char kWaveTile[8][2] = {{0, -1}, {1, -1}, {2, -1}, {3, -1}, {5, 7}, {6, 8}, {4, -1}, {9, -1}};
 
 // Builds the record of chunk `ch` of head (b, h) at `rec`.  Called by a
 // whole work-group of kThreads threads; `smem` holds IntraLds::BYTES.
@@ -252,6 +285,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   TIn* sQ = reinterpret_cast<TIn*>(smem + L::R2);
   Op* sTm = reinterpret_cast<Op*>(smem + L::R2);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
+  float* sBlk = reinterpret_cast<float*>(smem + L::BLK);
   float* sRed = reinterpret_cast<float*>(smem + L::RED);
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -279,7 +313,10 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     *reinterpret_cast<raw16*>(sQ + r * L::LK + c) = in.q[i];
     if (!gcum) {
 #pragma unroll
-      for (int x = 0; x < VE; ++x) sG[r * L::LG + c + x] = raw_elem<TIn>(in.g[i], x);
+      for (int x = 0; x < VE; x += 4)
+        *reinterpret_cast<f32x4*>(sG + r * L::LG + c + x) =
+            f32x4{raw_elem<TIn>(in.g[i], x), raw_elem<TIn>(in.g[i], x + 1), raw_elem<TIn>(in.g[i], x + 2),
+                  raw_elem<TIn>(in.g[i], x + 3)};
     }
   }
   if (tid < kC) sBeta[tid] = in.beta;
@@ -288,111 +325,161 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   for (int i = 0; i < IR::NV; ++i) vreg[i] = in.v[i];
   constexpr int NVV = kC * DV / VE;
   constexpr int VPT = IR::NV;
+  // Gamma, kept as sums local to each 16-row block (G) plus the block
+  // starts (BLK): the exponents of the intra-block factors are then sums of
+  // at most 16 decays rather than differences of two long cumulative sums.
   if (gcum) {
     for (int n = tid; n < kC * DK / 4; n += kThreads) {
       const int r = n / (DK / 4), c = (n % (DK / 4)) * 4;
-      const int rr = min(r, Lrows - 1);
+      const int rr = min(r, Lrows - 1), pr = min(16 * (r / 16) - 1, Lrows - 1);
       const f32x4 gv = *reinterpret_cast<const f32x4*>(gcum + base_k + rr * tokk + c);
-      *reinterpret_cast<f32x4*>(sG + r * L::LG + c) = gv * kLog2e;
+      const f32x4 gpv = pr >= 0 ? *reinterpret_cast<const f32x4*>(gcum + base_k + pr * tokk + c) : zero4();
+      *reinterpret_cast<f32x4*>(sG + r * L::LG + c) = (gv - gpv) * kLog2e;
+    }
+    if (tid < DK) {
+      double bs[5];
+#pragma unroll
+      for (int a = 0; a < 5; ++a) {
+        const int pr = min(a < 4 ? 16 * a - 1 : kC - 1, Lrows - 1);
+        bs[a] = pr >= 0 ? (double)gcum[base_k + pr * tokk + tid] : 0.0;
+      }
+      block_exponents<DK>(sBlk, tid, bs);
     }
   } else {
-    // inclusive scan of each channel over the chunk's rows, in row order
+    // thread (block a, channel c) sums its block's 16 rows in row order; the
+    // block starts are the block totals above, added in block order
+    float* sTot = sA;   // [4][DK], free until the Gram tiles
+    __syncthreads();
+    if (tid < 4 * DK) {
+      const int c = tid % DK, a = tid / DK;
+      float gr[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) gr[i] = sG[(16 * a + i) * L::LG + c];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) gr[i] += gr[i - 1];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sG[(16 * a + i) * L::LG + c] = gr[i] * kLog2e;
+      sTot[a * DK + c] = gr[15];
+    }
     __syncthreads();
     if (tid < DK) {
-      float gr[kC];
+      double bs[5];
+      bs[0] = 0.0;
 #pragma unroll
-      for (int r = 0; r < kC; ++r) gr[r] = sG[r * L::LG + tid];
-      float acc = 0.f;
-#pragma unroll
-      for (int r = 0; r < kC; ++r) {
-        acc += gr[r];
-        sG[r * L::LG + tid] = acc * kLog2e;
-      }
+      for (int a = 0; a < 4; ++a) bs[a + 1] = bs[a] + (double)sTot[a * DK + tid];
+      block_exponents<DK>(sBlk, tid, bs);
     }
   }
   __syncthreads();
   if (!after_stage()) return false;
 
-  // ---- phase 1: Gram tiles (A -> LDS, scale M -> record), Khat, dec, Qbar
-  for (int ti = 0; ti < 2; ++ti) {
-    const int idx = kWaveTile[w][ti];
-    if (idx < 0) break;
-    const int a = kTileA[idx], bb = kTileB[idx];
-    const bool diag = a == bb;
-    const int p = 16 * a - 1;
-    const int r = 16 * a + l16, s = 16 * bb + l16;
-    f32x4 accA = zero4(), accM = zero4();
+  // ---- phase 1: Gram tiles (A -> LDS, scale M -> record), Khat, dec,
+  // Qbar (record) and Kbar (registers, staged transposed after the solve)
+  {
+    const int t0i = kWaveTile[w][0], t1i = kWaveTile[w][1];
+    const int ntile = t0i < 0 ? 0 : (t1i < 0 ? 1 : 2);   // wave-uniform
+    if (ntile > 0) {
+      // both tiles of a wave share the row block a, hence the row operand
+      const int a = kTileA[t0i];
+      const int bb0 = kTileB[t0i], bb1 = ntile > 1 ? kTileB[t1i] : bb0;
+      const bool diag = a == bb0;   // only single-tile waves hold a diagonal tile
+      const int r = 16 * a + l16, s0 = 16 * bb0 + l16, s1 = 16 * bb1 + l16;
+      f32x4 accA0 = zero4(), accM0 = zero4(), accA1 = zero4(), accM1 = zero4();
 #pragma unroll 2
-    for (int sl = 0; sl < DK / 32; ++sl) {
-      const int c0 = 32 * sl + g4, c1 = c0 + 16;
-      const f32x4 gp0 = p >= 0 ? *reinterpret_cast<const f32x4*>(sG + p * L::LG + c0) : zero4();
-      const f32x4 gp1 = p >= 0 ? *reinterpret_cast<const f32x4*>(sG + p * L::LG + c1) : zero4();
-      const f32x4 er0 = exp2v(*reinterpret_cast<const f32x4*>(sG + r * L::LG + c0) - gp0);
-      const f32x4 er1 = exp2v(*reinterpret_cast<const f32x4*>(sG + r * L::LG + c1) - gp1);
-      const f32x4 fs0 = exp2v(gp0 - *reinterpret_cast<const f32x4*>(sG + s * L::LG + c0));
-      const f32x4 fs1 = exp2v(gp1 - *reinterpret_cast<const f32x4*>(sG + s * L::LG + c1));
-      const f32x4 rk0 = widen4(load4(sK + r * L::LK + c0)) * er0, rk1 = widen4(load4(sK + r * L::LK + c1)) * er1;
-      const f32x4 rq0 = widen4(load4(sQ + r * L::LK + c0)) * er0, rq1 = widen4(load4(sQ + r * L::LK + c1)) * er1;
-      const f32x4 ck0 = widen4(load4(sK + s * L::LK + c0)) * fs0, ck1 = widen4(load4(sK + s * L::LK + c1)) * fs1;
-      const Slab<Gm> RK = make_slab<Gm>(rk0, rk1);
-      if (P::kMixed && diag) {
-        Slab<Gm> CKh, CKl, RQh, RQl;
-        make_slab_split<Gm>(ck0, ck1, CKh, CKl);
-        make_slab_split<Gm>(rq0, rq1, RQh, RQl);
-        accA = mma(CKh, RK, accA);
-        accM = mma(CKh, RQh, accM);
-        accM = mma(CKl, RQh, accM);
-        accM = mma(CKh, RQl, accM);
-      } else {
-        const Slab<Gm> CK = make_slab<Gm>(ck0, ck1);
-        accA = mma(CK, RK, accA);                         // A^T tile: lane holds A[r][16bb + g4 + i]
-        accM = mma(CK, make_slab<Gm>(rq0, rq1), accM);    // M^T tile: lane holds M[r][16bb + g4 + i]
+      for (int sl = 0; sl < DK / 32; ++sl) {
+        const int c0 = 32 * sl + g4, c1 = c0 + 16;
+        // row factor e^{Gamma_r - Gamma_p}: the local sum itself
+        const f32x4 er0 = exp2v(*reinterpret_cast<const f32x4*>(sG + r * L::LG + c0));
+        const f32x4 er1 = exp2v(*reinterpret_cast<const f32x4*>(sG + r * L::LG + c1));
+        // column factor e^{Gamma_p - Gamma_s} = e^{(Gamma_p - Gamma_p') - local_s}, p' = s's block start
+        const f32x4 d00 = diag ? zero4() : *reinterpret_cast<const f32x4*>(sBlk + (t0i - 4) * DK + c0);
+        const f32x4 d01 = diag ? zero4() : *reinterpret_cast<const f32x4*>(sBlk + (t0i - 4) * DK + c1);
+        const f32x4 rk0 = widen4(load4(sK + r * L::LK + c0)) * er0, rk1 = widen4(load4(sK + r * L::LK + c1)) * er1;
+        const f32x4 rq0 = widen4(load4(sQ + r * L::LK + c0)) * er0, rq1 = widen4(load4(sQ + r * L::LK + c1)) * er1;
+        const Slab<Gm> RK = make_slab<Gm>(rk0, rk1);
+        const f32x4 fs0 = exp2v(d00 - *reinterpret_cast<const f32x4*>(sG + s0 * L::LG + c0));
+        const f32x4 fs1 = exp2v(d01 - *reinterpret_cast<const f32x4*>(sG + s0 * L::LG + c1));
+        const f32x4 ck0 = widen4(load4(sK + s0 * L::LK + c0)) * fs0, ck1 = widen4(load4(sK + s0 * L::LK + c1)) * fs1;
+        if (P::kMixed && diag) {
+          Slab<Gm> CKh, CKl, RQh, RQl;
+          make_slab_split<Gm>(ck0, ck1, CKh, CKl);
+          make_slab_split<Gm>(rq0, rq1, RQh, RQl);
+          accA0 = mma(CKh, RK, accA0);
+          accM0 = mma(CKh, RQh, accM0);
+          accM0 = mma(CKl, RQh, accM0);
+          accM0 = mma(CKh, RQl, accM0);
+        } else {
+          const Slab<Gm> RQ = make_slab<Gm>(rq0, rq1);
+          const Slab<Gm> CK = make_slab<Gm>(ck0, ck1);
+          accA0 = mma(CK, RK, accA0);   // A^T tile: lane holds A[r][16bb + g4 + i]
+          accM0 = mma(CK, RQ, accM0);   // M^T tile: lane holds M[r][16bb + g4 + i]
+          if (ntile > 1) {
+            const f32x4 d10 = *reinterpret_cast<const f32x4*>(sBlk + (t1i - 4) * DK + c0);
+            const f32x4 d11 = *reinterpret_cast<const f32x4*>(sBlk + (t1i - 4) * DK + c1);
+            const f32x4 ft0 = exp2v(d10 - *reinterpret_cast<const f32x4*>(sG + s1 * L::LG + c0));
+            const f32x4 ft1 = exp2v(d11 - *reinterpret_cast<const f32x4*>(sG + s1 * L::LG + c1));
+            const Slab<Gm> CK1 = make_slab<Gm>(widen4(load4(sK + s1 * L::LK + c0)) * ft0,
+                                               widen4(load4(sK + s1 * L::LK + c1)) * ft1);
+            accA1 = mma(CK1, RK, accA1);
+            accM1 = mma(CK1, RQ, accM1);
+          }
+        }
+      }
+      const float br = sBeta[r];
+      for (int ti = 0; ti < ntile; ++ti) {
+        const int bb = ti ? bb1 : bb0;
+        const f32x4 accA = ti ? accA1 : accA0, accM = ti ? accM1 : accM0;
+        f32x4 arow, mrow;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int sc = 16 * bb + g4 + i;
+          arow[i] = sc < r ? br * accA[i] : 0.f;
+          mrow[i] = sc <= r ? accM[i] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(sA + r * L::LA + 16 * bb + g4) = arow;
+        store4<Op>(rM + (bb * 4 + a) * 256 + 4 * lane, narrow4<Op>(mrow * scale));
       }
     }
-    const float br = sBeta[r];
-    f32x4 arow, mrow;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sc = 16 * bb + g4 + i;
-      arow[i] = sc < r ? br * accA[i] : 0.f;
-      mrow[i] = sc <= r ? accM[i] : 0.f;
-    }
-    *reinterpret_cast<f32x4*>(sA + r * L::LA + 16 * bb + g4) = arow;
-    store4<Op>(rM + (bb * 4 + a) * 256 + 4 * lane, narrow4<Op>(mrow * scale));
   }
   if (w >= 2) {   // the six tiles above the diagonal of the record's M are zero
     // (the mirror of lower tile (a, b): row block b, column block a)
     const int zt = w - 2, kt = kTileA[4 + zt], rt = kTileB[4 + zt];
     store4<Op>(rM + (kt * 4 + rt) * 256 + 4 * lane, narrow4<Op>(zero4()));
   }
-  // Khat tiles and Qbar tiles: NTK = DK / 4 tasks of each kind, task t of
-  // wave w in [kTaskBegin(w), kTaskBegin(w + 1)); a Khat task is one 16x16
-  // tile (st, ct), a Qbar task one tile (ct, rt)
+  // Khat tiles (st, ct), NTK of them: a quarter each to waves 6 and 7, an
+  // eighth each to waves 0-3 (waves 4 and 5 carry two Gram tiles)
   constexpr int NTK = DK / 4;
-  auto task_begin = [](int wv) -> int {
-    // waves 0-3 take 5/32 of the tasks each, 4-5 none, 6-7 6/32 each
-    constexpr int T = 2 * NTK;
-    return wv <= 4 ? wv * (5 * T / 32) : (wv <= 6 ? 4 * (5 * T / 32) : 4 * (5 * T / 32) + (T - 4 * (5 * T / 32)) / 2);
-  };
-  const int tb = task_begin(w), te = w == kNW - 1 ? 2 * NTK : task_begin(w + 1);
-  for (int t = tb; t < te; ++t) {
-    if (t < NTK) {   // Khat tile t: lane holds Khat[16st + g4 + i][16ct + l16]
+  {
+    const int kb0 = w < 4 ? w * (NTK / 8) : (w < 6 ? 0 : NTK / 2 + (w - 6) * (NTK / 4));
+    const int kb1 = w < 4 ? kb0 + NTK / 8 : (w < 6 ? 0 : kb0 + NTK / 4);
+    for (int t = kb0; t < kb1; ++t) {   // lane holds Khat[16st + g4 + i][16ct + l16]
       const int st = t / (DK / 16), ct = t % (DK / 16);
       const int col = 16 * ct + l16, row0 = 16 * st + g4;
-      const float gC = sG[(kC - 1) * L::LG + col];
+      // e^{Gamma_C - Gamma_r} = e^{(Gamma_C - Gamma_p) - local_r}, p = row block st's start
+      const float dC = sBlk[(6 + st) * DK + col];
       f32x4 val;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        val[i] = to_f32(sK[(row0 + i) * L::LK + col]) * exp2_fast(gC - sG[(row0 + i) * L::LG + col]);
+        val[i] = to_f32(sK[(row0 + i) * L::LK + col]) * exp2_fast(dC - sG[(row0 + i) * L::LG + col]);
       store4<Op>(rK + t * 256 + 4 * lane, narrow4<Op>(val));
-    } else {         // Qbar = scale e^Gamma q, tile (ct, rt): lane holds Qbar[16rt + l16][16ct + g4 + i]
-      const int qt = t - NTK, ct = qt / 4, rt = qt % 4;
-      const int row = 16 * rt + l16, col = 16 * ct + g4;
-      const f32x4 qb = widen4(load4(sQ + row * L::LK + col)) * exp2v(*reinterpret_cast<const f32x4*>(sG + row * L::LG + col));
-      store4<Op>(rQ + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(qb * scale));
     }
   }
-  if (tid >= kThreads - DK) rDec[tid - (kThreads - DK)] = exp2_fast(sG[(kC - 1) * L::LG + tid - (kThreads - DK)]);
+  if (tid >= 256 && tid < 256 + DK) rDec[tid - 256] = exp2_fast(sBlk[18 * DK + tid - 256]);
+  // Qbar = scale e^Gamma q into the record and Kbar = e^Gamma k into
+  // registers, tiles (ct, rt) of this wave: lane holds row 16rt + l16,
+  // columns 16ct + g4 .. +3 (one exponential for both)
+  V4<Op> kbar[NQW];
+#pragma unroll
+  for (int j = 0; j < NQW; ++j) {
+    int ct, rt;
+    wave_tile(w, j, NQW, ct, rt);
+    const int row = 16 * rt + l16, col = 16 * ct + g4;
+    const f32x4 e = exp2v((*reinterpret_cast<const f32x4*>(sBlk + (10 + rt) * DK + col) +
+                           *reinterpret_cast<const f32x4*>(sG + row * L::LG + col)) +
+                          *reinterpret_cast<const f32x4*>(sBlk + (14 + rt) * DK + col));
+    store4<Op>(rQ + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(widen4(load4(sQ + row * L::LK + col)) * e * scale));
+    kbar[j] = narrow4<Op>(widen4(load4(sK + row * L::LK + col)) * e);
+  }
   __syncthreads();   // sQ is dead from here on; R2 becomes Tm
 
   // ---- phase 2: X = (I + A)^-1 by 16x16 blocks, fp32
@@ -431,19 +518,14 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     sTm[r * L::LB + s] = from_f32<Op>(s <= r ? sX[r * L::LA + s] * sBeta[s] : 0.f);
   }
 
-  // ---- phase 3a: Kbar^T = (e^Gamma k)^T into R1 (through registers), then W^T
-  constexpr int NKB = kC * DK / kThreads;
-  Op kb[NKB];
-#pragma unroll
-  for (int i = 0; i < NKB; ++i) {
-    const int n = tid + kThreads * i, s = n & 63, c = n >> 6;
-    kb[i] = from_f32<Op>(to_f32(sK[s * L::LK + c]) * exp2_fast(sG[s * L::LG + c]));
-  }
+  // ---- phase 3a: Kbar^T into R1 (from the registers of phase 1), then W
   __syncthreads();   // sK and sX dead; sTm complete
 #pragma unroll
-  for (int i = 0; i < NKB; ++i) {
-    const int n = tid + kThreads * i, s = n & 63, c = n >> 6;
-    sKbt[c * L::LB + s] = kb[i];
+  for (int j = 0; j < NQW; ++j) {
+    int ct, rt;
+    wave_tile(w, j, NQW, ct, rt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sKbt[(16 * ct + g4 + i) * L::LB + 16 * rt + l16] = kbar[j][i];
   }
   __syncthreads();
 #pragma unroll
@@ -463,10 +545,10 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   const float sv = P::kMixed ? fp16_range_scale(block_max(vmax, sRed)) : 1.f;   // barriers inside
   if (!P::kMixed) __syncthreads();   // R1 (Kbar^T) readers done
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
+  for (int i = 0; i < VPT; ++i) {   // consecutive lanes hold consecutive rows (see load_inputs)
     const int n = tid + kThreads * i;
     if (n < NVV) {
-      const int r = n / (DV / VE), c = (n % (DV / VE)) * VE;
+      const int r = n % kC, c = (n / kC) * VE;
 #pragma unroll
       for (int x = 0; x < VE; ++x) sVt[(c + x) * L::LB + r] = from_f32<Op>(raw_elem<TIn>(vreg[i], x) * sv);
     }
