@@ -1,0 +1,188 @@
+"""GPU parity at the full sizes of the five workloads, through the same
+entry points and launch configuration the benchmark times (fused prefill with
+the library workspace, batched decode step).
+
+Inputs are the seeded synthetic draws of gated_delta_rule_96_amd.synth; the
+decay is produced on the GPU by kda_prepare_decay from z and A, the oracle
+applies its own fp64 gate to the same z and rounds it to bf16, the input
+precision of g in this mode (both sides then see the same g except where the
+fp32 and fp64 gates fall on different sides of a bf16 rounding boundary).
+Where the oracle cannot cover the whole workload in seconds, it is run on
+sampled heads over the full sequence (every output of those heads is
+compared); heads and sequences are independent in the method, so the other
+heads only have to be present to give the launch its real shape.
+
+Tolerances as in the other parity tests: max |err| <= 2e-2 * rms(ref) for
+bf16 inputs, outputs and final states alike.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_96_amd import kda, synth
+from kda_testutil import TOL, err_ratio, f32, say
+from oracle import gate as ogate
+from oracle import seq
+
+BF = torch.bfloat16
+TOLB = TOL[BF]
+
+
+def _bf(x) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(BF)
+
+
+def _oracle_inputs(d, heads):
+    """bf16-rounded inputs of the chosen heads as fp32 numpy, and the
+    oracle's gate of their z."""
+    sel = lambda x: f32(_bf(x[:, :, heads]))
+    q, k, v, z = (sel(d[n]) for n in ("q", "k", "v", "z"))
+    beta = f32(_bf(d["beta"][:, :, heads]))
+    g = f32(_bf(ogate.gate(z, d["A"][heads])))
+    return q, k, v, g, beta
+
+
+def _gpu_prefill(d, dev, h0=None, ws=None):
+    q, k, v, beta, z = (_bf(d[n]).to(dev) for n in ("q", "k", "v", "beta", "z"))
+    A = torch.from_numpy(d["A"].copy()).to(dev)
+    g, _ = kda.prepare_decay(z, A, want_gcum=False)
+    return kda.fwd_chunked(q, k, v, g, beta, h0, workspace=ws)
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(300)
+def test_config1_full_b4_h16_t8192():
+    """B=4, H=16, T=8192, dk=dv=128, bf16 inputs, fp32 initial state
+    N(0, 0.02): every output and final state against the oracle."""
+    B, H, T, D = 4, 16, 8192, 128
+    say(f"full config B={B} H={H} T={T}")
+    d = synth.make_inputs(B, T, H, D, D, seed=21)
+    dev = torch.device("cuda:0")
+    h0 = torch.from_numpy(d["h0"]).to(dev)
+    o, ht = _gpu_prefill(d, dev, h0)
+    torch.cuda.synchronize()
+    q, k, v, g, beta = _oracle_inputs(d, list(range(H)))
+    o_ref, h_ref = seq.kda_seq(q, k, v, g, beta, d["h0"])
+    eo, eh = err_ratio(f32(o), o_ref), err_ratio(ht.cpu().numpy(), h_ref)
+    say(f"config B4 H16 T8192: o err/rms {eo:.3e}, state err/rms {eh:.3e}")
+    assert eo <= TOLB and eh <= TOLB
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(300)
+def test_config2_b1_h32_t65536_sampled_heads():
+    """B=1, H=32, T=65536 (the benchmark workload, same entry point and
+    workspace): all outputs and the final state of three heads."""
+    B, H, T, D = 1, 32, 65536, 128
+    heads = [0, 13, 31]
+    say(f"full config B={B} H={H} T={T}, heads {heads}")
+    d = synth.make_inputs(B, T, H, D, D, seed=22)
+    dev = torch.device("cuda:0")
+    h0 = torch.from_numpy(d["h0"]).to(dev)
+    ws = kda.alloc_workspace(B, T, H, D, D, BF, dev)
+    o, ht = _gpu_prefill(d, dev, h0, ws)
+    torch.cuda.synchronize()
+    assert kda.workspace_error(ws) == 0
+    q, k, v, g, beta = _oracle_inputs(d, heads)
+    o_ref, h_ref = seq.kda_seq(q, k, v, g, beta, d["h0"][:, heads])
+    eo = err_ratio(f32(o[:, :, heads]), o_ref)
+    eh = err_ratio(ht[:, heads].cpu().numpy(), h_ref)
+    say(f"config B1 H32 T64K: o err/rms {eo:.3e}, state err/rms {eh:.3e}")
+    assert eo <= TOLB and eh <= TOLB
+
+
+def _device_draw(shape_k, shape_v, shape_b, gen, dev):
+    """Stand-in inputs for the heads the oracle does not check (same
+    distributions, drawn on the device)."""
+    unit = lambda x: x / x.norm(dim=-1, keepdim=True)
+    q = unit(torch.randn(shape_k, generator=gen, device=dev))
+    k = unit(torch.randn(shape_k, generator=gen, device=dev))
+    z = torch.randn(shape_k, generator=gen, device=dev)
+    v = torch.randn(shape_v, generator=gen, device=dev)
+    beta = torch.sigmoid(torch.randn(shape_b, generator=gen, device=dev))
+    return {"q": q, "k": k, "z": z, "v": v, "beta": beta}
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(600)
+def test_config3_million_tokens_16_segments_sampled_heads():
+    """B=1, H=32, T=1,048,576 as 16 segments of 65536 carrying the fp32
+    state between calls (ht written over h0 in place); two sampled heads
+    checked on every output of every segment and on the final state."""
+    B, H, TS, NSEG, D = 1, 32, 65536, 16, 128
+    heads = [5, 26]
+    say(f"million-token config: {NSEG} segments of {TS}, heads {heads}")
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(23)
+    A_all = synth.head_A(23, H)
+    A = torch.from_numpy(A_all.copy()).to(dev)
+    state = torch.from_numpy(synth.initial_state(23, B, H, D, D)).to(dev)
+    ref_state = synth.initial_state(23, B, H, D, D)[:, heads].astype(np.float64)
+    ws = kda.alloc_workspace(B, TS, H, D, D, BF, dev)
+    worst_o = 0.0
+    for sgi in range(NSEG):
+        other = _device_draw((B, TS, H, D), (B, TS, H, D), (B, TS, H), gen, dev)
+        ds = synth.make_inputs(B, TS, H, D, D, seed=23, part=sgi, with_h0=False, heads=heads)
+        x = {}
+        for n in ("q", "k", "z", "v", "beta"):
+            t = other[n]
+            t[:, :, heads] = torch.from_numpy(ds[n]).to(dev)
+            x[n] = t.to(BF)
+        g, _ = kda.prepare_decay(x["z"], A, want_gcum=False)
+        o, _ = kda.fwd_chunked(x["q"], x["k"], x["v"], g, x["beta"], state, ht=state, workspace=ws)
+        torch.cuda.synchronize()
+        assert kda.workspace_error(ws) == 0
+        ds["A"] = A_all[heads]
+        q, k, v, gr, beta = (f32(_bf(ds[n])) for n in ("q", "k", "v", "z", "beta"))
+        gr = f32(_bf(ogate.gate(gr, ds["A"])))
+        o_ref, ref_state = seq.kda_seq(q, k, v, gr, beta, ref_state)
+        eo = err_ratio(f32(o[:, :, heads]), o_ref)
+        worst_o = max(worst_o, eo)
+        assert eo <= TOLB, f"segment {sgi}: o err/rms {eo:.3e}"
+    eh = err_ratio(state[:, heads].cpu().numpy(), ref_state)
+    say(f"million-token config: worst o err/rms {worst_o:.3e}, final state err/rms {eh:.3e}")
+    assert eh <= TOLB
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(300)
+def test_config4_decode_b256_h32_1000_steps_sampled():
+    """B=256, H=32, 1000 consecutive decode steps against a random fp32
+    state N(0, 0.02) (token inputs cycle through 16 seeded steps): every
+    step's output and the final state of eight sampled (b, h) pairs."""
+    B, H, D, STEPS, POOL = 256, 32, 128, 1000, 16
+    pairs = [(0, 0), (3, 31), (77, 5), (128, 16), (200, 9), (255, 31), (255, 0), (31, 22)]
+    say(f"decode config B={B} H={H} steps={STEPS}")
+    dev = torch.device("cuda:0")
+    state0 = synth.initial_state(24, B, H, D, D)
+    state = torch.from_numpy(state0).to(dev)
+    pool = []
+    for s in range(POOL):
+        tk = synth.decode_tokens(B, H, D, D, seed=24, step=s)
+        z = _bf(tk["z"]).to(dev)
+        g, _ = kda.prepare_decay(z[:, None].contiguous(), torch.from_numpy(tk["A"]).to(dev), want_gcum=False)
+        pool.append((_bf(tk["q"]).to(dev), _bf(tk["k"]).to(dev), _bf(tk["v"]).to(dev), g[:, 0].contiguous(),
+                     _bf(tk["beta"]).to(dev), tk))
+    bi = np.array([p[0] for p in pairs])
+    hi = np.array([p[1] for p in pairs])
+    ref = state0[bi, hi][None].astype(np.float64)          # [1, P, dk, dv]
+    worst_o = 0.0
+    o_all = []
+    for s in range(STEPS):
+        q, k, v, g, beta, _ = pool[s % POOL]
+        o = kda.decode_step(q, k, v, g, beta, state)
+        o_all.append(o[bi, hi].clone())
+    torch.cuda.synchronize()
+    for s in range(STEPS):
+        tk = pool[s % POOL][5]
+        sel = lambda x: f32(_bf(x))[bi, hi][None]
+        gq = f32(_bf(ogate.gate(f32(_bf(tk["z"]))[bi, hi][None, None], tk["A"][hi])[0]))
+        o_ref, ref = seq.kda_decode_ref(sel(tk["q"]), sel(tk["k"]), sel(tk["v"]), gq, sel(tk["beta"]), ref)
+        eo = err_ratio(o_all[s].cpu().numpy()[None], o_ref)
+        worst_o = max(worst_o, eo)
+    eh = err_ratio(state[bi, hi].cpu().numpy()[None], ref)
+    say(f"decode config: worst step o err/rms {worst_o:.3e}, final state err/rms {eh:.3e}")
+    assert worst_o <= TOLB and eh <= TOLB
