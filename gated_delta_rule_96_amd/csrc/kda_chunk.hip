@@ -157,7 +157,11 @@ struct InRegs {
   float beta;
 };
 
-template <typename TIn, int DK, int DV>
+// Parts of the inputs (bit mask of load_inputs): the next chunk's loads
+// can be issued in portions spread over the current chunk's phases.
+constexpr int kLoadK = 1, kLoadQ = 2, kLoadG = 4, kLoadV = 8, kLoadBeta = 16, kLoadAll = 31;
+
+template <typename TIn, int DK, int DV, int kParts = kLoadAll>
 __device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* __restrict__ q,
                                             const TIn* __restrict__ k, const TIn* __restrict__ v,
                                             const TIn* __restrict__ g, const TIn* __restrict__ beta, int b, int h,
@@ -176,9 +180,9 @@ __device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* 
     const int n = tid + kThreads * i;
     const int r = n / (DK / VE), c = (n % (DK / VE)) * VE;
     const bool ok = r < Lrows;
-    in.k[i] = ok ? *reinterpret_cast<const raw16*>(k + base_k + r * tokk + c) : zero16;
-    in.q[i] = ok ? *reinterpret_cast<const raw16*>(q + base_k + r * tokk + c) : zero16;
-    in.g[i] = (ok && g) ? *reinterpret_cast<const raw16*>(g + base_k + r * tokk + c) : zero16;
+    if (kParts & kLoadK) in.k[i] = ok ? *reinterpret_cast<const raw16*>(k + base_k + r * tokk + c) : zero16;
+    if (kParts & kLoadQ) in.q[i] = ok ? *reinterpret_cast<const raw16*>(q + base_k + r * tokk + c) : zero16;
+    if (kParts & kLoadG) in.g[i] = (ok && g) ? *reinterpret_cast<const raw16*>(g + base_k + r * tokk + c) : zero16;
   }
   // v: consecutive lanes take consecutive rows of one column block, so that
   // the transposed LDS staging of V is free of bank conflicts
@@ -186,9 +190,10 @@ __device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* 
   for (int i = 0; i < IR::NV; ++i) {
     const int n = tid + kThreads * i;
     const int r = n % kC, c = (n / kC) * VE;
-    in.v[i] = r < Lrows ? *reinterpret_cast<const raw16*>(v + base_v + r * tokv + c) : zero16;
+    if (kParts & kLoadV) in.v[i] = r < Lrows ? *reinterpret_cast<const raw16*>(v + base_v + r * tokv + c) : zero16;
   }
-  in.beta = (tid < kC && tid < Lrows) ? to_f32(beta[((size_t)b * T_len + t0 + tid) * H + h]) : 0.f;
+  if (kParts & kLoadBeta)
+    in.beta = (tid < kC && tid < Lrows) ? to_f32(beta[((size_t)b * T_len + t0 + tid) * H + h]) : 0.f;
 }
 
 // The BLK rows of channel c from the chunk's block starts bs[a] = Gamma_p(a)
@@ -262,12 +267,16 @@ __constant__ signed char kWaveTile[8][2] = {{0, -1}, {1, -1}, {2, -1}, {3, -1}, 
 // Builds the record of chunk `ch` of head (b, h) at `rec`.  Called by a
 // whole work-group of kThreads threads; `smem` holds IntraLds::BYTES.
 // `in` holds the chunk's inputs (load_inputs); right after they are staged
-// in LDS, `after_stage()` runs with every thread (it may reuse `in`, e.g. to
-// prefetch the next chunk); if it returns false nothing is written.
-template <typename TIn, int DK, int DV, typename AfterStage>
+// in LDS, `after_stage()` runs with every thread; if it returns false
+// nothing is written.  From then on `in` is free (v is read from it once
+// more, before the last call): `prefetch(parts)` is called by every thread
+// at four points of the later phases, with kLoadK | kLoadBeta, kLoadQ,
+// kLoadG, kLoadV in turn (as std::integral_constant), e.g. to load the next
+// chunk's inputs into `in` in portions while this one is computed.
+template <typename TIn, int DK, int DV, typename AfterStage, typename Prefetch>
 __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& in, const float* __restrict__ gcum,
                                               float scale, int b, int h, int T_len, int H, int ch,
-                                              char* __restrict__ rec, AfterStage after_stage) {
+                                              char* __restrict__ rec, AfterStage after_stage, Prefetch prefetch) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using Gm = typename P::Gram;
@@ -320,9 +329,6 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     }
   }
   if (tid < kC) sBeta[tid] = in.beta;
-  raw16 vreg[IR::NV];
-#pragma unroll
-  for (int i = 0; i < IR::NV; ++i) vreg[i] = in.v[i];
   constexpr int NVV = kC * DV / VE;
   constexpr int VPT = IR::NV;
   // Gamma, kept as sums local to each 16-row block (G) plus the block
@@ -372,6 +378,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   }
   __syncthreads();
   if (!after_stage()) return false;
+  prefetch(std::integral_constant<int, kLoadK | kLoadBeta>{});
 
   // ---- phase 1: Gram tiles (A -> LDS, scale M -> record), Khat, dec,
   // Qbar (record) and Kbar (registers, staged transposed after the solve)
@@ -385,7 +392,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       const bool diag = a == bb0;   // only single-tile waves hold a diagonal tile
       const int r = 16 * a + l16, s0 = 16 * bb0 + l16, s1 = 16 * bb1 + l16;
       f32x4 accA0 = zero4(), accM0 = zero4(), accA1 = zero4(), accM1 = zero4();
-#pragma unroll 2
+#pragma unroll
       for (int sl = 0; sl < DK / 32; ++sl) {
         const int c0 = 32 * sl + g4, c1 = c0 + 16;
         // row factor e^{Gamma_r - Gamma_p}: the local sum itself
@@ -441,6 +448,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       }
     }
   }
+  prefetch(std::integral_constant<int, kLoadQ>{});
   if (w >= 2) {   // the six tiles above the diagonal of the record's M are zero
     // (the mirror of lower tile (a, b): row block b, column block a)
     const int zt = w - 2, kt = kTileA[4 + zt], rt = kTileB[4 + zt];
@@ -449,21 +457,27 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   // Khat tiles (st, ct), NTK of them: a quarter each to waves 6 and 7, an
   // eighth each to waves 0-3 (waves 4 and 5 carry two Gram tiles)
   constexpr int NTK = DK / 4;
-  {
-    const int kb0 = w < 4 ? w * (NTK / 8) : (w < 6 ? 0 : NTK / 2 + (w - 6) * (NTK / 4));
-    const int kb1 = w < 4 ? kb0 + NTK / 8 : (w < 6 ? 0 : kb0 + NTK / 4);
-    for (int t = kb0; t < kb1; ++t) {   // lane holds Khat[16st + g4 + i][16ct + l16]
-      const int st = t / (DK / 16), ct = t % (DK / 16);
+  // lane holds Khat[16st + g4 + i][16ct + l16] of tile t = st * (DK/16) + ct;
+  // e^{Gamma_C - Gamma_r} = e^{(Gamma_C - Gamma_p) - local_r}, p = row block st's start.
+  // Fixed trip counts (unrolled), so that every task's LDS reads are issued
+  // before the first exponential.
+  auto khat_tasks = [&](int kb0, auto ntask) {
+    constexpr int N = decltype(ntask)::value;
+    f32x4 val[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int t = kb0 + j, st = t / (DK / 16), ct = t % (DK / 16);
       const int col = 16 * ct + l16, row0 = 16 * st + g4;
-      // e^{Gamma_C - Gamma_r} = e^{(Gamma_C - Gamma_p) - local_r}, p = row block st's start
       const float dC = sBlk[(6 + st) * DK + col];
-      f32x4 val;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        val[i] = to_f32(sK[(row0 + i) * L::LK + col]) * exp2_fast(dC - sG[(row0 + i) * L::LG + col]);
-      store4<Op>(rK + t * 256 + 4 * lane, narrow4<Op>(val));
+        val[j][i] = to_f32(sK[(row0 + i) * L::LK + col]) * exp2_fast(dC - sG[(row0 + i) * L::LG + col]);
     }
-  }
+#pragma unroll
+    for (int j = 0; j < N; ++j) store4<Op>(rK + (kb0 + j) * 256 + 4 * lane, narrow4<Op>(val[j]));
+  };
+  if (w < 4) khat_tasks(w * (NTK / 8), std::integral_constant<int, NTK / 8>{});
+  else if (w >= 6) khat_tasks(NTK / 2 + (w - 6) * (NTK / 4), std::integral_constant<int, NTK / 4>{});
   if (tid >= 256 && tid < 256 + DK) rDec[tid - 256] = exp2_fast(sBlk[18 * DK + tid - 256]);
   // Qbar = scale e^Gamma q into the record and Kbar = e^Gamma k into
   // registers, tiles (ct, rt) of this wave: lane holds row 16rt + l16,
@@ -498,6 +512,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
 #pragma unroll
     for (int i = 0; i < 16; ++i) Xb[i * L::LA + j] = x[i];
   }
+  prefetch(std::integral_constant<int, kLoadG>{});
   __syncthreads();
   // off-diagonal blocks by distance d = a - b: X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb
   for (int d = 1; d < 4; ++d) {
@@ -537,6 +552,10 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   }
 
   // ---- phase 3b: V^T (range-scaled) into R1, then Ut = Tm V
+  raw16 vreg[IR::NV];
+#pragma unroll
+  for (int i = 0; i < IR::NV; ++i) vreg[i] = in.v[i];
+  prefetch(std::integral_constant<int, kLoadV>{});
   float vmax = 0.f;
 #pragma unroll
   for (int i = 0; i < VPT; ++i)
@@ -591,7 +610,8 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __rest
   InRegs<TIn, DK, DV> in;
   load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, ch);
   produce_chunk<TIn, DK, DV>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, ch,
-                             ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [] { return true; });
+                             ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [] { return true; },
+                             [](auto) {});
 }
 
 // ---------------------------------------------------------------------------
@@ -622,19 +642,36 @@ constexpr int kSpinLimit = 1 << 20;   // about a second of polling before giving
 // The XCD (accelerator complex die, each with its own L2) this wave runs on.
 __device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xf; }
 
+// A flag word read from this XCD's L2 (the load misses the CU's L1: sc0).
+// Sees every store that has reached this L2, i.e. stores made by work-groups
+// on the same XCD; a device-scope load (sc1) may go out to memory instead,
+// which costs a fabric round trip.
+__device__ __forceinline__ int load_flag_l2(const int* p) {
+  int v;
+  asm volatile("global_load_dword %0, %1, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
 // Polls *p until it is >= target and returns the value seen.  Executed by
 // every lane of one whole wave: all lanes load the same word and the loop
 // condition goes through readfirstlane, so the loop is wave-uniform (no
-// lane-divergent loop inside code that also holds barriers).  Returns -1
-// after kSpinLimit polls, or as soon as another work-group reported an
-// error; sets *err on a timeout.
+// lane-divergent loop inside code that also holds barriers).  Polls read
+// this XCD's L2; every 8th poll is a device-scope load (the writer may run
+// on another XCD), and checks the error word.  kSleep: pause between polls
+// (units of 64 cycles).  Returns -1 after kSpinLimit polls, or as soon as
+// another work-group reported an error; sets *err on a timeout.
+template <int kSleep = 2>
 __device__ __forceinline__ int spin_until_geq(const int* p, int target, int* err) {
   for (int it = 0; it < kSpinLimit; ++it) {
-    const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const bool dev = (it & 7) == 7;
+    const int v = __builtin_amdgcn_readfirstlane(dev ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                     : load_flag_l2(p));
     if (v >= target) return v;
-    const int e = __builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (e != 0) return -1;
-    __builtin_amdgcn_s_sleep(2);
+    if (dev) {
+      const int e = __builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (e != 0) return -1;
+    }
+    __builtin_amdgcn_s_sleep(kSleep);
   }
   if ((threadIdx.x & 63) == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return -1;
@@ -951,6 +988,9 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
 // items of that XCD's heads, in chunk-major order, round robin, and write
 // each chunk's record into the head's ring of R slots.  Records
 // therefore live only in L2 / Infinity Cache between producer and consumer.
+// A producer loads its next item's inputs in four portions issued during
+// the current item's phases, so that the loads overlap the compute and no
+// phase waits for one large burst of requests to be accepted.
 // Ordering: producer stores, then a release in every wave, then
 // ready[slot] = (c + 1) << 4 | XCD; the consumer polls ready, then an
 // acquire, then reads.  Work-group i is dispatched to XCD i % 8, so a head's
@@ -959,9 +999,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
 // Both sides check where they actually run (the XCC_ID hardware register;
 // the consumer publishes its XCD, the producer tags the flag with its own)
 // and use agent-scope fences whenever the two differ.  A slot is reused only after every
-// consumer of the head stored done >= c + 1 for the chunk that held it.  A
-// producer starts loading its next item's inputs as soon as the current
-// item's inputs are staged, so loads overlap the compute.
+// consumer of the head stored done >= c + 1 for the chunk that held it.
 // Every wait is bounded (kSpinLimit); on a timeout the work-group sets the
 // error word and leaves, so the grid always drains.
 //
@@ -1023,12 +1061,19 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   // Release: if the head's consumers run on this XCD they read through the
   // same L2, so it is enough that every wave's record stores have reached
   // the L2; otherwise an agent-scope release (L2 write-back).
+  // A consumer's XCD word is written once, at its start, so a head whose
+  // consumers were seen on this XCD is remembered (bit of same_mask).
+  unsigned same_mask = 0;
   auto publish = [&](int pi) {
-    const int pc = pi / nloc, pj = xcd + 8 * (pi % nloc);
-    bool same = true;
-    for (int vb = 0; vb < NS; ++vb)
-      same = same && __builtin_amdgcn_readfirstlane(__hip_atomic_load(cxcc + pj * NS + vb, __ATOMIC_RELAXED,
-                                                                      __HIP_MEMORY_SCOPE_AGENT)) == my_xcc + 1;
+    const int pc = pi / nloc, pl = pi % nloc, pj = xcd + 8 * pl;
+    bool same = pl < 32 && ((same_mask >> pl) & 1u);
+    if (!same) {
+      same = true;
+      for (int vb = 0; vb < NS; ++vb)
+        same = same && __builtin_amdgcn_readfirstlane(__hip_atomic_load(cxcc + pj * NS + vb, __ATOMIC_RELAXED,
+                                                                        __HIP_MEMORY_SCOPE_AGENT)) == my_xcc + 1;
+      if (same && pl < 32) same_mask |= 1u << pl;
+    }
     if (same) wait_vmem();
     else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
@@ -1041,15 +1086,11 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
     const int nxt = it + P;
     // Runs once this chunk's inputs are in LDS: publish the previous item
-    // (its record stores drained while this item was staged), start loading
-    // the next item's inputs, then wait until the ring slot of chunk c is
-    // free (it held chunk c - R, which the head's consumers must have read).
+    // (its record stores drained while this item was staged), then wait
+    // until the ring slot of chunk c is free (it held chunk c - R, which the
+    // head's consumers must have read).
     auto after_stage = [&]() -> bool {
       if (pending >= 0) publish(pending);
-      if (nxt < total) {
-        const int jn = xcd + 8 * (nxt % nloc), bn = head0 + jn;
-        load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bn / H, bn % H, T_len, H, nxt / nloc);
-      }
       if (c < R) return true;
       if (w == 0) {
         bool ok = true;
@@ -1061,8 +1102,16 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
       __syncthreads();
       return ok != 0;
     };
+    // the next item's inputs, loaded in portions during this item's phases
+    auto prefetch = [&](auto parts) {
+      if (nxt < total) {
+        const int jn = xcd + 8 * (nxt % nloc), bn = head0 + jn;
+        load_inputs<TIn, DK, DV, decltype(parts)::value>(in, q, k, v, g, beta, bn / H, bn % H, T_len, H,
+                                                         nxt / nloc);
+      }
+    };
     if (!produce_chunk<TIn, DK, DV>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
-                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage))
+                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage, prefetch))
       return;
     pending = it;
     if (nxt >= total) {
