@@ -146,7 +146,9 @@ __device__ __forceinline__ void wave_tile(int w, int j, int per_wave, int& x, in
 
 // One chunk's raw inputs in registers (rows past the end of the sequence
 // are zero): 16-byte vectors of k, q, g and v rows (k, q, g row-major over
-// the threads, v column-block-major), and beta.
+// the threads, v column-block-major), and beta.  Inputs are read once, so
+// their loads are non-temporal: they do not displace the chunk records that
+// producers and consumers exchange through the L2.
 template <typename TIn, int DK, int DV>
 struct InRegs {
   static constexpr int VE = 16 / sizeof(TIn);
@@ -180,9 +182,11 @@ __device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* 
     const int n = tid + kThreads * i;
     const int r = n / (DK / VE), c = (n % (DK / VE)) * VE;
     const bool ok = r < Lrows;
-    if (kParts & kLoadK) in.k[i] = ok ? *reinterpret_cast<const raw16*>(k + base_k + r * tokk + c) : zero16;
-    if (kParts & kLoadQ) in.q[i] = ok ? *reinterpret_cast<const raw16*>(q + base_k + r * tokk + c) : zero16;
-    if (kParts & kLoadG) in.g[i] = (ok && g) ? *reinterpret_cast<const raw16*>(g + base_k + r * tokk + c) : zero16;
+    const size_t off = base_k + r * tokk + c;
+    if (kParts & kLoadK) in.k[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const raw16*>(k + off)) : zero16;
+    if (kParts & kLoadQ) in.q[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const raw16*>(q + off)) : zero16;
+    if (kParts & kLoadG)
+      in.g[i] = (ok && g) ? __builtin_nontemporal_load(reinterpret_cast<const raw16*>(g + off)) : zero16;
   }
   // v: consecutive lanes take consecutive rows of one column block, so that
   // the transposed LDS staging of V is free of bank conflicts
@@ -190,69 +194,85 @@ __device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* 
   for (int i = 0; i < IR::NV; ++i) {
     const int n = tid + kThreads * i;
     const int r = n % kC, c = (n / kC) * VE;
-    if (kParts & kLoadV) in.v[i] = r < Lrows ? *reinterpret_cast<const raw16*>(v + base_v + r * tokv + c) : zero16;
+    if (kParts & kLoadV)
+      in.v[i] = r < Lrows ? __builtin_nontemporal_load(reinterpret_cast<const raw16*>(v + base_v + r * tokv + c)) : zero16;
   }
   if (kParts & kLoadBeta)
     in.beta = (tid < kC && tid < Lrows) ? to_f32(beta[((size_t)b * T_len + t0 + tid) * H + h]) : 0.f;
 }
 
-// The BLK rows of channel c from the chunk's block starts bs[a] = Gamma_p(a)
-// (a = 0..3) and bs[4] = Gamma_C, in fp64 (natural log units): every
-// exponent that involves a block start is formed in fp64 and rounded once,
-// so its fp32 error is set by its own size, not by the size of Gamma.
-template <int DK>
-__device__ __forceinline__ void block_exponents(float* sBlk, int c, const double* bs) {
-  constexpr double l2e = 1.4426950408889634;
-  const int pa[6] = {1, 2, 3, 2, 3, 3}, pb[6] = {0, 0, 0, 1, 1, 2};
-#pragma unroll
-  for (int i = 0; i < 6; ++i) sBlk[i * DK + c] = (float)((bs[pa[i]] - bs[pb[i]]) * l2e);
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    sBlk[(6 + a) * DK + c] = (float)((bs[4] - bs[a]) * l2e);
-    const double x = bs[a] * l2e;
-    const float hi = (float)x;
-    sBlk[(10 + a) * DK + c] = hi;
-    sBlk[(14 + a) * DK + c] = (float)(x - (double)hi);
-  }
-  sBlk[18 * DK + c] = (float)(bs[4] * l2e);
+// 2^x for x given in fp64, rounded to fp32 with about one ulp of error
+// whatever the size of x: x = n + f with n = floor(x) exact, 2^f by
+// v_exp_f32 on f in [0, 1), then an exact scaling by 2^n (results below
+// the fp32 range flush towards zero).
+__device__ __forceinline__ float exp2_split(double x) {
+  const double n = floor(x);
+  const int ni = n < -400.0 ? -400 : (n > 400.0 ? 400 : (int)n);
+  return ldexpf(exp2_fast((float)(x - n)), ni);
 }
 
+// Per-channel factors built from the chunk's block starts, fp32 rows of
+// [kNBlk][DK]; Gamma_p(a) = Gamma at row 16a - 1 (0 for a = 0), Gamma_C at
+// the chunk's last row:
+constexpr int kBlkF = 0;     // rows 0-3   e^{Gamma_p(a)}
+constexpr int kBlkE = 4;     // rows 4-7   e^{Gamma_C - Gamma_p(a)} * 2^64
+constexpr int kBlkD = 8;     // rows 8-13  e^{Gamma_p(a) - Gamma_p(b)}, off-diagonal
+                             //            tiles (a, b) in kTileA/kTileB order 4..9
+constexpr int kBlkDec = 14;  // row 14     e^{Gamma_C}
+constexpr int kNBlk = 15;
+// The 2^64 in the Khat factor keeps e^{Gamma_C - Gamma_p(a)} out of the
+// fp32 subnormal range wherever the product with e^{-G} is not negligible.
+constexpr float kTwoM64 = 5.421010862427522e-20f;   // 2^-64
+
 // ---------------------------------------------------------------------------
-// Intra-chunk kernel: one work-group (8 waves) per (b*h, chunk).
-// LDS regions are reused across phases (lifetimes in brackets):
-//   G  : fp32 (Gamma - Gamma_p)*log2(e) [C][DK+4], p = the row before the
-//        row's 16-row block (sums local to the block)              [all]
-//   BLK: fp32 [19][DK], exponents built from the block starts Gamma_p,
-//        p = 16a - 1, summed in fp64 (times log2(e)):               [phase 1]
-//        rows 0-5   Gamma_p(a) - Gamma_p(b) for the off-diagonal tiles
-//                   (a, b) in kTileA/kTileB order 4..9
-//        rows 6-9   Gamma_C - Gamma_p(a), a = 0..3 (C = the chunk's last row)
-//        rows 10-13 Gamma_p(a) rounded to fp32, rows 14-17 the remainder
-//        row 18     Gamma_C
-//   R1 : k [C][DK] (in)  | Kbar^T [DK][C] (Op) | V^T [DV][C] (Op)
-//   X  : A, X fp32 [C][C+4] each
-//   R2 : q [C][DK] (in)  | Tm [C][C] (Op)
+// Intra-chunk work: one work-group (8 waves) per (b*h, chunk).
+// G = Gamma - Gamma_p(a) for a row in 16-row block a (a sum of at most 16
+// decays, kept in fp32); everything else is a product of
+//   KP = k e^{G},  QP = q e^{G},  KM = k e^{-G}      (fp32, two exponentials
+// per element) and per-channel factors of the block starts (BLK):
+//   A, M tile (a, b):  row operand KP or QP (block a), column operand
+//                      KM * e^{Gamma_p(a) - Gamma_p(b)} (block b)
+//   Qbar = scale e^{Gamma_p(a)} QP,  Kbar = e^{Gamma_p(a)} KP,
+//   Khat = e^{Gamma_C - Gamma_p(a)} KM
+// LDS regions, reused across phases (lifetimes in brackets):
+//   P0 : g, then G (fp32 [C][LG])                        [phase 0]
+//        -> KP (fp32 [C][LG])                              [0 - 2b]
+//   P1 : k, q (input type, [C][LK] each)                   [phase 0]
+//        -> QP at 0, KM at PB (fp32 [C][LG] each)          [0 - 2a]
+//        -> Kbar^T (Op [DK][LB]) at 0, V^T (Op [DV][LB]) at KT   [2b - 3]
+//   X  : block totals (phase 0), then A and X fp32 [C][LA]  [1 - 2b]
+//        -> Tm (Op [C][LB]) where A was                     [2b - 3]
+//   BLK: fp32 [kNBlk][DK] per-channel factors                [0 - 2b]
+// Phases: 0 stage inputs, block scans, exponentials, factors; 1 Gram tiles
+// (A -> LDS, scale M -> record); 2a wave 0 inverts the diagonal blocks of
+// I + A while waves 1-7 write Qbar, Khat, e^{Gamma_C} to the record;
+// 2b Kbar^T and V^T staged, off-diagonal blocks of the inverse, Tm;
+// 3 W = Tm Kbar, Ut = Tm V to the record.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct IntraLds {
   using Op = typename Policy<TIn>::Op;
   static constexpr int PI = 16 / sizeof(TIn), PO = 16 / sizeof(Op);
-  static constexpr int LG = DK + 4;     // Gamma rows (fp32)
+  static constexpr int LG = DK + 4;     // fp32 rows (G, KP, QP, KM)
   static constexpr int LK = DK + PI;    // k / q rows (input type)
-  static constexpr int LB = kC + PO;    // channel-major Op rows (Kbar^T, V^T, W^T, Ut^T) and M / Tm rows
+  static constexpr int LB = kC + PO;    // channel-major Op rows (Kbar^T, V^T) and Tm rows
   static constexpr int LA = kC + 4;     // A / X rows (fp32)
   static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
-  static constexpr size_t G = 0;
-  static constexpr size_t R1 = G + (size_t)kC * LG * 4;
-  static constexpr size_t R1_SIZE = mx((size_t)kC * LK * sizeof(TIn), mx((size_t)DK, (size_t)DV) * LB * sizeof(Op));
-  static constexpr size_t X = R1 + R1_SIZE;
+  static constexpr size_t r16(size_t a) { return (a + 15) / 16 * 16; }
+  static constexpr size_t PB = (size_t)kC * LG * 4;                       // one fp32 [C][LG] array
+  static constexpr size_t KIN = r16((size_t)kC * LK * sizeof(TIn));       // one staged input array
+  static constexpr size_t KT = r16((size_t)DK * LB * sizeof(Op));         // Kbar^T
+  static constexpr size_t P0 = 0;
+  static constexpr size_t P1 = P0 + PB;
+  static constexpr size_t P1_SIZE = mx(mx(2 * KIN, 2 * PB), KT + (size_t)DV * LB * sizeof(Op));
+  static constexpr size_t X = P1 + P1_SIZE;
   static constexpr size_t X_SIZE = 2 * (size_t)kC * LA * 4;
-  static constexpr size_t R2 = X + X_SIZE;
-  static constexpr size_t R2_SIZE = mx((size_t)kC * LK * sizeof(TIn), (size_t)kC * LB * sizeof(Op));
-  static constexpr size_t BLK = R2 + R2_SIZE;   // fp32 [19][DK], see above
-  static constexpr size_t BETA = BLK + 19 * (size_t)DK * 4;
+  static constexpr size_t BLK = X + X_SIZE;
+  static constexpr size_t BETA = BLK + (size_t)kNBlk * DK * 4;
   static constexpr size_t RED = BETA + kC * 4;
   static constexpr size_t BYTES = RED + 16 * 4;
+  static_assert((size_t)kC * LB * sizeof(Op) <= (size_t)kC * LA * 4, "Tm fits where A was");
+  static_assert(4 * (size_t)DK * 4 <= (size_t)kC * LA * 4, "block totals fit in A");
 };
 
 // The 10 tiles (a, b) of the lower 4x4 block triangle: diagonal first.
@@ -260,8 +280,7 @@ __constant__ signed char kTileA[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
 __constant__ signed char kTileB[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
 // Gram tiles of wave w (-1: none): a diagonal tile (the costlier kind, with
 // split operands) for waves 0-3; two off-diagonal tiles of one row block for
-// waves 4 and 5 (they share the row operand); one for waves 6 and 7.  The
-// Khat tile work goes to the waves with lighter Gram shares.
+// waves 4 and 5 (they share the row operand); one for waves 6 and 7.
 __constant__ signed char kWaveTile[8][2] = {{0, -1}, {1, -1}, {2, -1}, {3, -1}, {5, 7}, {6, 8}, {4, -1}, {9, -1}};
 
 // Builds the record of chunk `ch` of head (b, h) at `rec`.  Called by a
@@ -282,17 +301,22 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   using Gm = typename P::Gram;
   using L = IntraLds<TIn, DK, DV>;
   using R = Rec<TIn, DK, DV>;
+  using IR = InRegs<TIn, DK, DV>;
   constexpr int VE = 16 / sizeof(TIn);   // input elements per 16-byte vector
-  constexpr int NQT = (DK / 16) * 4;     // Q'^T / W^T tiles
+  constexpr int NQT = (DK / 16) * 4;     // 16x16 tiles of a [C][DK] matrix
   constexpr int NQW = NQT / kNW;         // ... per wave
-  float* sG = reinterpret_cast<float*>(smem + L::G);
-  TIn* sK = reinterpret_cast<TIn*>(smem + L::R1);
-  Op* sKbt = reinterpret_cast<Op*>(smem + L::R1);
-  Op* sVt = reinterpret_cast<Op*>(smem + L::R1);
+  float* sG = reinterpret_cast<float*>(smem + L::P0);     // g, G (phase 0)
+  float* sKP = reinterpret_cast<float*>(smem + L::P0);
+  TIn* sK = reinterpret_cast<TIn*>(smem + L::P1);         // phase 0
+  TIn* sQ = reinterpret_cast<TIn*>(smem + L::P1 + L::KIN);
+  float* sQP = reinterpret_cast<float*>(smem + L::P1);
+  float* sKM = reinterpret_cast<float*>(smem + L::P1 + L::PB);
+  Op* sKbt = reinterpret_cast<Op*>(smem + L::P1);          // phases 2b-3
+  Op* sVt = reinterpret_cast<Op*>(smem + L::P1 + L::KT);
   float* sA = reinterpret_cast<float*>(smem + L::X);
   float* sX = sA + kC * L::LA;
-  TIn* sQ = reinterpret_cast<TIn*>(smem + L::R2);
-  Op* sTm = reinterpret_cast<Op*>(smem + L::R2);
+  float* sTot = sA;                                       // [4][DK], phase 0
+  Op* sTm = reinterpret_cast<Op*>(smem + L::X);           // phases 2b-3
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sBlk = reinterpret_cast<float*>(smem + L::BLK);
   float* sRed = reinterpret_cast<float*>(smem + L::RED);
@@ -312,8 +336,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   Op* rU = reinterpret_cast<Op*>(rec + R::U_OFF_BYTES);
   float* rUinv = reinterpret_cast<float*>(rec + R::UINV_OFF_BYTES);
 
-  // ---- phase 0: stage k, q, beta, Gamma from the input registers
-  using IR = InRegs<TIn, DK, DV>;
+  // ---- phase 0: stage k, q, beta (and g) from the input registers
 #pragma unroll
   for (int i = 0; i < IR::NK; ++i) {
     const int n = tid + kThreads * i;
@@ -329,59 +352,80 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     }
   }
   if (tid < kC) sBeta[tid] = in.beta;
-  constexpr int NVV = kC * DV / VE;
-  constexpr int VPT = IR::NV;
-  // Gamma, kept as sums local to each 16-row block (G) plus the block
-  // starts (BLK): the exponents of the intra-block factors are then sums of
-  // at most 16 decays rather than differences of two long cumulative sums.
-  if (gcum) {
-    for (int n = tid; n < kC * DK / 4; n += kThreads) {
-      const int r = n / (DK / 4), c = (n % (DK / 4)) * 4;
-      const int rr = min(r, Lrows - 1), pr = min(16 * (r / 16) - 1, Lrows - 1);
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(gcum + base_k + rr * tokk + c);
-      const f32x4 gpv = pr >= 0 ? *reinterpret_cast<const f32x4*>(gcum + base_k + pr * tokk + c) : zero4();
-      *reinterpret_cast<f32x4*>(sG + r * L::LG + c) = (gv - gpv) * kLog2e;
-    }
-    if (tid < DK) {
-      double bs[5];
+  __syncthreads();
+
+  // Block scans: thread (block a, channel c) forms G for its 16 rows (local
+  // sums in row order, or differences of the given cumulative sums), the two
+  // exponentials and the products with its k and q.
+  const bool scan = tid < 4 * DK;   // wave-uniform (4 DK is a multiple of 64)
+  float kp[16], qp[16], km[16];
+  if (scan) {
+    const int c = tid % DK, a = tid / DK;
+    float x[16];
+    if (gcum) {
+      const int pr = min(16 * a - 1, Lrows - 1);
+      const float g0 = pr >= 0 ? gcum[base_k + (size_t)pr * tokk + c] : 0.f;
 #pragma unroll
-      for (int a = 0; a < 5; ++a) {
-        const int pr = min(a < 4 ? 16 * a - 1 : kC - 1, Lrows - 1);
-        bs[a] = pr >= 0 ? (double)gcum[base_k + pr * tokk + tid] : 0.0;
+      for (int i = 0; i < 16; ++i) x[i] = gcum[base_k + (size_t)min(16 * a + i, Lrows - 1) * tokk + c] - g0;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = sG[(16 * a + i) * L::LG + c];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
+      sTot[a * DK + c] = x[15];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float kv = to_f32(sK[(16 * a + i) * L::LK + c]), qv = to_f32(sQ[(16 * a + i) * L::LK + c]);
+      const float ep = exp2_fast(x[i] * kLog2e), em = exp2_fast(-x[i] * kLog2e);
+      kp[i] = kv * ep;
+      qp[i] = qv * ep;
+      km[i] = kv * em;
+    }
+  }
+  __syncthreads();   // staged k, q, g read; block totals written
+  if (scan) {
+    const int c = tid % DK, a = tid / DK;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sKP[(16 * a + i) * L::LG + c] = kp[i];
+      sQP[(16 * a + i) * L::LG + c] = qp[i];
+      sKM[(16 * a + i) * L::LG + c] = km[i];
+    }
+    // factors from the block starts, summed in fp64 (natural log units):
+    // thread group a builds one kind of row
+    double bs[5];
+    if (gcum) {
+#pragma unroll
+      for (int j = 0; j < 5; ++j) {
+        const int pr = min(j < 4 ? 16 * j - 1 : kC - 1, Lrows - 1);
+        bs[j] = pr >= 0 ? (double)gcum[base_k + (size_t)pr * tokk + c] : 0.0;
       }
-      block_exponents<DK>(sBlk, tid, bs);
-    }
-  } else {
-    // thread (block a, channel c) sums its block's 16 rows in row order; the
-    // block starts are the block totals above, added in block order
-    float* sTot = sA;   // [4][DK], free until the Gram tiles
-    __syncthreads();
-    if (tid < 4 * DK) {
-      const int c = tid % DK, a = tid / DK;
-      float gr[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) gr[i] = sG[(16 * a + i) * L::LG + c];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) gr[i] += gr[i - 1];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sG[(16 * a + i) * L::LG + c] = gr[i] * kLog2e;
-      sTot[a * DK + c] = gr[15];
-    }
-    __syncthreads();
-    if (tid < DK) {
-      double bs[5];
+    } else {
       bs[0] = 0.0;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) bs[a + 1] = bs[a] + (double)sTot[a * DK + tid];
-      block_exponents<DK>(sBlk, tid, bs);
+      for (int j = 0; j < 4; ++j) bs[j + 1] = bs[j] + (double)sTot[j * DK + c];
+    }
+    constexpr double l2e = 1.4426950408889634;
+    if (a == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sBlk[(kBlkF + j) * DK + c] = exp2_split(bs[j] * l2e);
+    } else if (a == 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sBlk[(kBlkE + j) * DK + c] = exp2_split((bs[4] - bs[j]) * l2e + 64.0);
+    } else if (a == 2) {
+      const int ta[6] = {1, 2, 3, 2, 3, 3}, tb[6] = {0, 0, 0, 1, 1, 2};
+#pragma unroll
+      for (int j = 0; j < 6; ++j) sBlk[(kBlkD + j) * DK + c] = exp2_split((bs[ta[j]] - bs[tb[j]]) * l2e);
+    } else {
+      sBlk[kBlkDec * DK + c] = exp2_split(bs[4] * l2e);
     }
   }
   __syncthreads();
   if (!after_stage()) return false;
   prefetch(std::integral_constant<int, kLoadK | kLoadBeta>{});
 
-  // ---- phase 1: Gram tiles (A -> LDS, scale M -> record), Khat, dec,
-  // Qbar (record) and Kbar (registers, staged transposed after the solve)
+  // ---- phase 1: Gram tiles (A -> LDS, scale M -> record)
   {
     const int t0i = kWaveTile[w][0], t1i = kWaveTile[w][1];
     const int ntile = t0i < 0 ? 0 : (t1i < 0 ? 1 : 2);   // wave-uniform
@@ -391,22 +435,16 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       const int bb0 = kTileB[t0i], bb1 = ntile > 1 ? kTileB[t1i] : bb0;
       const bool diag = a == bb0;   // only single-tile waves hold a diagonal tile
       const int r = 16 * a + l16, s0 = 16 * bb0 + l16, s1 = 16 * bb1 + l16;
+      const float* d0p = sBlk + (kBlkD + (diag ? 0 : t0i - 4)) * DK;
+      const float* d1p = sBlk + (kBlkD + (ntile > 1 ? t1i - 4 : 0)) * DK;
       f32x4 accA0 = zero4(), accM0 = zero4(), accA1 = zero4(), accM1 = zero4();
 #pragma unroll
       for (int sl = 0; sl < DK / 32; ++sl) {
         const int c0 = 32 * sl + g4, c1 = c0 + 16;
-        // row factor e^{Gamma_r - Gamma_p}: the local sum itself
-        const f32x4 er0 = exp2v(*reinterpret_cast<const f32x4*>(sG + r * L::LG + c0));
-        const f32x4 er1 = exp2v(*reinterpret_cast<const f32x4*>(sG + r * L::LG + c1));
-        // column factor e^{Gamma_p - Gamma_s} = e^{(Gamma_p - Gamma_p') - local_s}, p' = s's block start
-        const f32x4 d00 = diag ? zero4() : *reinterpret_cast<const f32x4*>(sBlk + (t0i - 4) * DK + c0);
-        const f32x4 d01 = diag ? zero4() : *reinterpret_cast<const f32x4*>(sBlk + (t0i - 4) * DK + c1);
-        const f32x4 rk0 = widen4(load4(sK + r * L::LK + c0)) * er0, rk1 = widen4(load4(sK + r * L::LK + c1)) * er1;
-        const f32x4 rq0 = widen4(load4(sQ + r * L::LK + c0)) * er0, rq1 = widen4(load4(sQ + r * L::LK + c1)) * er1;
-        const Slab<Gm> RK = make_slab<Gm>(rk0, rk1);
-        const f32x4 fs0 = exp2v(d00 - *reinterpret_cast<const f32x4*>(sG + s0 * L::LG + c0));
-        const f32x4 fs1 = exp2v(d01 - *reinterpret_cast<const f32x4*>(sG + s0 * L::LG + c1));
-        const f32x4 ck0 = widen4(load4(sK + s0 * L::LK + c0)) * fs0, ck1 = widen4(load4(sK + s0 * L::LK + c1)) * fs1;
+        auto ld = [&](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
+        const Slab<Gm> RK = make_slab<Gm>(ld(sKP + r * L::LG + c0), ld(sKP + r * L::LG + c1));
+        const f32x4 rq0 = ld(sQP + r * L::LG + c0), rq1 = ld(sQP + r * L::LG + c1);
+        f32x4 ck0 = ld(sKM + s0 * L::LG + c0), ck1 = ld(sKM + s0 * L::LG + c1);
         if (P::kMixed && diag) {
           Slab<Gm> CKh, CKl, RQh, RQl;
           make_slab_split<Gm>(ck0, ck1, CKh, CKl);
@@ -416,17 +454,17 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
           accM0 = mma(CKl, RQh, accM0);
           accM0 = mma(CKh, RQl, accM0);
         } else {
+          if (!diag) {
+            ck0 = ck0 * ld(d0p + c0);
+            ck1 = ck1 * ld(d0p + c1);
+          }
           const Slab<Gm> RQ = make_slab<Gm>(rq0, rq1);
           const Slab<Gm> CK = make_slab<Gm>(ck0, ck1);
           accA0 = mma(CK, RK, accA0);   // A^T tile: lane holds A[r][16bb + g4 + i]
           accM0 = mma(CK, RQ, accM0);   // M^T tile: lane holds M[r][16bb + g4 + i]
           if (ntile > 1) {
-            const f32x4 d10 = *reinterpret_cast<const f32x4*>(sBlk + (t1i - 4) * DK + c0);
-            const f32x4 d11 = *reinterpret_cast<const f32x4*>(sBlk + (t1i - 4) * DK + c1);
-            const f32x4 ft0 = exp2v(d10 - *reinterpret_cast<const f32x4*>(sG + s1 * L::LG + c0));
-            const f32x4 ft1 = exp2v(d11 - *reinterpret_cast<const f32x4*>(sG + s1 * L::LG + c1));
-            const Slab<Gm> CK1 = make_slab<Gm>(widen4(load4(sK + s1 * L::LK + c0)) * ft0,
-                                               widen4(load4(sK + s1 * L::LK + c1)) * ft1);
+            const Slab<Gm> CK1 = make_slab<Gm>(ld(sKM + s1 * L::LG + c0) * ld(d1p + c0),
+                                               ld(sKM + s1 * L::LG + c1) * ld(d1p + c1));
             accA1 = mma(CK1, RK, accA1);
             accM1 = mma(CK1, RQ, accM1);
           }
@@ -448,72 +486,100 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       }
     }
   }
-  prefetch(std::integral_constant<int, kLoadQ>{});
   if (w >= 2) {   // the six tiles above the diagonal of the record's M are zero
     // (the mirror of lower tile (a, b): row block b, column block a)
     const int zt = w - 2, kt = kTileA[4 + zt], rt = kTileB[4 + zt];
     store4<Op>(rM + (kt * 4 + rt) * 256 + 4 * lane, narrow4<Op>(zero4()));
   }
-  // Khat tiles (st, ct), NTK of them: a quarter each to waves 6 and 7, an
-  // eighth each to waves 0-3 (waves 4 and 5 carry two Gram tiles)
-  constexpr int NTK = DK / 4;
-  // lane holds Khat[16st + g4 + i][16ct + l16] of tile t = st * (DK/16) + ct;
-  // e^{Gamma_C - Gamma_r} = e^{(Gamma_C - Gamma_p) - local_r}, p = row block st's start.
-  // Fixed trip counts (unrolled), so that every task's LDS reads are issued
-  // before the first exponential.
-  auto khat_tasks = [&](int kb0, auto ntask) {
-    constexpr int N = decltype(ntask)::value;
-    f32x4 val[N];
+  // V's range (for its fp16 staging): wave maxima of the chunk's v, combined
+  // after the barrier
+  float vmax = 0.f;
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int t = kb0 + j, st = t / (DK / 16), ct = t % (DK / 16);
-      const int col = 16 * ct + l16, row0 = 16 * st + g4;
-      const float dC = sBlk[(6 + st) * DK + col];
+  for (int i = 0; i < IR::NV; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        val[j][i] = to_f32(sK[(row0 + i) * L::LK + col]) * exp2_fast(dC - sG[(row0 + i) * L::LG + col]);
-    }
-#pragma unroll
-    for (int j = 0; j < N; ++j) store4<Op>(rK + (kb0 + j) * 256 + 4 * lane, narrow4<Op>(val[j]));
-  };
-  if (w < 4) khat_tasks(w * (NTK / 8), std::integral_constant<int, NTK / 8>{});
-  else if (w >= 6) khat_tasks(NTK / 2 + (w - 6) * (NTK / 4), std::integral_constant<int, NTK / 4>{});
-  if (tid >= 256 && tid < 256 + DK) rDec[tid - 256] = exp2_fast(sBlk[18 * DK + tid - 256]);
-  // Qbar = scale e^Gamma q into the record and Kbar = e^Gamma k into
-  // registers, tiles (ct, rt) of this wave: lane holds row 16rt + l16,
-  // columns 16ct + g4 .. +3 (one exponential for both)
-  V4<Op> kbar[NQW];
-#pragma unroll
-  for (int j = 0; j < NQW; ++j) {
-    int ct, rt;
-    wave_tile(w, j, NQW, ct, rt);
-    const int row = 16 * rt + l16, col = 16 * ct + g4;
-    const f32x4 e = exp2v((*reinterpret_cast<const f32x4*>(sBlk + (10 + rt) * DK + col) +
-                           *reinterpret_cast<const f32x4*>(sG + row * L::LG + col)) +
-                          *reinterpret_cast<const f32x4*>(sBlk + (14 + rt) * DK + col));
-    store4<Op>(rQ + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(widen4(load4(sQ + row * L::LK + col)) * e * scale));
-    kbar[j] = narrow4<Op>(widen4(load4(sK + row * L::LK + col)) * e);
-  }
-  __syncthreads();   // sQ is dead from here on; R2 becomes Tm
+    for (int x = 0; x < VE; ++x) vmax = fmaxf(vmax, fabsf(raw_elem<TIn>(in.v[i], x)));
+  vmax = wave_max_dpp(vmax);
+  if (lane == 0) sRed[w] = vmax;
+  prefetch(std::integral_constant<int, kLoadQ>{});
+  __syncthreads();   // A complete
 
-  // ---- phase 2: X = (I + A)^-1 by 16x16 blocks, fp32
-  if (w == 0) {   // diagonal blocks by forward substitution; lane = (block, column)
+  // ---- phase 2a: diagonal blocks of X = (I + A)^-1 (wave 0) while waves
+  // 1-7 write Qbar, Khat and e^{Gamma_C} to the record
+  if (w == 0) {
+    // forward substitution, right-looking: lane = (block a, column j); once
+    // x_m is final it is eliminated from every later row at once
     const int a = lane >> 4, j = lane & 15;
     const float* Ab = sA + 16 * a * L::LA + 16 * a;
     float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = (i == j) ? 1.f : 0.f;
+    for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < i; ++m) acc -= Ab[i * L::LA + m] * x[m];
-      x[i] = acc;
-    }
+    for (int m = 0; m < 15; ++m)
+#pragma unroll
+      for (int i = m + 1; i < 16; ++i) x[i] = fmaf(-Ab[i * L::LA + m], x[m], x[i]);
     float* Xb = sX + 16 * a * L::LA + 16 * a;
 #pragma unroll
     for (int i = 0; i < 16; ++i) Xb[i * L::LA + j] = x[i];
+  } else {
+    if (tid >= 64 && tid < 64 + DK) rDec[tid - 64] = sBlk[kBlkDec * DK + tid - 64];
+    for (int t = w - 1; t < 2 * NQT; t += kNW - 1) {
+      if (t < NQT) {
+        // Qbar tile (ct, rt): lane holds row 16rt + l16, columns 16ct + g4 .. +3
+        const int ct = t >> 2, rt = t & 3;
+        const int row = 16 * rt + l16, col = 16 * ct + g4;
+        const f32x4 f = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + col);
+        store4<Op>(rQ + t * 256 + 4 * lane,
+                   narrow4<Op>(*reinterpret_cast<const f32x4*>(sQP + row * L::LG + col) * (f * scale)));
+      } else {
+        // Khat tile t' = st * (DK/16) + ct: lane holds Khat[16st + g4 + i][16ct + l16]
+        const int tk = t - NQT, st = tk / (DK / 16), ct = tk % (DK / 16);
+        const int col = 16 * ct + l16, row0 = 16 * st + g4;
+        const float e = sBlk[(kBlkE + st) * DK + col];
+        f32x4 val;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) val[i] = (sKM[(row0 + i) * L::LG + col] * e) * kTwoM64;
+        store4<Op>(rK + tk * 256 + 4 * lane, narrow4<Op>(val));
+      }
+    }
   }
   prefetch(std::integral_constant<int, kLoadG>{});
-  __syncthreads();
+  __syncthreads();   // QP, KM dead; diagonal blocks of X complete
+
+  // ---- phase 2b: Kbar^T and V^T (range-scaled) into P1, then the
+  // off-diagonal blocks of X, then Tm = X Diag(beta) where A was
+  float sv = 1.f;
+  if (P::kMixed) {
+    float m = sRed[0];
+#pragma unroll
+    for (int i = 1; i < kNW; ++i) m = fmaxf(m, sRed[i]);
+    sv = fp16_range_scale(m);
+  }
+#pragma unroll
+  for (int j = 0; j < NQW; ++j) {   // Kbar tile (ct, rt) staged transposed
+    int ct, rt;
+    wave_tile(w, j, NQW, ct, rt);
+    const int row = 16 * rt + l16, col = 16 * ct + g4;
+    const f32x4 f = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + col);
+    const V4<Op> kb = narrow4<Op>(*reinterpret_cast<const f32x4*>(sKP + row * L::LG + col) * f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sKbt[(col + i) * L::LB + row] = kb[i];
+  }
+  constexpr int NVV = kC * DV / VE;
+  {
+    raw16 vreg[IR::NV];
+#pragma unroll
+    for (int i = 0; i < IR::NV; ++i) vreg[i] = in.v[i];
+    prefetch(std::integral_constant<int, kLoadV>{});
+#pragma unroll
+    for (int i = 0; i < IR::NV; ++i) {   // consecutive lanes hold consecutive rows (see load_inputs)
+      const int n = tid + kThreads * i;
+      if (n < NVV) {
+        const int r = n % kC, c = (n / kC) * VE;
+#pragma unroll
+        for (int x = 0; x < VE; ++x) sVt[(c + x) * L::LB + r] = from_f32<Op>(raw_elem<TIn>(vreg[i], x) * sv);
+      }
+    }
+  }
   // off-diagonal blocks by distance d = a - b: X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb
   for (int d = 1; d < 4; ++d) {
     if (w < 4 - d) {
@@ -527,22 +593,13 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     }
     __syncthreads();
   }
-  // Tm = X Diag(beta), lower triangle
-  for (int n = tid; n < kC * kC; n += kThreads) {
+  for (int n = tid; n < kC * kC; n += kThreads) {   // A is dead: Tm takes its place
     const int r = n >> 6, s = n & 63;
     sTm[r * L::LB + s] = from_f32<Op>(s <= r ? sX[r * L::LA + s] * sBeta[s] : 0.f);
   }
+  __syncthreads();   // Tm, Kbar^T, V^T complete
 
-  // ---- phase 3a: Kbar^T into R1 (from the registers of phase 1), then W
-  __syncthreads();   // sK and sX dead; sTm complete
-#pragma unroll
-  for (int j = 0; j < NQW; ++j) {
-    int ct, rt;
-    wave_tile(w, j, NQW, ct, rt);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sKbt[(16 * ct + g4 + i) * L::LB + 16 * rt + l16] = kbar[j][i];
-  }
-  __syncthreads();
+  // ---- phase 3: W = Tm Kbar (as W^T tiles) and Ut = Tm V into the record
 #pragma unroll
   for (int j = 0; j < NQW; ++j) {   // W^T tile (ct, rt)
     int ct, rt;
@@ -550,29 +607,6 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     const f32x4 acc = tri_mma(sKbt + (16 * ct + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
     store4<Op>(rW + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(acc));
   }
-
-  // ---- phase 3b: V^T (range-scaled) into R1, then Ut = Tm V
-  raw16 vreg[IR::NV];
-#pragma unroll
-  for (int i = 0; i < IR::NV; ++i) vreg[i] = in.v[i];
-  prefetch(std::integral_constant<int, kLoadV>{});
-  float vmax = 0.f;
-#pragma unroll
-  for (int i = 0; i < VPT; ++i)
-#pragma unroll
-    for (int x = 0; x < VE; ++x) vmax = fmaxf(vmax, fabsf(raw_elem<TIn>(vreg[i], x)));
-  const float sv = P::kMixed ? fp16_range_scale(block_max(vmax, sRed)) : 1.f;   // barriers inside
-  if (!P::kMixed) __syncthreads();   // R1 (Kbar^T) readers done
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {   // consecutive lanes hold consecutive rows (see load_inputs)
-    const int n = tid + kThreads * i;
-    if (n < NVV) {
-      const int r = n % kC, c = (n / kC) * VE;
-#pragma unroll
-      for (int x = 0; x < VE; ++x) sVt[(c + x) * L::LB + r] = from_f32<Op>(raw_elem<TIn>(vreg[i], x) * sv);
-    }
-  }
-  __syncthreads();
   constexpr int NUT = (DV / 16) * 4;
   constexpr int NUW = NUT / kNW;
   f32x4 ut[NUW];
@@ -586,7 +620,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   }
   // Ut into the record as Op, range-scaled by su (exact power of two)
   float su = 1.f, suinv = 1.f;
-  if (P::kMixed) fp16_range_scale2(block_max(umax, sRed), su, suinv);
+  if (P::kMixed) fp16_range_scale2(block_max(umax, sRed + 8), su, suinv);
 #pragma unroll
   for (int j = 0; j < NUW; ++j) {
     int jt, st;
@@ -883,7 +917,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 
     // O = Qbar S + (scale M) U, as O^T tiles (O^T = S^T Qbar^T + U^T (scale
     // M)^T): lane l holds row 16rt + l%16, columns 16jt + 4(l/16) .. +3,
-    // stored as one 16-byte vector
+    // stored as one 16-byte non-temporal vector (written once, not re-read)
     const int t0 = c * kC;
     const bool full = t0 + kC <= T_len;   // uniform; only the last chunk is partial
     float* orow = o + (((size_t)b * T_len + t0 + l16) * H + h) * DV + 16 * jt0 + g4;
@@ -923,7 +957,8 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
         const f32x4 r = accQ[jj] * iss + accM[jj] * ius;
-        if (full || t0 + 16 * rt + l16 < T_len) *reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj) = r;
+        if (full || t0 + 16 * rt + l16 < T_len)
+          __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj));
       }
     }
 
