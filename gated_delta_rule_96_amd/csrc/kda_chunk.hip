@@ -881,25 +881,37 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) Sb[ct][jj] = narrow4<Op>(S[ct][jj] * ss);
 
-    // U = Ut - W S
-    // (each stage reads all its LDS operands of one row block before the
-    // products, so that one LDS latency is paid per block, not per product)
-    f32x4 U[4][NJ];
+    // U = Ut - W S and the Qbar S part of O, row block by row block: the two
+    // products need only S, so their LDS reads and MFMAs interleave (each
+    // block's operands are read before its products, one LDS latency per
+    // block).  O^T = S^T Qbar^T + U^T (scale M)^T: lane l holds row
+    // 16rt + l%16, columns 16jt + 4(l/16) .. +3.
+    f32x4 U[4][NJ], accQ[4][NJ];
     float umax = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       f32x4 Pv[NJ];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) Pv[jj] = zero4();
-      Slab<Op> Wa[DK / 32];
+      for (int jj = 0; jj < NJ; ++jj) {
+        Pv[jj] = zero4();
+        accQ[st][jj] = zero4();
+      }
+      Slab<Op> Wa[DK / 32], Qa[DK / 32];
 #pragma unroll
-      for (int sl = 0; sl < DK / 32; ++sl)
+      for (int sl = 0; sl < DK / 32; ++sl) {
         Wa[sl] = slab_of<Op>(load4(sW + ((2 * sl) * 4 + st) * 256 + 4 * lane),
                              load4(sW + ((2 * sl + 1) * 4 + st) * 256 + 4 * lane));
+        Qa[sl] = slab_of<Op>(load4(sQ + ((2 * sl) * 4 + st) * 256 + 4 * lane),
+                             load4(sQ + ((2 * sl + 1) * 4 + st) * 256 + 4 * lane));
+      }
 #pragma unroll
       for (int sl = 0; sl < DK / 32; ++sl) {
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) Pv[jj] = mma(Wa[sl], slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]), Pv[jj]);
+        for (int jj = 0; jj < NJ; ++jj) {
+          const Slab<Op> sb = slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]);
+          Pv[jj] = mma(Wa[sl], sb, Pv[jj]);
+          accQ[st][jj] = mma(sb, Qa[sl], accQ[st][jj]);
+        }
       }
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
@@ -915,37 +927,25 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) Ub[st][jj] = narrow4<Op>(U[st][jj] * us);
 
-    // O = Qbar S + (scale M) U, as O^T tiles (O^T = S^T Qbar^T + U^T (scale
-    // M)^T): lane l holds row 16rt + l%16, columns 16jt + 4(l/16) .. +3,
-    // stored as one 16-byte non-temporal vector (written once, not re-read)
+    // O = Qbar S + (scale M) U, stored as 16-byte non-temporal vectors
+    // (written once, not re-read)
     const int t0 = c * kC;
     const bool full = t0 + kC <= T_len;   // uniform; only the last chunk is partial
     float* orow = o + (((size_t)b * T_len + t0 + l16) * H + h) * DV + 16 * jt0 + g4;
     const size_t ors = (size_t)16 * H * DV;   // 16 rows
+    f32x4 Ov[4][NJ];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      f32x4 accQ[NJ], accM[NJ];
+      f32x4 accM[NJ];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        accQ[jj] = zero4();
-        accM[jj] = zero4();
-      }
-      Slab<Op> Qa[DK / 32], Ma[2];
-#pragma unroll
-      for (int sl = 0; sl < DK / 32; ++sl)
-        Qa[sl] = slab_of<Op>(load4(sQ + ((2 * sl) * 4 + rt) * 256 + 4 * lane),
-                             load4(sQ + ((2 * sl + 1) * 4 + rt) * 256 + 4 * lane));
+      for (int jj = 0; jj < NJ; ++jj) accM[jj] = zero4();
+      Slab<Op> Ma[2];
       const int nms = rt < 2 ? 1 : 2;   // slabs of M's row block rt that are not all zero
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl)
         if (sl < nms)
           Ma[sl] = slab_of<Op>(load4(sM + ((2 * sl) * 4 + rt) * 256 + 4 * lane),
                                load4(sM + ((2 * sl + 1) * 4 + rt) * 256 + 4 * lane));
-#pragma unroll
-      for (int sl = 0; sl < DK / 32; ++sl) {
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) accQ[jj] = mma(slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]), Qa[sl], accQ[jj]);
-      }
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
         if (sl < nms) {
@@ -955,11 +955,21 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        const f32x4 r = accQ[jj] * iss + accM[jj] * ius;
-        if (full || t0 + 16 * rt + l16 < T_len)
-          __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj));
-      }
+      for (int jj = 0; jj < NJ; ++jj) Ov[rt][jj] = accQ[rt][jj] * iss + accM[jj] * ius;
+    }
+    if (full) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          __builtin_nontemporal_store(Ov[rt][jj], reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj));
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          if (t0 + 16 * rt + l16 < T_len)
+            __builtin_nontemporal_store(Ov[rt][jj], reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj));
     }
 
     // S <- e^{Gamma_C} S + Khat^T U
