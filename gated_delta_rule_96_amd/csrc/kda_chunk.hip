@@ -50,6 +50,8 @@
 //   K  : tile (st, ct) lane l = Khat[16st + 4(l/16) + i][16ct + l%16]    (Op)
 //   M  : tile (kt, rt) lane l = scale M[16rt + l%16][16kt + 4(l/16) + i] (Op)
 //        (tiles above the diagonal are zero)
+//   (tile order: tile_cr / tile_k below, the two tiles of one operand slab
+//   next to each other)
 //   dec: fp32 [dk] = e^{Gamma_C};  uinv: fp32, 1 / (scale factor of U)
 //   U  : tile (st, jt) lane l = Ut[16st + 4(l/16) + i][16jt + l%16] * su (Op),
 //        tiles column-block major (index 4 jt + st)
@@ -87,6 +89,17 @@ struct Rec {
   static constexpr size_t BYTES = (U_OFF_BYTES + (size_t)kC * DV * sizeof(Op) + 255) / 256 * 256;
   static_assert(U_OFF_BYTES % 16 == 0, "record alignment");
 };
+
+// Record tile order.  The state pass reads operand slabs made of two tiles
+// that are consecutive along the reduction index (reduction tiles 2s and
+// 2s + 1); those two tiles are stored next to each other, so one paired LDS
+// read puts a lane's slab straight into consecutive registers.
+//   W, Q, M tile (ct, rt), reduction tile ct, 4 row tiles rt
+__host__ __device__ constexpr int tile_cr(int ct, int rt) { return (ct >> 1) * 8 + rt * 2 + (ct & 1); }
+//   K tile (st, ct), reduction tile st, NCT column tiles ct
+template <int NCT> __host__ __device__ constexpr int tile_k(int st, int ct) {
+  return (st >> 1) * (2 * NCT) + ct * 2 + (st & 1);
+}
 
 typedef float raw16 __attribute__((ext_vector_type(4)));   // 16 raw bytes
 
@@ -482,14 +495,14 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
           mrow[i] = sc <= r ? accM[i] : 0.f;
         }
         *reinterpret_cast<f32x4*>(sA + r * L::LA + 16 * bb + g4) = arow;
-        store4<Op>(rM + (bb * 4 + a) * 256 + 4 * lane, narrow4<Op>(mrow * scale));
+        store4<Op>(rM + tile_cr(bb, a) * 256 + 4 * lane, narrow4<Op>(mrow * scale));
       }
     }
   }
   if (w >= 2) {   // the six tiles above the diagonal of the record's M are zero
     // (the mirror of lower tile (a, b): row block b, column block a)
     const int zt = w - 2, kt = kTileA[4 + zt], rt = kTileB[4 + zt];
-    store4<Op>(rM + (kt * 4 + rt) * 256 + 4 * lane, narrow4<Op>(zero4()));
+    store4<Op>(rM + tile_cr(kt, rt) * 256 + 4 * lane, narrow4<Op>(zero4()));
   }
   // V's range (for its fp16 staging): wave maxima of the chunk's v, combined
   // after the barrier
@@ -528,17 +541,17 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
         const int ct = t >> 2, rt = t & 3;
         const int row = 16 * rt + l16, col = 16 * ct + g4;
         const f32x4 f = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + col);
-        store4<Op>(rQ + t * 256 + 4 * lane,
+        store4<Op>(rQ + tile_cr(ct, rt) * 256 + 4 * lane,
                    narrow4<Op>(*reinterpret_cast<const f32x4*>(sQP + row * L::LG + col) * (f * scale)));
       } else {
-        // Khat tile t' = st * (DK/16) + ct: lane holds Khat[16st + g4 + i][16ct + l16]
+        // Khat tile (st, ct): lane holds Khat[16st + g4 + i][16ct + l16]
         const int tk = t - NQT, st = tk / (DK / 16), ct = tk % (DK / 16);
         const int col = 16 * ct + l16, row0 = 16 * st + g4;
         const float e = sBlk[(kBlkE + st) * DK + col];
         f32x4 val;
 #pragma unroll
         for (int i = 0; i < 4; ++i) val[i] = (sKM[(row0 + i) * L::LG + col] * e) * kTwoM64;
-        store4<Op>(rK + tk * 256 + 4 * lane, narrow4<Op>(val));
+        store4<Op>(rK + tile_k<DK / 16>(st, ct) * 256 + 4 * lane, narrow4<Op>(val));
       }
     }
   }
@@ -605,7 +618,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     int ct, rt;
     wave_tile(w, j, NQW, ct, rt);
     const f32x4 acc = tri_mma(sKbt + (16 * ct + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
-    store4<Op>(rW + (ct * 4 + rt) * 256 + 4 * lane, narrow4<Op>(acc));
+    store4<Op>(rW + tile_cr(ct, rt) * 256 + 4 * lane, narrow4<Op>(acc));
   }
   constexpr int NUT = (DV / 16) * 4;
   constexpr int NUW = NUT / kNW;
@@ -899,10 +912,10 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       Slab<Op> Wa[DK / 32], Qa[DK / 32];
 #pragma unroll
       for (int sl = 0; sl < DK / 32; ++sl) {
-        Wa[sl] = slab_of<Op>(load4(sW + ((2 * sl) * 4 + st) * 256 + 4 * lane),
-                             load4(sW + ((2 * sl + 1) * 4 + st) * 256 + 4 * lane));
-        Qa[sl] = slab_of<Op>(load4(sQ + ((2 * sl) * 4 + st) * 256 + 4 * lane),
-                             load4(sQ + ((2 * sl + 1) * 4 + st) * 256 + 4 * lane));
+        Wa[sl] = slab_of<Op>(load4(sW + tile_cr(2 * sl, st) * 256 + 4 * lane),
+                             load4(sW + tile_cr(2 * sl + 1, st) * 256 + 4 * lane));
+        Qa[sl] = slab_of<Op>(load4(sQ + tile_cr(2 * sl, st) * 256 + 4 * lane),
+                             load4(sQ + tile_cr(2 * sl + 1, st) * 256 + 4 * lane));
       }
 #pragma unroll
       for (int sl = 0; sl < DK / 32; ++sl) {
@@ -944,8 +957,8 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl)
         if (sl < nms)
-          Ma[sl] = slab_of<Op>(load4(sM + ((2 * sl) * 4 + rt) * 256 + 4 * lane),
-                               load4(sM + ((2 * sl + 1) * 4 + rt) * 256 + 4 * lane));
+          Ma[sl] = slab_of<Op>(load4(sM + tile_cr(2 * sl, rt) * 256 + 4 * lane),
+                               load4(sM + tile_cr(2 * sl + 1, rt) * 256 + 4 * lane));
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
         if (sl < nms) {
@@ -980,8 +993,8 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl)
-          Ka[cc][sl] = slab_of<Op>(load4(sK + ((2 * sl) * NCT + cp + cc) * 256 + 4 * lane),
-                                   load4(sK + ((2 * sl + 1) * NCT + cp + cc) * 256 + 4 * lane));
+          Ka[cc][sl] = slab_of<Op>(load4(sK + tile_k<NCT>(2 * sl, cp + cc) * 256 + 4 * lane),
+                                   load4(sK + tile_k<NCT>(2 * sl + 1, cp + cc) * 256 + 4 * lane));
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int ct = cp + cc;
