@@ -73,3 +73,13 @@ def test_gate_pins_reject_mutants():
     no_exp = -5.0 / (1 + np.exp(-(A[None, None, :, None] * z)))          # exp(A) replaced by A
     flipped = -5.0 / (1 + np.exp(+(np.exp(A)[None, None, :, None] * z)))  # sign of the argument
     assert abs(no_exp.item() + 3.75) > 1e-3 and abs(flipped.item() + 3.75) > 1e-3
+
+
+def test_softplus_gate_pins_reject_mutants():
+    A = np.array([0.7])
+    x = np.log(np.e - 1.0)
+    z = np.full((1, 1, 1, 1), x / np.exp(0.7))
+    assert abs(gate.gate_softplus(z, A).item() + 1.0) < 1e-14
+    no_log1p = -(np.maximum(x, 0) + np.exp(-abs(x)))                  # log1p dropped
+    no_max = -np.log1p(np.exp(-abs(x)))                                 # max(x, 0) dropped
+    assert abs(no_log1p + 1.0) > 1e-3 and abs(no_max + 1.0) > 1e-3

@@ -169,6 +169,36 @@ def test_gate_closed_forms():
     assert np.all(gate.gate(np.full((1, 1, 3, 1), 200.0), A) == -5.0)    # floor reached
 
 
+def test_softplus_gate_closed_forms():
+    A = np.array([-1.0, 0.0, 0.7])
+    e = np.exp(A)[None, None, :, None]
+    np.testing.assert_allclose(gate.gate_softplus(np.zeros((1, 1, 3, 2)), A), -math.log(2.0), rtol=0, atol=1e-15)
+    z1 = (math.log(math.e - 1.0) / e) * np.ones((1, 1, 3, 2))       # Softplus(ln(e - 1)) = 1
+    np.testing.assert_allclose(gate.gate_softplus(z1, A), -1.0, rtol=0, atol=1e-14)
+    rng = np.random.default_rng(3)
+    zz = 4 * rng.standard_normal((2, 5, 3, 4))
+    # Softplus(x) - Softplus(-x) = x
+    np.testing.assert_allclose(gate.gate_softplus(zz, A) - gate.gate_softplus(-zz, A), -e * zz, atol=1e-12)
+    big = np.full((1, 1, 3, 1), 300.0)
+    np.testing.assert_allclose(gate.gate_softplus(big, A), -e * big, rtol=1e-15)   # no floor: -x
+    assert np.all(np.isfinite(gate.gate_softplus(-big, A))) and np.all(gate.gate_softplus(-big, A) < 0)
+
+
+def test_total_forgetting_closed_form():
+    # With exp(g) = 0 (a log-decay far below any floor) the state keeps only
+    # the current token: S_t = beta_t k_t v_t^T, o_t = beta_t (q_t . k_t) v_t / sqrt(dk).
+    rng = np.random.default_rng(5)
+    q, k, v, _, beta, h0 = _rand_case(rng, 1, 7, 2, 4, 3)
+    g = np.full(q.shape, -800.0)
+    o, ht = seq.kda_seq(q, k, v, g, beta, h0)
+    qk = np.einsum("bthd,bthd->bth", q.astype(np.float64), k.astype(np.float64))
+    want = (beta * qk)[..., None] * v / math.sqrt(4)
+    np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-12)
+    k64, v64, b64 = (x.astype(np.float64) for x in (k, v, beta))
+    np.testing.assert_allclose(ht[0], b64[0, -1][:, None, None] * np.einsum("hd,he->hde", k64[0, -1], v64[0, -1]),
+                               rtol=1e-12, atol=1e-12)
+
+
 def test_gate_monotone_and_in_range():
     d = synth.make_inputs(1, 256, 4, 64, 8, seed=1, with_h0=False)
     g = gate.gate(d["z"], d["A"])
