@@ -88,6 +88,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=DSTEPS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards by "
@@ -160,6 +161,64 @@ def main():
     log(f"two-kernel schedule: intra-chunk {ms_intra:.3f} ms + state pass {ms_state:.3f} ms; same output {same}")
 
     flop, abytes = prefill_alg_counts(B, T, H, DK, DV, CHUNK)
+
+    # ---------------- unbounded-decay ablation: the same workload through the
+    # kernel for a log-decay with no lower bound (diagonal tiles by position
+    # pairs), on the bounded g and on the unbounded -Softplus gate of the same
+    # z and A; parity of the latter on two whole heads
+    ablation = None
+    if not args.no_ablation:
+        o_a = torch.empty_like(o)
+        ht_a = torch.empty_like(ht)
+
+        def time_unbounded(gg, n):
+            kda.fwd_chunked(q, k, v, gg, beta, h0, ht=ht_a, workspace=ws, out=o_a, unbounded=True)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                kda.fwd_chunked(q, k, v, gg, beta, h0, ht=ht_a, workspace=ws, out=o_a, unbounded=True)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if kda.workspace_error(ws) != 0:
+                raise RuntimeError("unbounded prefill reported a hand-off timeout")
+            return e0.elapsed_time(e1) / n
+
+        ms_u_bounded = time_unbounded(g, n_k)
+        g_sp, _ = kda.prepare_decay(z, A, want_gcum=False, softplus=True)
+        ms_u_sp = time_unbounded(g_sp, n_k)
+        g_sp_min = float(g_sp.float().min())
+        ab_parity = None
+        if not args.no_cpu_baseline:
+            from oracle import gate as ogate
+            from oracle import seq
+
+            heads = [3, 28]
+            f = lambda t: t.float().numpy()
+            sel = lambda t: f(t[:, :, heads].cpu())
+            o_ref, _ = seq.kda_seq(sel(q), sel(k), sel(v), sel(g_sp), sel(beta), d["h0"][:, heads],
+                                   nthreads=seq.threads_default())
+            o_gpu = o_a[:, :, heads].cpu().double().numpy()
+            rms = math.sqrt(float(np.mean(o_ref * o_ref)))
+            ab_parity = {"sample": f"o of heads {heads}, all {T} tokens, vs fp64 oracle on the same bf16 g",
+                         "max_err_over_rms": float(np.max(np.abs(o_gpu - o_ref)) / rms), "tolerance": 2e-2}
+        ablation = {
+            "what": "same workload through kda_fwd_chunked_unbounded (decay with no lower bound: the 4 diagonal "
+                    "16x16 tiles of A and M per chunk as fp32 position-pair sums instead of rescaled dense MFMA "
+                    "tiles)",
+            "bounded_kernel_ms": round(ms_step, 4),
+            "unbounded_kernel_ms_bounded_g": round(ms_u_bounded, 4),
+            "unbounded_kernel_ms_softplus_g": round(ms_u_sp, 4),
+            "softplus_g_min": round(g_sp_min, 2),
+            "slowdown": round(ms_u_sp / ms_step, 3),
+            "mfma_frac_bounded": round(flop / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_unbounded": round(flop / (ms_u_sp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "parity_unbounded_softplus_g": ab_parity,
+        }
+        log(f"ablation: unbounded kernel {ms_u_bounded:.3f} ms (bounded g), {ms_u_sp:.3f} ms (softplus g, "
+            f"min {g_sp_min:.1f}) vs bounded {ms_step:.3f} ms"
+            + (f"; parity {ab_parity['max_err_over_rms']:.2e}" if ab_parity else ""))
+        del o_a, ht_a, g_sp
+
     tok_s = B * T / (ms_step * 1e-3)
     gbs = abytes / (ms_step * 1e-3) / 1e9
     tflops = flop / (ms_step * 1e-3) / 1e12
@@ -255,6 +314,7 @@ def main():
                                                "state_pass_kernel": round(ms_state, 4),
                                                "bitwise_equal_output": same}},
         "decode": decode,
+        "unbounded_decay_ablation": ablation,
         "parity": parity,
         "cpu_baseline": cpu,
     }

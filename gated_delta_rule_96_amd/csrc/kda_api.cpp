@@ -49,8 +49,9 @@ const char* kda_status_str(int s) {
   }
 }
 
-int kda_prepare_decay(const void* z, const float* A, float gmin, void* g, float* gcum, int dtype, int B, int T,
-                      int H, int dk, int chunk, void* stream) {
+namespace {
+int prepare_decay_impl(const void* z, const float* A, float gmin, void* g, float* gcum, int dtype, int B, int T,
+                       int H, int dk, int chunk, int softplus, void* stream) {
   if (!valid_dtype(dtype)) return KDA_ERR_DTYPE;
   if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || chunk <= 0 || !size_ok(B, T, H, dk)) return KDA_ERR_SHAPE;
   if (!supported_d(dk) || chunk != kChunk) return KDA_ERR_UNSUPPORTED;
@@ -61,9 +62,21 @@ int kda_prepare_decay(const void* z, const float* A, float gmin, void* g, float*
   }
   if ((z && !aligned16(z)) || (g && !aligned16(g)) || (gcum && !aligned16(gcum)) || (A && !aligned16(A)))
     return KDA_ERR_ALIGN;
-  hipError_t e = kda::launch_prepare_decay(dtype == KDA_BF16, z, A, gmin, g, gcum, B, T, H, dk, chunk,
+  hipError_t e = kda::launch_prepare_decay(dtype == KDA_BF16, z, A, gmin, g, gcum, B, T, H, dk, chunk, softplus,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+}  // namespace
+
+int kda_prepare_decay(const void* z, const float* A, float gmin, void* g, float* gcum, int dtype, int B, int T,
+                      int H, int dk, int chunk, void* stream) {
+  return prepare_decay_impl(z, A, gmin, g, gcum, dtype, B, T, H, dk, chunk, 0, stream);
+}
+
+int kda_prepare_decay_softplus(const void* z, const float* A, void* g, float* gcum, int dtype, int B, int T, int H,
+                               int dk, int chunk, void* stream) {
+  if (!z) return KDA_ERR_NULL;
+  return prepare_decay_impl(z, A, 0.f, g, gcum, dtype, B, T, H, dk, chunk, 1, stream);
 }
 
 size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
@@ -83,7 +96,8 @@ size_t kda_fwd_stages_workspace_bytes(int B, int T, int H, int dk, int dv, int c
 
 namespace {
 
-// Shared validation of the prefill calls; `stages` is 3 for kda_fwd_chunked.
+// Shared validation of the prefill calls; `stages` is 3 for kda_fwd_chunked
+// (the stage mask, without the unbounded-decay bit).
 int check_fwd(const void* q, const void* k, const void* v, const void* g, const float* gcum, const void* beta,
               const float* h0, const float* ht, const float* o, int dtype, int B, int T, int H, int dk, int dv,
               int chunk, const void* workspace, int stages) {
@@ -105,26 +119,46 @@ int check_fwd(const void* q, const void* k, const void* v, const void* g, const 
 
 }  // namespace
 
-int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g, const float* gcum,
-                    const void* beta, float scale, const float* h0, float* ht, float* o, int dtype, int B, int T,
-                    int H, int dk, int dv, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+int fwd_fused_impl(const void* q, const void* k, const void* v, const void* g, const float* gcum, const void* beta,
+                   float scale, const float* h0, float* ht, float* o, int dtype, int B, int T, int H, int dk, int dv,
+                   int chunk, void* workspace, size_t workspace_bytes, int unbounded, void* stream) {
   const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace, 3);
   if (st != KDA_OK) return st;
   if (workspace_bytes < kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
   hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
-                                       workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+                                       workspace, workspace_bytes, unbounded, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+}  // namespace
+
+int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                    const void* beta, float scale, const float* h0, float* ht, float* o, int dtype, int B, int T,
+                    int H, int dk, int dv, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_fused_impl(q, k, v, g, gcum, beta, scale, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace,
+                        workspace_bytes, 0, stream);
+}
+
+int kda_fwd_chunked_unbounded(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                              const void* beta, float scale, const float* h0, float* ht, float* o, int dtype, int B,
+                              int T, int H, int dk, int dv, int chunk, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return fwd_fused_impl(q, k, v, g, gcum, beta, scale, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace,
+                        workspace_bytes, 1, stream);
 }
 
 int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                            const void* beta, float scale, const float* h0, float* ht, float* o, int dtype, int B,
                            int T, int H, int dk, int dv, int chunk, void* workspace, size_t workspace_bytes,
                            int stages, void* stream) {
-  const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace, stages);
+  const int mask = stages & ~KDA_STAGES_UNBOUNDED;
+  if ((stages & KDA_STAGES_UNBOUNDED) && mask < 1) return KDA_ERR_SHAPE;
+  const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace, mask);
   if (st != KDA_OK) return st;
   if (workspace_bytes < kda_fwd_stages_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
   hipError_t e = kda::launch_fwd_stages(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
-                                        workspace, stages, static_cast<hipStream_t>(stream));
+                                        workspace, mask, (stages & KDA_STAGES_UNBOUNDED) ? 1 : 0,
+                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

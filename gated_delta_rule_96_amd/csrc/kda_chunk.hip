@@ -225,48 +225,54 @@ __device__ __forceinline__ float exp2_split(double x) {
 }
 
 // Per-channel factors built from the chunk's block starts, fp32 rows of
-// [kNBlk][DK]; Gamma_p(a) = Gamma at row 16a - 1 (0 for a = 0), Gamma_C at
-// the chunk's last row:
+// [kNBlk][DK]; Gamma_p(a) = Gamma at row 16a - 1 (0 for a = 0; Gamma_p(4) =
+// Gamma_C at the chunk's last row), T_a = Gamma_p(a+1) - Gamma_p(a):
 constexpr int kBlkF = 0;     // rows 0-3   e^{Gamma_p(a)}
-constexpr int kBlkE = 4;     // rows 4-7   e^{Gamma_C - Gamma_p(a)} * 2^64
-constexpr int kBlkD = 8;     // rows 8-13  e^{Gamma_p(a) - Gamma_p(b)}, off-diagonal
+constexpr int kBlkE = 4;     // rows 4-7   e^{Gamma_C - Gamma_p(a+1)}
+constexpr int kBlkD = 8;     // rows 8-13  e^{Gamma_p(a) - Gamma_p(b+1)}, off-diagonal
                              //            tiles (a, b) in kTileA/kTileB order 4..9
 constexpr int kBlkDec = 14;  // row 14     e^{Gamma_C}
-constexpr int kNBlk = 15;
-// The 2^64 in the Khat factor keeps e^{Gamma_C - Gamma_p(a)} out of the
-// fp32 subnormal range wherever the product with e^{-G} is not negligible.
-constexpr float kTwoM64 = 5.421010862427522e-20f;   // 2^-64
+constexpr int kBlkM = 15;    // rows 15-18 e^{-T_a} (bounded decay only: <= e^80)
+constexpr int kNBlk = 19;
 
 // ---------------------------------------------------------------------------
 // Intra-chunk work: one work-group (8 waves) per (b*h, chunk).
 // G = Gamma - Gamma_p(a) for a row in 16-row block a (a sum of at most 16
-// decays, kept in fp32); everything else is a product of
-//   KP = k e^{G},  QP = q e^{G},  KM = k e^{-G}      (fp32, two exponentials
-// per element) and per-channel factors of the block starts (BLK):
-//   A, M tile (a, b):  row operand KP or QP (block a), column operand
-//                      KM * e^{Gamma_p(a) - Gamma_p(b)} (block b)
+// decays, kept in fp32; G <= 0 and G decreases along the block); everything
+// else is a product of
+//   KP = k e^{G},  QP = q e^{G},  KE = k e^{T_a - G}      (fp32, all three
+// bounded by |k| or |q|: two exponentials per element) and per-channel
+// factors of the block starts (BLK):
+//   A, M tile (a, b), b < a: row operand KP or QP (block a), column operand
+//                            KE * e^{Gamma_p(a) - Gamma_p(b+1)} (block b)
+//   diagonal tile (a, a):    bounded decay (g >= -5): column operand
+//                            KE * e^{-T_a} <= e^80 |k|, inside the bf16 range;
+//                            unbounded decay (kUnb): position-pair sums
+//                            sum_c k_rc k_sc e^{G_rc - G_sc} in fp32
 //   Qbar = scale e^{Gamma_p(a)} QP,  Kbar = e^{Gamma_p(a)} KP,
-//   Khat = e^{Gamma_C - Gamma_p(a)} KM
+//   Khat = e^{Gamma_C - Gamma_p(a+1)} KE
 // LDS regions, reused across phases (lifetimes in brackets):
 //   P0 : g, then G (fp32 [C][LG])                        [phase 0]
 //        -> KP (fp32 [C][LG])                              [0 - 2b]
 //   P1 : k, q (input type, [C][LK] each)                   [phase 0]
-//        -> QP at 0, KM at PB (fp32 [C][LG] each)          [0 - 2a]
+//        -> QP at 0, KE at PB (fp32 [C][LG] each)          [0 - 2a]
 //        -> Kbar^T (Op [DK][LB]) at 0, V^T (Op [DV][LB]) at KT   [2b - 3]
-//   X  : block totals (phase 0), then A and X fp32 [C][LA]  [1 - 2b]
+//   X  : (phase 0: diagonal A tiles where A goes; M's diagonal tiles and
+//        the block totals where X goes), then A and X fp32 [C][LA]  [1 - 2b]
 //        -> Tm (Op [C][LB]) where A was                     [2b - 3]
 //   BLK: fp32 [kNBlk][DK] per-channel factors                [0 - 2b]
-// Phases: 0 stage inputs, block scans, exponentials, factors; 1 Gram tiles
-// (A -> LDS, scale M -> record); 2a wave 0 inverts the diagonal blocks of
-// I + A while waves 1-7 write Qbar, Khat, e^{Gamma_C} to the record;
-// 2b Kbar^T and V^T staged, off-diagonal blocks of the inverse, Tm;
-// 3 W = Tm Kbar, Ut = Tm V to the record.
+// Phases: 0 stage inputs, block scans, exponentials, factors (kUnb: and the
+// diagonal tiles by position pairs); 1 Gram tiles (A -> LDS, scale M ->
+// record); 2a wave 0 inverts the diagonal blocks of I + A while waves 1-7
+// write Qbar, Khat, e^{Gamma_C} to the record; 2b Kbar^T and V^T staged,
+// off-diagonal blocks of the inverse, Tm; 3 W = Tm Kbar, Ut = Tm V to the
+// record.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct IntraLds {
   using Op = typename Policy<TIn>::Op;
   static constexpr int PI = 16 / sizeof(TIn), PO = 16 / sizeof(Op);
-  static constexpr int LG = DK + 4;     // fp32 rows (G, KP, QP, KM)
+  static constexpr int LG = DK + 4;     // fp32 rows (G, KP, QP, KE)
   static constexpr int LK = DK + PI;    // k / q rows (input type)
   static constexpr int LB = kC + PO;    // channel-major Op rows (Kbar^T, V^T) and Tm rows
   static constexpr int LA = kC + 4;     // A / X rows (fp32)
@@ -285,7 +291,7 @@ struct IntraLds {
   static constexpr size_t RED = BETA + kC * 4;
   static constexpr size_t BYTES = RED + 16 * 4;
   static_assert((size_t)kC * LB * sizeof(Op) <= (size_t)kC * LA * 4, "Tm fits where A was");
-  static_assert(4 * (size_t)DK * 4 <= (size_t)kC * LA * 4, "block totals fit in A");
+  static_assert(4 * 256 * 4 + 4 * (size_t)DK * 4 <= (size_t)kC * LA * 4, "M diagonal tiles and totals fit in X");
 };
 
 // The 10 tiles (a, b) of the lower 4x4 block triangle: diagonal first.
@@ -305,7 +311,7 @@ __constant__ signed char kWaveTile[8][2] = {{0, -1}, {1, -1}, {2, -1}, {3, -1}, 
 // at four points of the later phases, with kLoadK | kLoadBeta, kLoadQ,
 // kLoadG, kLoadV in turn (as std::integral_constant), e.g. to load the next
 // chunk's inputs into `in` in portions while this one is computed.
-template <typename TIn, int DK, int DV, typename AfterStage, typename Prefetch>
+template <typename TIn, int DK, int DV, bool kUnb, typename AfterStage, typename Prefetch>
 __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& in, const float* __restrict__ gcum,
                                               float scale, int b, int h, int T_len, int H, int ch,
                                               char* __restrict__ rec, AfterStage after_stage, Prefetch prefetch) {
@@ -323,12 +329,13 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   TIn* sK = reinterpret_cast<TIn*>(smem + L::P1);         // phase 0
   TIn* sQ = reinterpret_cast<TIn*>(smem + L::P1 + L::KIN);
   float* sQP = reinterpret_cast<float*>(smem + L::P1);
-  float* sKM = reinterpret_cast<float*>(smem + L::P1 + L::PB);
+  float* sKE = reinterpret_cast<float*>(smem + L::P1 + L::PB);
   Op* sKbt = reinterpret_cast<Op*>(smem + L::P1);          // phases 2b-3
   Op* sVt = reinterpret_cast<Op*>(smem + L::P1 + L::KT);
   float* sA = reinterpret_cast<float*>(smem + L::X);
   float* sX = sA + kC * L::LA;
-  float* sTot = sA;                                       // [4][DK], phase 0
+  float* sMd = sX;                                        // [4][16][16], phase 0-1
+  float* sTot = sX + 4 * 256;                             // [4][DK], phase 0
   Op* sTm = reinterpret_cast<Op*>(smem + L::X);           // phases 2b-3
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sBlk = reinterpret_cast<float*>(smem + L::BLK);
@@ -371,7 +378,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   // sums in row order, or differences of the given cumulative sums), the two
   // exponentials and the products with its k and q.
   const bool scan = tid < 4 * DK;   // wave-uniform (4 DK is a multiple of 64)
-  float kp[16], qp[16], km[16];
+  float kp[16], qp[16], ke[16];
   if (scan) {
     const int c = tid % DK, a = tid / DK;
     float x[16];
@@ -385,25 +392,59 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       for (int i = 0; i < 16; ++i) x[i] = sG[(16 * a + i) * L::LG + c];
 #pragma unroll
       for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
-      sTot[a * DK + c] = x[15];
     }
+    sTot[a * DK + c] = x[15];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      if (kUnb) sG[(16 * a + i) * L::LG + c] = x[i] * kLog2e;   // for the position pairs
       const float kv = to_f32(sK[(16 * a + i) * L::LK + c]), qv = to_f32(sQ[(16 * a + i) * L::LK + c]);
-      const float ep = exp2_fast(x[i] * kLog2e), em = exp2_fast(-x[i] * kLog2e);
+      const float ep = exp2_fast(x[i] * kLog2e), ee = exp2_fast((x[15] - x[i]) * kLog2e);
       kp[i] = kv * ep;
       qp[i] = qv * ep;
-      km[i] = kv * em;
+      ke[i] = kv * ee;
     }
   }
-  __syncthreads();   // staged k, q, g read; block totals written
+  __syncthreads();   // staged g read (kUnb: G written); block totals written
+  if (kUnb) {
+    // Diagonal tiles by position pairs, fp32: entry (i, j), j <= i, of tile
+    // a is sum_c y_rc k_sc e^{G_rc - G_sc} (r = 16a + i, s = 16a + j, y = k
+    // for A, q for M; the factor is <= 1 since G decreases along a block).
+    // Wave w takes tile w / 2 and 8 of its rows, paired (i, 15 - i) so that
+    // both waves of a tile have the same number of entries.  A goes where
+    // A will be, scale M to the diagonal-tile area in X.
+    const int a = w >> 1;
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int e = lane + 64 * e2, slot = e >> 4, j = e & 15;
+      const int pr = (w & 1) * 4 + (slot >> 1);
+      const int i = (slot & 1) ? 15 - pr : pr;
+      const int r = 16 * a + i, sc = 16 * a + j;
+      float accA = 0.f, accM = 0.f;
+      if (j <= i) {
+        for (int c = 0; c < DK; c += 4) {
+          const f32x4 ex = exp2v(*reinterpret_cast<const f32x4*>(sG + r * L::LG + c) -
+                                 *reinterpret_cast<const f32x4*>(sG + sc * L::LG + c));
+          const f32x4 ks = widen4(load4(sK + sc * L::LK + c)) * ex;
+          const f32x4 kr = widen4(load4(sK + r * L::LK + c)), qr = widen4(load4(sQ + r * L::LK + c));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            accA = fmaf(kr[u], ks[u], accA);
+            accM = fmaf(qr[u], ks[u], accM);
+          }
+        }
+      }
+      sA[r * L::LA + sc] = j < i ? sBeta[r] * accA : 0.f;
+      sMd[a * 256 + i * 16 + j] = j <= i ? accM * scale : 0.f;
+    }
+    __syncthreads();   // G, staged k and q read
+  }
   if (scan) {
     const int c = tid % DK, a = tid / DK;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       sKP[(16 * a + i) * L::LG + c] = kp[i];
       sQP[(16 * a + i) * L::LG + c] = qp[i];
-      sKM[(16 * a + i) * L::LG + c] = km[i];
+      sKE[(16 * a + i) * L::LG + c] = ke[i];
     }
     // factors from the block starts, summed in fp64 (natural log units):
     // thread group a builds one kind of row
@@ -425,13 +466,16 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       for (int j = 0; j < 4; ++j) sBlk[(kBlkF + j) * DK + c] = exp2_split(bs[j] * l2e);
     } else if (a == 1) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sBlk[(kBlkE + j) * DK + c] = exp2_split((bs[4] - bs[j]) * l2e + 64.0);
+      for (int j = 0; j < 4; ++j) sBlk[(kBlkE + j) * DK + c] = exp2_split((bs[4] - bs[j + 1]) * l2e);
     } else if (a == 2) {
       const int ta[6] = {1, 2, 3, 2, 3, 3}, tb[6] = {0, 0, 0, 1, 1, 2};
 #pragma unroll
-      for (int j = 0; j < 6; ++j) sBlk[(kBlkD + j) * DK + c] = exp2_split((bs[ta[j]] - bs[tb[j]]) * l2e);
+      for (int j = 0; j < 6; ++j) sBlk[(kBlkD + j) * DK + c] = exp2_split((bs[ta[j]] - bs[tb[j] + 1]) * l2e);
     } else {
       sBlk[kBlkDec * DK + c] = exp2_split(bs[4] * l2e);
+      // e^{-T_a} from the same fp32 totals as KE's exponents
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sBlk[(kBlkM + j) * DK + c] = exp2_split(-(double)sTot[j * DK + c] * l2e);
     }
   }
   __syncthreads();
@@ -442,13 +486,18 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   {
     const int t0i = kWaveTile[w][0], t1i = kWaveTile[w][1];
     const int ntile = t0i < 0 ? 0 : (t1i < 0 ? 1 : 2);   // wave-uniform
-    if (ntile > 0) {
+    if (kUnb && t0i >= 0 && t0i < 4) {
+      // diagonal tile from the position pairs of phase 0: scale M to the record
+      // (lane holds M[16a + l16][16a + g4 + i]); A is already in place
+      const float* md = sMd + t0i * 256 + l16 * 16 + g4;
+      store4<Op>(rM + tile_cr(t0i, t0i) * 256 + 4 * lane, narrow4<Op>(f32x4{md[0], md[1], md[2], md[3]}));
+    } else if (ntile > 0) {
       // both tiles of a wave share the row block a, hence the row operand
       const int a = kTileA[t0i];
       const int bb0 = kTileB[t0i], bb1 = ntile > 1 ? kTileB[t1i] : bb0;
       const bool diag = a == bb0;   // only single-tile waves hold a diagonal tile
       const int r = 16 * a + l16, s0 = 16 * bb0 + l16, s1 = 16 * bb1 + l16;
-      const float* d0p = sBlk + (kBlkD + (diag ? 0 : t0i - 4)) * DK;
+      const float* d0p = sBlk + (diag ? kBlkM + a : kBlkD + t0i - 4) * DK;
       const float* d1p = sBlk + (kBlkD + (ntile > 1 ? t1i - 4 : 0)) * DK;
       f32x4 accA0 = zero4(), accM0 = zero4(), accA1 = zero4(), accM1 = zero4();
 #pragma unroll
@@ -457,7 +506,8 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
         auto ld = [&](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
         const Slab<Gm> RK = make_slab<Gm>(ld(sKP + r * L::LG + c0), ld(sKP + r * L::LG + c1));
         const f32x4 rq0 = ld(sQP + r * L::LG + c0), rq1 = ld(sQP + r * L::LG + c1);
-        f32x4 ck0 = ld(sKM + s0 * L::LG + c0), ck1 = ld(sKM + s0 * L::LG + c1);
+        // column operand: KE times e^{-T_a} (diagonal) or e^{Gamma_p(a) - Gamma_p(b+1)}
+        const f32x4 ck0 = ld(sKE + s0 * L::LG + c0) * ld(d0p + c0), ck1 = ld(sKE + s0 * L::LG + c1) * ld(d0p + c1);
         if (P::kMixed && diag) {
           Slab<Gm> CKh, CKl, RQh, RQl;
           make_slab_split<Gm>(ck0, ck1, CKh, CKl);
@@ -467,17 +517,13 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
           accM0 = mma(CKl, RQh, accM0);
           accM0 = mma(CKh, RQl, accM0);
         } else {
-          if (!diag) {
-            ck0 = ck0 * ld(d0p + c0);
-            ck1 = ck1 * ld(d0p + c1);
-          }
           const Slab<Gm> RQ = make_slab<Gm>(rq0, rq1);
           const Slab<Gm> CK = make_slab<Gm>(ck0, ck1);
           accA0 = mma(CK, RK, accA0);   // A^T tile: lane holds A[r][16bb + g4 + i]
           accM0 = mma(CK, RQ, accM0);   // M^T tile: lane holds M[r][16bb + g4 + i]
           if (ntile > 1) {
-            const Slab<Gm> CK1 = make_slab<Gm>(ld(sKM + s1 * L::LG + c0) * ld(d1p + c0),
-                                               ld(sKM + s1 * L::LG + c1) * ld(d1p + c1));
+            const Slab<Gm> CK1 = make_slab<Gm>(ld(sKE + s1 * L::LG + c0) * ld(d1p + c0),
+                                               ld(sKE + s1 * L::LG + c1) * ld(d1p + c1));
             accA1 = mma(CK1, RK, accA1);
             accM1 = mma(CK1, RQ, accM1);
           }
@@ -550,7 +596,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
         const float e = sBlk[(kBlkE + st) * DK + col];
         f32x4 val;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) val[i] = (sKM[(row0 + i) * L::LG + col] * e) * kTwoM64;
+        for (int i = 0; i < 4; ++i) val[i] = sKE[(row0 + i) * L::LG + col] * e;
         store4<Op>(rK + tile_k<DK / 16>(st, ct) * 256 + 4 * lane, narrow4<Op>(val));
       }
     }
@@ -645,8 +691,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
 }
 
 // Two-stage schedule, stage 1: one work-group per (b*h, chunk), records for
-// every chunk of every head in the workspace.
-template <typename TIn, int DK, int DV>
+// every chunk of every head in the workspace.  kUnb: decay not bounded below
+// (diagonal tiles by position pairs).
+template <typename TIn, int DK, int DV, bool kUnb>
 __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                                const TIn* __restrict__ v, const TIn* __restrict__ g,
                                                                const float* __restrict__ gcum,
@@ -656,9 +703,9 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __rest
   const int ch = blockIdx.x % nchunks, bh = blockIdx.x / nchunks;
   InRegs<TIn, DK, DV> in;
   load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, ch);
-  produce_chunk<TIn, DK, DV>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, ch,
-                             ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [] { return true; },
-                             [](auto) {});
+  produce_chunk<TIn, DK, DV, kUnb>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, ch,
+                                   ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [] { return true; },
+                                   [](auto) {});
 }
 
 // ---------------------------------------------------------------------------
@@ -1071,7 +1118,7 @@ struct FusedLds {
   static constexpr size_t BYTES = (A > B ? A : B) + 16;
 };
 
-template <typename TIn, int DK, int DV>
+template <typename TIn, int DK, int DV, bool kUnb>
 __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                              const TIn* __restrict__ v, const TIn* __restrict__ g,
                                                              const float* __restrict__ gcum,
@@ -1168,7 +1215,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
                                                          nxt / nloc);
       }
     };
-    if (!produce_chunk<TIn, DK, DV>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
+    if (!produce_chunk<TIn, DK, DV, kUnb>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
                                     ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage, prefetch))
       return;
     pending = it;
@@ -1214,7 +1261,7 @@ static size_t fused_ws_bytes(int nbh) {
 template <typename TIn, int DK, int DV>
 static hipError_t go_fused(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                            const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                           int H, void* ws, size_t ws_bytes, hipStream_t st) {
+                           int H, void* ws, size_t ws_bytes, bool unb, hipStream_t st) {
   const int nchunks = (T_len + kC - 1) / kC;
   const int nbh = B * H;
   int dev = 0, cus = 0;
@@ -1236,9 +1283,10 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
     const int nh = nbh - head0 < batch ? nbh - head0 : batch;
     const int nctrl = 16 + nh * kRingSlots + 2 * NS * nh;
     hipLaunchKernelGGL(clear_ints_kernel, dim3((nctrl + 255) / 256), dim3(256), 0, st, ctrl, nctrl);
-    hipLaunchKernelGGL((fused_fwd_kernel<TIn, DK, DV>), dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q,
-                       (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len,
-                       H, nchunks, head0, nh, ring, ctrl, kRingSlots);
+    auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true> : fused_fwd_kernel<TIn, DK, DV, false>;
+    hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q, (const TIn*)k, (const TIn*)v,
+                       (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len, H, nchunks, head0, nh, ring,
+                       ctrl, kRingSlots);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1248,13 +1296,13 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
 template <typename TIn, int DK, int DV>
 static hipError_t go_stages(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                             const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                            int H, void* ws, int stages, hipStream_t st) {
+                            int H, void* ws, int stages, bool unb, hipStream_t st) {
   const int nchunks = (T_len + kC - 1) / kC;
   const unsigned nbh = (unsigned)B * (unsigned)H;
   if (stages & 1) {
-    hipLaunchKernelGGL((intra_chunk_kernel<TIn, DK, DV>), dim3(nchunks * nbh), dim3(kThreads), 0, st, (const TIn*)q,
-                       (const TIn*)k, (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, (char*)ws,
-                       T_len, H, nchunks);
+    auto kern = unb ? intra_chunk_kernel<TIn, DK, DV, true> : intra_chunk_kernel<TIn, DK, DV, false>;
+    hipLaunchKernelGGL(kern, dim3(nchunks * nbh), dim3(kThreads), 0, st, (const TIn*)q, (const TIn*)k,
+                       (const TIn*)v, (const TIn*)g, gcum, (const TIn*)beta, scale, (char*)ws, T_len, H, nchunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1294,28 +1342,34 @@ size_t fwd_fused_workspace_bytes(int is_bf16, int nbh, int dk, int dv) {
 template <typename TIn>
 static hipError_t fused_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                           const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                          int H, int dk, int dv, void* ws, size_t wsb, hipStream_t st) {
-  KDA_DISPATCH_D(go_fused, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, wsb, st);
+                          int H, int dk, int dv, void* ws, size_t wsb, bool unb, hipStream_t st) {
+  KDA_DISPATCH_D(go_fused, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, wsb, unb, st);
 }
 template <typename TIn>
 static hipError_t stages_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                            const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                           int H, int dk, int dv, void* ws, int stages, hipStream_t st) {
-  KDA_DISPATCH_D(go_stages, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, st);
+                           int H, int dk, int dv, void* ws, int stages, bool unb, hipStream_t st) {
+  KDA_DISPATCH_D(go_stages, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, unb, st);
 }
 
 hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
-                            int B, int T_len, int H, int dk, int dv, void* ws, size_t ws_bytes, hipStream_t st) {
-  if (is_bf16) return fused_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, st);
-  return fused_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, st);
+                            int B, int T_len, int H, int dk, int dv, void* ws, size_t ws_bytes, int unbounded,
+                            hipStream_t st) {
+  const bool u = unbounded != 0;
+  if (is_bf16)
+    return fused_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, st);
+  return fused_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, st);
 }
 
 hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                              const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
-                             int B, int T_len, int H, int dk, int dv, void* ws, int stages, hipStream_t st) {
-  if (is_bf16) return stages_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, st);
-  return stages_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, st);
+                             int B, int T_len, int H, int dk, int dv, void* ws, int stages, int unbounded,
+                             hipStream_t st) {
+  const bool u = unbounded != 0;
+  if (is_bf16)
+    return stages_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, u, st);
+  return stages_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, u, st);
 }
 
 }  // namespace kda

@@ -7,9 +7,10 @@
 
 namespace kda {
 
-// Decay preparation: gate (z != nullptr) and/or chunk-local cumsum.
+// Decay preparation: gate (z != nullptr; softplus != 0 selects the unbounded
+// -Softplus gate instead of gmin * Sigmoid) and/or chunk-local cumsum.
 hipError_t launch_prepare_decay(int is_bf16, const void* z, const float* A, float gmin, void* g,
-                                float* gcum, int B, int T, int H, int dk, int chunk,
+                                float* gcum, int B, int T, int H, int dk, int chunk, int softplus,
                                 hipStream_t stream);
 
 // Bytes of one per-chunk record of the prefill workspace.
@@ -18,15 +19,17 @@ size_t fwd_record_bytes(int is_bf16, int dk, int dv);
 size_t fwd_fused_workspace_bytes(int is_bf16, int nbh, int dk, int dv);
 
 // Chunked prefill, fused schedule (one persistent kernel per batch of heads).
+// unbounded != 0: the decay may go below -5 (diagonal tiles by position pairs).
 hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
                             int B, int T, int H, int dk, int dv, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream);
+                            int unbounded, hipStream_t stream);
 
 // Chunked prefill, two-stage schedule: bit 0 intra-chunk kernel, bit 1 state pass.
 hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                              const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
-                             int B, int T, int H, int dk, int dv, void* workspace, int stages, hipStream_t stream);
+                             int B, int T, int H, int dk, int dv, void* workspace, int stages, int unbounded,
+                             hipStream_t stream);
 
 // One decode token per (b, h), state updated in place.
 hipError_t launch_decode_step(int is_bf16, const void* q, const void* k, const void* v,

@@ -18,6 +18,7 @@ PKG = Path(__file__).resolve().parent
 LIB_PATH = PKG / "libkda.so"
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_STAGES_UNBOUNDED = 4
 CHUNK = 64
 GMIN = -5.0
 
@@ -44,12 +45,16 @@ def lib() -> ctypes.CDLL:
         L.kda_status_str.argtypes = [I]
         L.kda_prepare_decay.restype = I
         L.kda_prepare_decay.argtypes = [P, P, F, P, P, I, I, I, I, I, I, P]
+        L.kda_prepare_decay_softplus.restype = I
+        L.kda_prepare_decay_softplus.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         L.kda_fwd_workspace_bytes.restype = S
         L.kda_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kda_fwd_stages_workspace_bytes.restype = S
         L.kda_fwd_stages_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kda_fwd_chunked.restype = I
         L.kda_fwd_chunked.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, P]
+        L.kda_fwd_chunked_unbounded.restype = I
+        L.kda_fwd_chunked_unbounded.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, P]
         L.kda_fwd_chunked_stages.restype = I
         L.kda_fwd_chunked_stages.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, I, P]
         L.kda_decode_step.restype = I
@@ -93,9 +98,11 @@ def _check(status: int, where: str):
         raise KDAError(status, where)
 
 
-def prepare_decay(z=None, A=None, g=None, *, want_g=True, want_gcum=True, gmin=GMIN, chunk=CHUNK):
+def prepare_decay(z=None, A=None, g=None, *, want_g=True, want_gcum=True, gmin=GMIN, chunk=CHUNK,
+                  softplus=False):
     """Gate mode: prepare_decay(z, A) -> (g, gcum); scan mode: prepare_decay(g=g) -> gcum.
-    z, g: [B, T, H, dk] (bf16 or fp32); A: [H] fp32."""
+    z, g: [B, T, H, dk] (bf16 or fp32); A: [H] fp32.  softplus=True: the
+    unbounded gate g = -Softplus(exp(A) z) (kda_prepare_decay_softplus)."""
     if z is not None:
         B, T, H, dk = z.shape
         dt = _dtype_code(z)
@@ -103,8 +110,12 @@ def prepare_decay(z=None, A=None, g=None, *, want_g=True, want_gcum=True, gmin=G
             raise ValueError("A must be fp32 [H]")
         g_out = torch.empty_like(z) if want_g else None
         gcum = torch.empty(z.shape, dtype=torch.float32, device=z.device) if want_gcum else None
-        _check(lib().kda_prepare_decay(_ptr(z), _ptr(A), gmin, _ptr(g_out), _ptr(gcum), dt, B, T, H, dk, chunk,
-                                       _stream(z.device)), "kda_prepare_decay")
+        if softplus:
+            _check(lib().kda_prepare_decay_softplus(_ptr(z), _ptr(A), _ptr(g_out), _ptr(gcum), dt, B, T, H, dk,
+                                                    chunk, _stream(z.device)), "kda_prepare_decay_softplus")
+        else:
+            _check(lib().kda_prepare_decay(_ptr(z), _ptr(A), gmin, _ptr(g_out), _ptr(gcum), dt, B, T, H, dk,
+                                           chunk, _stream(z.device)), "kda_prepare_decay")
         return g_out, gcum
     if g is None:
         raise ValueError("need z (gate mode) or g (scan mode)")
@@ -136,12 +147,14 @@ def workspace_error(workspace: torch.Tensor) -> int:
 
 
 def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state=True, ht=None,
-                workspace=None, out=None, chunk=CHUNK, stages=None):
+                workspace=None, out=None, chunk=CHUNK, stages=None, unbounded=False):
     """o, ht = fwd_chunked(q, k, v, g, beta, h0).  q,k,g [B,T,H,dk]; v [B,T,H,dv];
     beta [B,T,H] (bf16 or fp32); h0/ht [B,H,dk,dv] fp32; o [B,T,H,dv] fp32.
     ht may be h0 itself (in-place carry).  stages=None runs the fused
     single-pass schedule (kda_fwd_chunked); stages in {1, 2, 3} runs the
-    two-kernel schedule (kda_fwd_chunked_stages) with that stage mask."""
+    two-kernel schedule (kda_fwd_chunked_stages) with that stage mask.
+    unbounded=True: the log-decay has no lower bound (kda_fwd_chunked_unbounded,
+    or KDA_STAGES_UNBOUNDED added to the stage mask)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q)
@@ -164,9 +177,11 @@ def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state
             _ptr(ht if final_state else None), _ptr(o), dt, B, T, H, dk, dv, chunk, _ptr(workspace),
             workspace.numel())
     if stages is None:
-        _check(lib().kda_fwd_chunked(*args, _stream(q.device)), "kda_fwd_chunked")
+        fn = lib().kda_fwd_chunked_unbounded if unbounded else lib().kda_fwd_chunked
+        _check(fn(*args, _stream(q.device)), "kda_fwd_chunked_unbounded" if unbounded else "kda_fwd_chunked")
     else:
-        _check(lib().kda_fwd_chunked_stages(*args, int(stages), _stream(q.device)), "kda_fwd_chunked_stages")
+        mask = int(stages) | (KDA_STAGES_UNBOUNDED if unbounded else 0)
+        _check(lib().kda_fwd_chunked_stages(*args, mask, _stream(q.device)), "kda_fwd_chunked_stages")
     return o, (ht if final_state else None)
 
 

@@ -90,6 +90,17 @@ const char* kda_status_str(int status);
 int kda_prepare_decay(const void* z, const float* A, float gmin, void* g, float* gcum,
                       int dtype, int B, int T, int H, int dk, int chunk, void* stream);
 
+/*
+ * Decay preparation with the predecessor's unbounded gate ("Key claims",
+ * section 2.1.1: Kimi Linear's negative Softplus log-decay, which K3
+ * replaces with the bounded one): g[b,t,h,c] = -Softplus(exp(A[h]) *
+ * z[b,t,h,c]), Softplus(x) = log(1 + e^x), in fp32, rounded (RNE) to dtype;
+ * g has no lower bound.  Outputs, layout and errors as kda_prepare_decay in
+ * gate mode (z and A required).  For kda_fwd_chunked_unbounded.
+ */
+int kda_prepare_decay_softplus(const void* z, const float* A, void* g, float* gcum, int dtype,
+                               int B, int T, int H, int dk, int chunk, void* stream);
+
 /* Bytes of device workspace kda_fwd_chunked needs for these sizes (0 if
  * the sizes are invalid or unsupported): ring buffers of a few chunk
  * records per head for at most one launch's batch of heads plus control
@@ -127,6 +138,22 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g,
                     int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_fwd_chunked for a log-decay with no lower bound (g <= 0, e.g. from
+ * kda_prepare_decay_softplus): the comparison point of "Key claims",
+ * section 2.1.1 / Fig. 3, where an unbounded decay rules out the rescaled
+ * dense diagonal tiles.  The diagonal 16x16 tiles of the two intra-chunk
+ * Gram matrices are then sums over position pairs in fp32 (each pair's
+ * decay factor formed directly, never above 1); everything else is
+ * unchanged.  Arguments, layouts, workspace, errors as kda_fwd_chunked;
+ * precondition, not checked: g <= 0 and finite.
+ */
+int kda_fwd_chunked_unbounded(const void* q, const void* k, const void* v, const void* g,
+                              const float* gcum, const void* beta, float scale, const float* h0,
+                              float* ht, float* o, int dtype, int B, int T, int H, int dk,
+                              int dv, int chunk, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * The same computation as kda_fwd_chunked on a two-kernel schedule with
  * every chunk record stored in the workspace (>= kda_fwd_stages_workspace_bytes):
  * bit 0 of `stages` = the intra-chunk kernel (reads q, k, v, g/gcum, beta;
@@ -136,8 +163,12 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g,
  * waits; for profiling each stage and for callers that schedule the stages
  * themselves.  Same results as kda_fwd_chunked up to nothing: both
  * schedules run the same per-chunk arithmetic.
- * Errors: as kda_fwd_chunked, plus KDA_ERR_SHAPE for stages outside 1..3.
+ * Adding KDA_STAGES_UNBOUNDED to `stages` runs the unbounded-decay
+ * intra-chunk kernel of kda_fwd_chunked_unbounded.
+ * Errors: as kda_fwd_chunked, plus KDA_ERR_SHAPE for stages outside 1..3
+ * (with or without KDA_STAGES_UNBOUNDED).
  */
+#define KDA_STAGES_UNBOUNDED 4
 int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const void* g,
                            const float* gcum, const void* beta, float scale, const float* h0,
                            float* ht, float* o, int dtype, int B, int T, int H, int dk, int dv,

@@ -98,3 +98,24 @@ def test_prepare_decay_validation():
     assert L.kda_prepare_decay(None, None, -5.0, FAKE, None, 1, 1, 64, 1, 128, 64, None) == 1
     assert L.kda_prepare_decay(None, None, -5.0, FAKE, FAKE, 1, 1, 64, 1, 128, 16, None) == 5
     assert L.kda_prepare_decay(None, None, -5.0, FAKE, FAKE, 1, 0, 64, 1, 128, 64, None) == 2
+
+
+def test_unbounded_entry_points_validate_like_the_bounded_ones():
+    L = kda.lib()
+    a = [FAKE, FAKE, FAKE, FAKE, None, FAKE, 0.1, None, None, FAKE, 1, 1, 64, 1, 128, 128, 64, FAKE, 1 << 40, None]
+    for i, code in ((0, 1), (5, 1), (9, 1)):
+        bad = list(a); bad[i] = None
+        assert L.kda_fwd_chunked_unbounded(*bad) == code
+    bad = list(a); bad[14] = 96
+    assert L.kda_fwd_chunked_unbounded(*bad) == 5
+    bad = list(a); bad[18] = 1024
+    assert L.kda_fwd_chunked_unbounded(*bad) == 6
+    # stage mask: the unbounded bit needs at least one stage; other bits are rejected
+    st = a[:19] + [kda.KDA_STAGES_UNBOUNDED, None]
+    assert L.kda_fwd_chunked_stages(*st) == 2
+    st = a[:19] + [8 | 1, None]
+    assert L.kda_fwd_chunked_stages(*st) == 2
+    # softplus gate: z and A are required
+    assert L.kda_prepare_decay_softplus(None, FAKE, FAKE, FAKE, 1, 1, 64, 1, 128, 64, None) == 1
+    assert L.kda_prepare_decay_softplus(FAKE, None, FAKE, FAKE, 1, 1, 64, 1, 128, 64, None) == 1
+    assert L.kda_prepare_decay_softplus(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 1, 96, 64, None) == 5

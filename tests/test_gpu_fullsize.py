@@ -93,6 +93,36 @@ def test_config2_b1_h32_t65536_sampled_heads():
     assert eo <= TOLB and eh <= TOLB
 
 
+@pytest.mark.gpu
+@pytest.mark.timeout(300)
+def test_config2_unbounded_kernel_softplus_decay_sampled_heads():
+    """The benchmark workload through kda_fwd_chunked_unbounded with the
+    unbounded gate g = -Softplus(exp(A) z) of the same z and A (the
+    ablation's second run): all outputs and the final state of two heads."""
+    B, H, T, D = 1, 32, 65536, 128
+    heads = [3, 28]
+    say(f"unbounded kernel B={B} H={H} T={T}, heads {heads}")
+    d = synth.make_inputs(B, T, H, D, D, seed=22)
+    dev = torch.device("cuda:0")
+    q, k, v, beta, z = (_bf(d[n]).to(dev) for n in ("q", "k", "v", "beta", "z"))
+    A = torch.from_numpy(d["A"].copy()).to(dev)
+    h0 = torch.from_numpy(d["h0"]).to(dev)
+    g, _ = kda.prepare_decay(z, A, want_gcum=False, softplus=True)
+    ws = kda.alloc_workspace(B, T, H, D, D, BF, dev)
+    o, ht = kda.fwd_chunked(q, k, v, g, beta, h0, workspace=ws, unbounded=True)
+    torch.cuda.synchronize()
+    assert kda.workspace_error(ws) == 0
+    sel = lambda x: f32(x[:, :, heads].cpu())
+    gs = sel(g)
+    g_ref = f32(_bf(ogate.gate_softplus(f32(_bf(d["z"][:, :, heads])), d["A"][heads])))
+    assert np.array_equal(np.abs(gs - g_ref) <= np.abs(g_ref) * 2.0 ** -7 + 1e-30, np.ones_like(gs, bool))
+    o_ref, h_ref = seq.kda_seq(sel(q), sel(k), sel(v), gs, sel(beta), d["h0"][:, heads])
+    eo = err_ratio(f32(o[:, :, heads]), o_ref)
+    eh = err_ratio(ht[:, heads].cpu().numpy(), h_ref)
+    say(f"unbounded B1 H32 T64K: min g {gs.min():.1f}, o err/rms {eo:.3e}, state err/rms {eh:.3e}")
+    assert eo <= TOLB and eh <= TOLB
+
+
 def _device_draw(shape_k, shape_v, shape_b, gen, dev):
     """Stand-in inputs for the heads the oracle does not check (same
     distributions, drawn on the device)."""
