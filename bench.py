@@ -89,6 +89,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards by "
@@ -219,6 +220,63 @@ def main():
             + (f"; parity {ab_parity['max_err_over_rms']:.2e}" if ab_parity else ""))
         del o_a, ht_a, g_sp
 
+    # ---------------- variable-length packed batch with prefix-state snapshots:
+    # the same 65536 tokens and 32 heads as 11 sequences of a geometric length
+    # mix, a state snapshot every 64 chunks (4096 tokens)
+    varlen = None
+    if not args.no_varlen:
+        lengths = [32768, 16384, 8192, 4096, 2048, 1024, 512, 256, 128, 64, 64]
+        cu = [0]
+        for L_ in lengths:
+            cu.append(cu[-1] + L_)
+        assert cu[-1] == T
+        every = 64
+        h0v = torch.zeros((len(lengths), H, DK, DV), dtype=torch.float32, device=dev)
+        o_v = torch.empty_like(o)
+        res = {}
+
+        def run_varlen():
+            res["o"], res["ht"], res["snaps"] = kda.fwd_chunked_varlen(q, k, v, g, beta, cu, h0v, snap_every=every,
+                                                                       workspace=ws, out=o_v)
+
+        run_varlen()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_k):
+            run_varlen()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_v = e0.elapsed_time(e1) / n_k
+        v_parity = None
+        if not args.no_cpu_baseline:
+            from oracle import seq
+
+            heads, si = [0, 17], 2          # the 8192-token sequence: its output and its snapshot at 4096
+            a_, b_ = cu[si], cu[si + 1]
+            f = lambda t: t.float().cpu().numpy()
+            sel = lambda t, hi=None: f(t[:, a_:(b_ if hi is None else a_ + hi)][:, :, heads])
+            o_ref, _ = seq.kda_seq(sel(q), sel(k), sel(v), sel(g), sel(beta), None, nthreads=seq.threads_default())
+            _, s_ref = seq.kda_seq(sel(q, 4096), sel(k, 4096), sel(v, 4096), sel(g, 4096), sel(beta, 4096), None,
+                                   nthreads=seq.threads_default())
+            sidx = sum((((L_ + 63) // 64) - 1) // every for L_ in lengths[:si])
+            o_gpu = res["o"][:, a_:b_][:, :, heads].cpu().double().numpy()
+            s_gpu = res["snaps"][sidx][heads].cpu().double().numpy()[None]
+            rms = lambda x: math.sqrt(float(np.mean(x * x)))
+            v_parity = {"sample": f"sequence {si} ({lengths[si]} tokens), heads {heads}: output and the snapshot "
+                                  f"after 4096 tokens vs fp64 oracle",
+                        "max_err_over_rms_o": float(np.max(np.abs(o_gpu - o_ref)) / rms(o_ref)),
+                        "max_err_over_rms_snapshot": float(np.max(np.abs(s_gpu - s_ref)) / rms(s_ref)),
+                        "tolerance": 2e-2}
+        varlen = {"workload": f"{len(lengths)} packed sequences of {lengths} tokens (sum {T}), H={H}, "
+                              f"dk=dv={DK}, zero initial states, a state snapshot every {every} chunks",
+                  "ms_per_call": round(ms_v, 4), "tokens_per_s": round(T / (ms_v * 1e-3), 1),
+                  "snapshots": int(res["snaps"].shape[0]) if res["snaps"] is not None else 0,
+                  "single_sequence_ms": round(ms_step, 4), "parity": v_parity}
+        log(f"varlen: {ms_v:.3f} ms per call ({varlen['snapshots']} snapshots)"
+            + (f"; parity o {v_parity['max_err_over_rms_o']:.2e}, snapshot "
+               f"{v_parity['max_err_over_rms_snapshot']:.2e}" if v_parity else ""))
+        del o_v, h0v, res
+
     tok_s = B * T / (ms_step * 1e-3)
     gbs = abytes / (ms_step * 1e-3) / 1e9
     tflops = flop / (ms_step * 1e-3) / 1e12
@@ -315,6 +373,7 @@ def main():
                                                "bitwise_equal_output": same}},
         "decode": decode,
         "unbounded_decay_ablation": ablation,
+        "varlen_snapshots": varlen,
         "parity": parity,
         "cpu_baseline": cpu,
     }

@@ -127,7 +127,8 @@ int fwd_fused_impl(const void* q, const void* k, const void* v, const void* g, c
   if (st != KDA_OK) return st;
   if (workspace_bytes < kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
   hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
-                                       workspace, workspace_bytes, unbounded, static_cast<hipStream_t>(stream));
+                                       workspace, workspace_bytes, unbounded, nullptr, 0,
+                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 }  // namespace
@@ -157,9 +158,69 @@ int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const vo
   if (st != KDA_OK) return st;
   if (workspace_bytes < kda_fwd_stages_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
   hipError_t e = kda::launch_fwd_stages(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
-                                        workspace, mask, (stages & KDA_STAGES_UNBOUNDED) ? 1 : 0,
+                                        workspace, mask, (stages & KDA_STAGES_UNBOUNDED) ? 1 : 0, nullptr, 0,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+long long kda_fwd_varlen_snapshots(const int* cu_seqlens, int N, int snap_every, int chunk) {
+  if (!cu_seqlens || N <= 0 || snap_every <= 0 || chunk != kChunk) return -1;
+  long long n = 0;
+  for (int i = 0; i < N; ++i) {
+    const long long len = (long long)cu_seqlens[i + 1] - cu_seqlens[i];
+    if (len < 0) return -1;
+    const long long nch = (len + kChunk - 1) / kChunk;   // snapshots at chunk ends before the last
+    n += nch > 0 ? (nch - 1) / snap_every : 0;
+  }
+  return n;
+}
+
+int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                           const void* beta, float scale, const int* cu_seqlens, int N, const float* h0, float* ht,
+                           float* o, float* snap, int snap_every, int dtype, int T, int H, int dk, int dv, int chunk,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, 1, T, H, dk, dv, chunk, workspace, 3);
+  if (st != KDA_OK) return st;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  if (N <= 0 || cu_seqlens[0] != 0 || cu_seqlens[N] != T || snap_every < 0) return KDA_ERR_SHAPE;
+  for (int i = 0; i < N; ++i)
+    if (cu_seqlens[i + 1] < cu_seqlens[i]) return KDA_ERR_SHAPE;
+  if ((long long)N * H > 2147483647LL / ((long long)dk * dv)) return KDA_ERR_SHAPE;
+  if (snap && snap_every > 0 && !aligned16(snap)) return KDA_ERR_ALIGN;
+  // the workspace sized for one sequence of T tokens serves every call below
+  if (workspace_bytes < kda_fwd_workspace_bytes(1, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const size_t esz = dtype == KDA_BF16 ? 2 : 4;
+  const size_t hk = (size_t)H * dk, hv = (size_t)H * dv, sd = (size_t)H * dk * dv;
+  const bool snaps = snap && snap_every > 0;
+  long long snap_off = 0;
+  for (int i = 0; i < N; ++i) {
+    const size_t t0 = (size_t)cu_seqlens[i];
+    const int len = cu_seqlens[i + 1] - cu_seqlens[i];
+    const float* h0_i = h0 ? h0 + i * sd : nullptr;
+    float* ht_i = ht ? ht + i * sd : nullptr;
+    hipError_t e = hipSuccess;
+    if (len == 0) {   // empty sequence: the final state is the initial one
+      if (ht_i && h0_i && ht_i != h0_i)
+        e = hipMemcpyAsync(ht_i, h0_i, sd * sizeof(float), hipMemcpyDeviceToDevice, hs);
+      else if (ht_i && !h0_i)
+        e = kda::launch_zero_words(ht_i, sd, hs);
+    } else {
+      auto at = [&](const void* p, size_t per_token) {
+        return p ? static_cast<const void*>(static_cast<const char*>(p) + t0 * per_token * esz) : nullptr;
+      };
+      e = kda::launch_fwd_fused(dtype == KDA_BF16, at(q, hk), at(k, hk), at(v, hv), at(g, hk),
+                                gcum ? gcum + t0 * hk : nullptr, at(beta, (size_t)H), scale, h0_i, ht_i,
+                                o + t0 * hv, 1, len, H, dk, dv, workspace, workspace_bytes, 0,
+                                snaps ? snap + (size_t)snap_off * sd : nullptr, snaps ? snap_every : 0, hs);
+      if (snaps) {
+        const long long nch = ((long long)len + kChunk - 1) / kChunk;
+        snap_off += (nch - 1) / snap_every;
+      }
+    }
+    if (e != hipSuccess) return KDA_ERR_HIP;
+  }
+  return KDA_OK;
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,

@@ -798,11 +798,21 @@ struct ConsumerLds {
   static_assert(SH % 16 == 0 && UPART % 16 == 0, "16-byte staging");
 };
 
+// Prefix-state snapshots: with p != nullptr and every > 0, the state after
+// chunk c (c + 1 a multiple of `every`, and not the sequence's end, which
+// is ht) is written to p + ((c + 1) / every - 1) * nbh * dk * dv + bh * dk * dv
+// ([snapshot][b * H + h][dk][dv], fp32).
+struct Snap {
+  float* p;
+  int every;
+  int nbh;
+};
+
 template <typename TIn, int DK, int DV, bool kRing>
 __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
                                               const float* __restrict__ h0, float* __restrict__ ht,
                                               float* __restrict__ o, int b, int h, int T_len, int H,
-                                              int nchunks) {
+                                              int nchunks, Snap snap) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using R = Rec<TIn, DK, DV>;
@@ -1058,6 +1068,16 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         for (int jj = 0; jj < NJ; ++jj) S[ct][jj] = S[ct][jj] * d + acc[jj] * ius;
       }
     }
+    if (snap.p && snap.every > 0 && (c + 1) % snap.every == 0 && (c + 1) * kC < T_len) {
+      float* sp = snap.p + ((size_t)((c + 1) / snap.every - 1) * snap.nbh + bh) * DK * DV;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sp[(size_t)(16 * ct + g4 + i) * DV + 16 * (jt0 + jj) + l16] = S[ct][jj][i];
+    }
     if (NBUF == 1) __syncthreads();   // Y_c
   }
 
@@ -1076,13 +1096,14 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __restrict__ ws,
                                                               const float* __restrict__ h0, float* __restrict__ ht,
-                                                              float* __restrict__ o, int T_len, int H, int nchunks) {
+                                                              float* __restrict__ o, int T_len, int H, int nchunks,
+                                                              Snap snap) {
   using CL = ConsumerLds<TIn, DK, DV>;
   __shared__ __align__(16) char smem[CL::BYTES];
   const int bh = blockIdx.x / CL::NS, vb = blockIdx.x % CL::NS;
   consume_chain<TIn, DK, DV, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
                                     Ring{nullptr, nullptr, nullptr, nullptr, 1}, vb, h0, ht, o, bh / H, bh % H,
-                                    T_len, H, nchunks);
+                                    T_len, H, nchunks, snap);
 }
 
 // ---------------------------------------------------------------------------
@@ -1126,7 +1147,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
                                                              const float* __restrict__ h0, float* __restrict__ ht,
                                                              float* __restrict__ o, int T_len, int H, int nchunks,
                                                              int head0, int nheads, char* __restrict__ ring,
-                                                             int* __restrict__ ctrl, int R) {
+                                                             int* __restrict__ ctrl, int R, Snap snap) {
   using Rc = Rec<TIn, DK, DV>;
   __shared__ __align__(16) char smem[FusedLds<TIn, DK, DV>::BYTES];
   int* sWord = reinterpret_cast<int*>(smem + FusedLds<TIn, DK, DV>::BYTES - 16);
@@ -1142,7 +1163,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     const int jh = xcd + 8 * (li / NS), vb = li % NS, bh = head0 + jh;
     consume_chain<TIn, DK, DV, true>(smem, ring + (size_t)jh * R * Rc::BYTES,
                                      Ring{ready + jh * R, done + jh * NS + vb, err, cxcc + jh * NS + vb, R}, vb, h0,
-                                     ht, o, bh / H, bh % H, T_len, H, nchunks);
+                                     ht, o, bh / H, bh % H, T_len, H, nchunks, snap);
     return;
   }
 
@@ -1227,7 +1248,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   }
 }
 
-__global__ void clear_ints_kernel(int* p, int n) {
+__global__ void clear_ints_kernel(int* p, int n) {   // also zero-fills fp32 buffers
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
@@ -1261,7 +1282,7 @@ static size_t fused_ws_bytes(int nbh) {
 template <typename TIn, int DK, int DV>
 static hipError_t go_fused(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                            const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                           int H, void* ws, size_t ws_bytes, bool unb, hipStream_t st) {
+                           int H, void* ws, size_t ws_bytes, bool unb, float* snap, int snap_every, hipStream_t st) {
   const int nchunks = (T_len + kC - 1) / kC;
   const int nbh = B * H;
   int dev = 0, cus = 0;
@@ -1286,7 +1307,7 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
     auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true> : fused_fwd_kernel<TIn, DK, DV, false>;
     hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q, (const TIn*)k, (const TIn*)v,
                        (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len, H, nchunks, head0, nh, ring,
-                       ctrl, kRingSlots);
+                       ctrl, kRingSlots, Snap{snap, snap_every, nbh});
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1296,7 +1317,7 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
 template <typename TIn, int DK, int DV>
 static hipError_t go_stages(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                             const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                            int H, void* ws, int stages, bool unb, hipStream_t st) {
+                            int H, void* ws, int stages, bool unb, float* snap, int snap_every, hipStream_t st) {
   const int nchunks = (T_len + kC - 1) / kC;
   const unsigned nbh = (unsigned)B * (unsigned)H;
   if (stages & 1) {
@@ -1308,7 +1329,7 @@ static hipError_t go_stages(const void* q, const void* k, const void* v, const v
   }
   if (stages & 2) {
     hipLaunchKernelGGL((state_pass_kernel<TIn, DK, DV>), dim3(ConsumerLds<TIn, DK, DV>::NS * nbh), dim3(kThreads), 0, st,
-                       (const char*)ws, h0, ht, o, T_len, H, nchunks);
+                       (const char*)ws, h0, ht, o, T_len, H, nchunks, Snap{snap, snap_every, (int)nbh});
     return hipGetLastError();
   }
   return hipSuccess;
@@ -1342,34 +1363,52 @@ size_t fwd_fused_workspace_bytes(int is_bf16, int nbh, int dk, int dv) {
 template <typename TIn>
 static hipError_t fused_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                           const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                          int H, int dk, int dv, void* ws, size_t wsb, bool unb, hipStream_t st) {
-  KDA_DISPATCH_D(go_fused, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, wsb, unb, st);
+                          int H, int dk, int dv, void* ws, size_t wsb, bool unb, float* snap, int snap_every,
+                          hipStream_t st) {
+  KDA_DISPATCH_D(go_fused, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, wsb, unb, snap, snap_every, st);
 }
 template <typename TIn>
 static hipError_t stages_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                            const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                           int H, int dk, int dv, void* ws, int stages, bool unb, hipStream_t st) {
-  KDA_DISPATCH_D(go_stages, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, unb, st);
+                           int H, int dk, int dv, void* ws, int stages, bool unb, float* snap, int snap_every,
+                           hipStream_t st) {
+  KDA_DISPATCH_D(go_stages, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, stages, unb, snap, snap_every,
+                 st);
 }
 
 hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
                             int B, int T_len, int H, int dk, int dv, void* ws, size_t ws_bytes, int unbounded,
-                            hipStream_t st) {
+                            float* snap, int snap_every, hipStream_t st) {
   const bool u = unbounded != 0;
   if (is_bf16)
-    return fused_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, st);
-  return fused_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, st);
+    return fused_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, snap,
+                         snap_every, st);
+  return fused_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, snap,
+                        snap_every, st);
 }
 
 hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                              const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
                              int B, int T_len, int H, int dk, int dv, void* ws, int stages, int unbounded,
-                             hipStream_t st) {
+                             float* snap, int snap_every, hipStream_t st) {
   const bool u = unbounded != 0;
   if (is_bf16)
-    return stages_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, u, st);
-  return stages_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, u, st);
+    return stages_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, u, snap,
+                          snap_every, st);
+  return stages_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, stages, u, snap,
+                         snap_every, st);
 }
 
+}  // namespace kda
+
+namespace kda {
+hipError_t launch_zero_words(void* p, size_t nwords, hipStream_t st) {
+  if (nwords == 0) return hipSuccess;
+  if (nwords > 0x7fffffffu) return hipErrorInvalidValue;
+  const int n = (int)nwords;
+  hipLaunchKernelGGL(clear_ints_kernel, dim3((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), dim3(256), 0, st,
+                     reinterpret_cast<int*>(p), n);
+  return hipGetLastError();
+}
 }  // namespace kda

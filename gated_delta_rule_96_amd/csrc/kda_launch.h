@@ -20,16 +20,21 @@ size_t fwd_fused_workspace_bytes(int is_bf16, int nbh, int dk, int dv);
 
 // Chunked prefill, fused schedule (one persistent kernel per batch of heads).
 // unbounded != 0: the decay may go below -5 (diagonal tiles by position pairs).
+// snap != nullptr, snap_every > 0: states after every snap_every chunks
+// (excluding the end) to snap[j][b * H + h][dk][dv].
 hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
                             int B, int T, int H, int dk, int dv, void* workspace, size_t workspace_bytes,
-                            int unbounded, hipStream_t stream);
+                            int unbounded, float* snap, int snap_every, hipStream_t stream);
 
 // Chunked prefill, two-stage schedule: bit 0 intra-chunk kernel, bit 1 state pass.
 hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                              const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
                              int B, int T, int H, int dk, int dv, void* workspace, int stages, int unbounded,
-                             hipStream_t stream);
+                             float* snap, int snap_every, hipStream_t stream);
+
+// Zero-fills nwords 4-byte words on the stream (a kernel, not a memset node).
+hipError_t launch_zero_words(void* p, size_t nwords, hipStream_t stream);
 
 // One decode token per (b, h), state updated in place.
 hipError_t launch_decode_step(int is_bf16, const void* q, const void* k, const void* v,

@@ -53,6 +53,10 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_stages_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kda_fwd_chunked.restype = I
         L.kda_fwd_chunked.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, P]
+        L.kda_fwd_chunked_varlen.restype = I
+        L.kda_fwd_chunked_varlen.argtypes = [P, P, P, P, P, P, F, P, I, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
+        L.kda_fwd_varlen_snapshots.restype = ctypes.c_longlong
+        L.kda_fwd_varlen_snapshots.argtypes = [P, I, I, I]
         L.kda_fwd_chunked_unbounded.restype = I
         L.kda_fwd_chunked_unbounded.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, P]
         L.kda_fwd_chunked_stages.restype = I
@@ -183,6 +187,54 @@ def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state
         mask = int(stages) | (KDA_STAGES_UNBOUNDED if unbounded else 0)
         _check(lib().kda_fwd_chunked_stages(*args, mask, _stream(q.device)), "kda_fwd_chunked_stages")
     return o, (ht if final_state else None)
+
+
+def _cu_array(cu_seqlens):
+    cu = [int(x) for x in cu_seqlens]
+    return (ctypes.c_int * len(cu))(*cu), len(cu) - 1
+
+
+def varlen_snapshots(cu_seqlens, snap_every, chunk=CHUNK) -> int:
+    """Number of snapshots fwd_chunked_varlen writes (kda_fwd_varlen_snapshots)."""
+    arr, n = _cu_array(cu_seqlens)
+    s = int(lib().kda_fwd_varlen_snapshots(ctypes.cast(arr, ctypes.c_void_p), n, int(snap_every), chunk))
+    if s < 0:
+        raise ValueError("invalid cu_seqlens or snap_every")
+    return s
+
+
+def fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, h0=None, *, gcum=None, scale=None, snap_every=0, ht=None,
+                       workspace=None, out=None, chunk=CHUNK):
+    """o, ht, snaps = fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, h0).
+    N sequences packed along tokens: q,k,g [1,T,H,dk]; v [1,T,H,dv]; beta
+    [1,T,H]; cu_seqlens host ints (N+1, from 0 to T); h0/ht [N,H,dk,dv] fp32.
+    snaps [S,H,dk,dv] fp32: the state after every snap_every chunks of each
+    sequence (before its end), sequences in order (None when snap_every=0)."""
+    _, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    arr, N = _cu_array(cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if workspace is None:
+        workspace = alloc_workspace(1, T, H, dk, dv, q.dtype, q.device, chunk)
+    o = torch.empty((1, T, H, dv), dtype=torch.float32, device=q.device) if out is None else out
+    if ht is None:
+        ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    for t in (h0, ht):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (N, H, dk, dv)):
+            raise ValueError("states must be fp32 [N, H, dk, dv]")
+    snaps = None
+    if snap_every > 0:
+        ns = varlen_snapshots(cu_seqlens, snap_every, chunk)
+        snaps = torch.empty((max(ns, 1), H, dk, dv), dtype=torch.float32, device=q.device)
+    _check(lib().kda_fwd_chunked_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gcum), _ptr(beta), float(scale),
+                                        ctypes.cast(arr, ctypes.c_void_p), N, _ptr(h0), _ptr(ht), _ptr(o),
+                                        _ptr(snaps), int(snap_every), dt, T, H, dk, dv, chunk, _ptr(workspace),
+                                        workspace.numel(), _stream(q.device)), "kda_fwd_chunked_varlen")
+    if snaps is not None:
+        snaps = snaps[:varlen_snapshots(cu_seqlens, snap_every, chunk)]
+    return o, ht, snaps
 
 
 def decode_step(q, k, v, g, beta, state, *, scale=None, out=None):

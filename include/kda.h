@@ -176,6 +176,38 @@ int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const vo
                            void* stream);
 
 /*
+ * Variable-length packed prefill with prefix-state snapshots ("Key claims",
+ * Infrastructure: states kept at prefix boundaries for reuse; "Method",
+ * section 2.1).  N sequences are packed along the token axis: q, k, g
+ * [1,T,H,dk], v [1,T,H,dv], beta [1,T,H], o [1,T,H,dv] fp32, gcum (if used)
+ * [1,T,H,dk]; sequence i is tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 of
+ * them, with its own chunks (every chunk starts at the sequence start), its
+ * own initial state h0[i] and final state ht[i] ([N,H,dk,dv] fp32; NULL h0:
+ * zero states; ht may alias h0).  cu_seqlens is a HOST array of N+1 ints
+ * with cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T; empty
+ * sequences are allowed (ht[i] = h0[i]).
+ * Snapshots: when snap != NULL and snap_every > 0, the state after every
+ * snap_every chunks of a sequence (after tokens 64 j snap_every, j = 1, 2,
+ * ..., strictly before the sequence's end) is written to snap
+ * [S,H,dk,dv] fp32, sequences in order, snapshots in order within one;
+ * S = kda_fwd_varlen_snapshots(cu_seqlens, N, snap_every, chunk).
+ * workspace: kda_fwd_workspace_bytes(1, T, H, dk, dv, chunk, dtype) bytes.
+ * One fused launch per non-empty sequence, in order on `stream`.
+ * Errors: as kda_fwd_chunked; KDA_ERR_NULL for cu_seqlens == NULL,
+ * KDA_ERR_SHAPE for inconsistent cu_seqlens or snap_every < 0,
+ * KDA_ERR_ALIGN for an unaligned snap.
+ */
+int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const void* g,
+                           const float* gcum, const void* beta, float scale,
+                           const int* cu_seqlens, int N, const float* h0, float* ht, float* o,
+                           float* snap, int snap_every, int dtype, int T, int H, int dk, int dv,
+                           int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of snapshots kda_fwd_chunked_varlen writes for these sequences
+ * (host computation; -1 for invalid arguments, including snap_every <= 0). */
+long long kda_fwd_varlen_snapshots(const int* cu_seqlens, int N, int snap_every, int chunk);
+
+/*
  * Decode step (page "How a Frontier Model Gets Built...", "Technical
  * Details": fixed-size running state instead of a KV cache): one new token
  * per (b, h).  state [B,H,dk,dv] fp32 is read and overwritten in place with

@@ -119,3 +119,26 @@ def test_unbounded_entry_points_validate_like_the_bounded_ones():
     assert L.kda_prepare_decay_softplus(None, FAKE, FAKE, FAKE, 1, 1, 64, 1, 128, 64, None) == 1
     assert L.kda_prepare_decay_softplus(FAKE, None, FAKE, FAKE, 1, 1, 64, 1, 128, 64, None) == 1
     assert L.kda_prepare_decay_softplus(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 1, 96, 64, None) == 5
+
+
+def test_varlen_validation_and_snapshot_count():
+    L = kda.lib()
+    cu = lambda *xs: (ctypes.c_int * len(xs))(*xs)
+
+    def call(c, N, T=100, snap=None, every=0, ws=FAKE, wsb=1 << 40):
+        return L.kda_fwd_chunked_varlen(FAKE, FAKE, FAKE, FAKE, None, FAKE, 0.1, c, N, None, None, FAKE, snap,
+                                        every, 1, T, 2, 128, 128, 64, ws, wsb, None)
+
+    assert call(None, 1) == 1
+    assert call(cu(0, 50, 40), 2) == 2         # decreasing
+    assert call(cu(1, 100), 1) == 2            # does not start at 0
+    assert call(cu(0, 99), 1) == 2             # does not end at T
+    assert call(cu(0, 100), 0) == 2            # N = 0
+    assert call(cu(0, 100), 1, every=-1) == 2
+    assert call(cu(0, 100), 1, snap=FAKE + 4, every=1) == 4
+    assert call(cu(0, 100), 1, wsb=1024) == 6
+    n = L.kda_fwd_varlen_snapshots
+    n.restype = ctypes.c_longlong
+    assert n(cu(0, 64, 200, 200, 1000), 4, 2, 64) == 0 + 1 + 0 + 6
+    assert n(cu(0, 65), 1, 1, 64) == 1 and n(cu(0, 64), 1, 1, 64) == 0
+    assert n(cu(0, 10), 1, 0, 64) == -1 and n(cu(0, 10), 1, 1, 32) == -1 and n(cu(5, 1), 1, 1, 64) == -1
