@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from gated_delta_rule_96_amd import synth
-from oracle import brute, chunkwise, gate, seq
+from oracle import brute, chunkwise, gate, layer, seq
 
 
 def _rand_case(rng, B, T, H, dk, dv, g_low=-5.0, with_h0=True):
@@ -230,3 +230,27 @@ def test_sixteen_row_rescaling_bound_fits_bf16():
     assert 16 * 5 < math.log(bf16_max)
     assert math.exp(-80) > 2.0 ** -126            # its inverse is a normal number too
     assert 17 * 5 < math.log(bf16_max) < 18 * 5   # 17 rows still fit, 18 could overflow
+
+
+# ---------------------------------------------------------------- layer steps
+def test_l2norm_rows_pins():
+    rng = np.random.default_rng(8)
+    x = 3 * rng.standard_normal((2, 5, 3, 64))
+    y = layer.l2norm_rows(x)
+    n2 = np.sum(x * x, axis=-1)
+    np.testing.assert_allclose(np.sum(y * y, axis=-1), n2 / (n2 + 1e-6), rtol=1e-13)   # unit up to eps
+    np.testing.assert_allclose(layer.l2norm_rows(7.5 * x, eps=0.0), layer.l2norm_rows(x, eps=0.0), rtol=1e-13)
+    assert np.all(layer.l2norm_rows(np.zeros((1, 4))) == 0.0)
+    e = np.zeros((1, 8)); e[0, 3] = 2.0
+    np.testing.assert_allclose(layer.l2norm_rows(e, eps=0.0), e / 2.0, rtol=0)
+
+
+def test_output_gate_pins():
+    rng = np.random.default_rng(9)
+    o = rng.standard_normal((2, 3, 4))
+    np.testing.assert_allclose(layer.output_gate(o, np.zeros_like(o)), o / 2, rtol=1e-15)
+    np.testing.assert_allclose(layer.output_gate(o, np.full_like(o, 800.0)), o, rtol=1e-15)
+    assert np.all(layer.output_gate(o, np.full_like(o, -800.0)) == 0.0)
+    og = 4 * rng.standard_normal(o.shape)
+    np.testing.assert_allclose(layer.output_gate(o, og) + layer.output_gate(o, -og), o, rtol=1e-13, atol=1e-15)
+
