@@ -90,6 +90,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards by "
@@ -277,6 +278,68 @@ def main():
                f"{v_parity['max_err_over_rms_snapshot']:.2e}" if v_parity else ""))
         del o_v, h0v, res
 
+    # ---------------- the layer's steps fused in: gate of z in the scan, q/k
+    # row normalisation in the kernel, sigmoid output gate on o; against the
+    # same steps as separate passes (decay kernel, torch normalisation and gate)
+    layer_res = None
+    if not args.no_layer:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        og = (2.0 * torch.randn((B, T, H, DV), generator=gen, device=dev)).to(torch.bfloat16)
+        o_l = torch.empty_like(o)
+        ht_l = torch.empty_like(ht)
+
+        def fused_layer():
+            kda.fwd_chunked_layer(q, k, v, z, A, beta, h0, og=og, qk_l2norm=True, ht=ht_l, workspace=ws, out=o_l)
+
+        def separate_steps():
+            gg, _ = kda.prepare_decay(z, A, want_gcum=False)
+            nrm = lambda x: (x.float() * torch.rsqrt((x.float() ** 2).sum(-1, keepdim=True) + 1e-6)).to(x.dtype)
+            oo, _ = kda.fwd_chunked(nrm(q), nrm(k), v, gg, beta, h0, ht=ht_l, workspace=ws)
+            return oo * torch.sigmoid(og.float())
+
+        def timed(fn, n):
+            fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        ms_fused_l = timed(fused_layer, n_k)
+        ms_sep = timed(separate_steps, n_k)
+        o_sep = separate_steps()
+        fused_layer()
+        torch.cuda.synchronize()
+        agree = float((o_l - o_sep).abs().max() / o_sep.pow(2).mean().sqrt())
+        l_parity = None
+        if not args.no_cpu_baseline:
+            from oracle import gate as ogate
+            from oracle import layer as olayer
+            from oracle import seq
+
+            heads = [6, 25]
+            f = lambda t: t[:, :, heads].float().cpu().numpy()
+            bfr = lambda x: torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+            qn, kn = bfr(olayer.l2norm_rows(f(q))), bfr(olayer.l2norm_rows(f(k)))
+            o_ref, _ = seq.kda_seq(qn, kn, f(v), ogate.gate(f(z), d["A"][heads]), f(beta), d["h0"][:, heads],
+                                   nthreads=seq.threads_default())
+            o_ref = olayer.output_gate(o_ref, f(og))
+            o_gpu = o_l[:, :, heads].cpu().double().numpy()
+            l_parity = {"sample": f"o of heads {heads}, all {T} tokens, vs fp64 oracle (gate of z, row "
+                                  "normalisation rounded to bf16, output gate)",
+                        "max_err_over_rms": float(np.max(np.abs(o_gpu - o_ref)) / math.sqrt(float(np.mean(o_ref ** 2)))),
+                        "tolerance": 2e-2}
+        layer_res = {"workload": "same prefill with z + A (decay gate in the scan), q/k row L2 normalisation in "
+                                 "the kernel and a sigmoid output gate og [B,T,H,dv] bf16",
+                     "fused_ms": round(ms_fused_l, 4), "separate_steps_ms": round(ms_sep, 4),
+                     "fused_vs_separate_max_err_over_rms": agree, "parity": l_parity}
+        log(f"layer: fused {ms_fused_l:.3f} ms vs separate steps {ms_sep:.3f} ms; agreement {agree:.2e}"
+            + (f"; parity {l_parity['max_err_over_rms']:.2e}" if l_parity else ""))
+        del og, o_l, ht_l, o_sep
+
     tok_s = B * T / (ms_step * 1e-3)
     gbs = abytes / (ms_step * 1e-3) / 1e9
     tflops = flop / (ms_step * 1e-3) / 1e12
@@ -374,6 +437,7 @@ def main():
         "decode": decode,
         "unbounded_decay_ablation": ablation,
         "varlen_snapshots": varlen,
+        "layer_prologue_epilogue": layer_res,
         "parity": parity,
         "cpu_baseline": cpu,
     }

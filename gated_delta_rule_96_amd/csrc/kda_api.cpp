@@ -127,7 +127,7 @@ int fwd_fused_impl(const void* q, const void* k, const void* v, const void* g, c
   if (st != KDA_OK) return st;
   if (workspace_bytes < kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
   hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
-                                       workspace, workspace_bytes, unbounded, nullptr, 0,
+                                       workspace, workspace_bytes, unbounded, nullptr, 0, nullptr, nullptr, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -160,6 +160,23 @@ int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const vo
   hipError_t e = kda::launch_fwd_stages(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
                                         workspace, mask, (stages & KDA_STAGES_UNBOUNDED) ? 1 : 0, nullptr, 0,
                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_fwd_chunked_layer(const void* q, const void* k, const void* v, const void* z, const float* A,
+                          const void* beta, const void* og, float scale, const float* h0, float* ht, float* o,
+                          int flags, int dtype, int B, int T, int H, int dk, int dv, int chunk, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const int st = check_fwd(q, k, v, z, nullptr, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace, 3);
+  if (st != KDA_OK) return st;
+  if (!z || !A) return KDA_ERR_NULL;
+  if (flags & ~KDA_LAYER_QK_L2NORM) return KDA_ERR_SHAPE;
+  if ((og && !aligned16(og)) || !aligned16(A)) return KDA_ERR_ALIGN;
+  if (workspace_bytes < kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
+  const int lf = 1 /* g is z */ | ((flags & KDA_LAYER_QK_L2NORM) ? 2 : 0);
+  hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, z, nullptr, beta, scale, h0, ht, o, B, T, H, dk,
+                                       dv, workspace, workspace_bytes, 0, nullptr, 0, A, og, lf,
+                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -212,7 +229,8 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
       e = kda::launch_fwd_fused(dtype == KDA_BF16, at(q, hk), at(k, hk), at(v, hv), at(g, hk),
                                 gcum ? gcum + t0 * hk : nullptr, at(beta, (size_t)H), scale, h0_i, ht_i,
                                 o + t0 * hv, 1, len, H, dk, dv, workspace, workspace_bytes, 0,
-                                snaps ? snap + (size_t)snap_off * sd : nullptr, snaps ? snap_every : 0, hs);
+                                snaps ? snap + (size_t)snap_off * sd : nullptr, snaps ? snap_every : 0, nullptr,
+                                nullptr, 0, hs);
       if (snaps) {
         const long long nch = ((long long)len + kChunk - 1) / kChunk;
         snap_off += (nch - 1) / snap_every;

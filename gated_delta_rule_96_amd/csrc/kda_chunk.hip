@@ -157,6 +157,53 @@ __device__ __forceinline__ void wave_tile(int w, int j, int per_wave, int& x, in
   }
 }
 
+// The layer's steps either side of the path, fused into the kernel (all
+// optional, selected per call; every test on them is wave-uniform):
+//   kLayerGateZ   the decay input is z: g = gmin Sigmoid(exp(A[h]) z), fp32,
+//                 in the staging of the scan (no separate decay pass)
+//   kLayerNormQK  q and k rows divided by sqrt(sum of squares + 1e-6) before
+//                 use, in fp32, then rounded to the input type
+//   og != nullptr output gate: o <- Sigmoid(og) * o, og [B,T,H,dv] of the
+//                 input type
+constexpr int kLayerGateZ = 1, kLayerNormQK = 2;
+// Sigmoid(x) = 1 / (1 + e^{-x}) with v_exp_f32 and v_rcp_f32 (about 2 ulp;
+// 0 and 1 at the far ends).
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-x * kLog2e));
+}
+constexpr float kGateMin = -5.0f;
+constexpr float kNormEps = 1e-6f;
+struct Layer {
+  const float* A;
+  const void* og;
+  int flags;
+};
+
+// Row-wise L2 normalisation of 16 raw bytes of a row that is spread over G
+// consecutive lanes (G a power of two dividing 64): every lane of the
+// group returns its elements divided by the row's norm.
+template <typename TIn, int G>
+__device__ __forceinline__ raw16 l2norm_part(raw16 v) {
+  constexpr int VE = 16 / sizeof(TIn);
+  float ss = 0.f;
+#pragma unroll
+  for (int x = 0; x < VE; ++x) ss = fmaf(raw_elem<TIn>(v, x), raw_elem<TIn>(v, x), ss);
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off);
+  const float inv = 1.0f / sqrtf(ss + kNormEps);
+  raw16 out;
+  if constexpr (sizeof(TIn) == 4) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) out[x] = v[x] * inv;
+  } else {
+    bf16x8 o8;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) o8[x] = from_f32<bf16>(raw_elem<TIn>(v, x) * inv);
+    out = __builtin_bit_cast(raw16, o8);
+  }
+  return out;
+}
+
 // One chunk's raw inputs in registers (rows past the end of the sequence
 // are zero): 16-byte vectors of k, q, g and v rows (k, q, g row-major over
 // the threads, v column-block-major), and beta.  Inputs are read once, so
@@ -314,7 +361,8 @@ __constant__ signed char kWaveTile[8][2] = {{0, -1}, {1, -1}, {2, -1}, {3, -1}, 
 template <typename TIn, int DK, int DV, bool kUnb, typename AfterStage, typename Prefetch>
 __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& in, const float* __restrict__ gcum,
                                               float scale, int b, int h, int T_len, int H, int ch,
-                                              char* __restrict__ rec, AfterStage after_stage, Prefetch prefetch) {
+                                              char* __restrict__ rec, AfterStage after_stage, Prefetch prefetch,
+                                              Layer lay = Layer{nullptr, nullptr, 0}) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using Gm = typename P::Gram;
@@ -357,18 +405,26 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   float* rUinv = reinterpret_cast<float*>(rec + R::UINV_OFF_BYTES);
 
   // ---- phase 0: stage k, q, beta (and g) from the input registers
+  const bool normqk = (lay.flags & kLayerNormQK) != 0;   // uniform
+  const bool gatez = (lay.flags & kLayerGateZ) != 0;
+  const float ea = gatez ? expf(lay.A[h]) : 0.f;   // exp(A), once per chunk
 #pragma unroll
   for (int i = 0; i < IR::NK; ++i) {
     const int n = tid + kThreads * i;
     const int r = n / (DK / VE), c = (n % (DK / VE)) * VE;
-    *reinterpret_cast<raw16*>(sK + r * L::LK + c) = in.k[i];
-    *reinterpret_cast<raw16*>(sQ + r * L::LK + c) = in.q[i];
+    *reinterpret_cast<raw16*>(sK + r * L::LK + c) = normqk ? l2norm_part<TIn, DK / VE>(in.k[i]) : in.k[i];
+    *reinterpret_cast<raw16*>(sQ + r * L::LK + c) = normqk ? l2norm_part<TIn, DK / VE>(in.q[i]) : in.q[i];
     if (!gcum) {
+      float gv[VE];
+#pragma unroll
+      for (int x = 0; x < VE; ++x) {
+        gv[x] = raw_elem<TIn>(in.g[i], x);
+        // (rows past the end of the sequence keep g = 0: no decay there)
+        if (gatez) gv[x] = r < Lrows ? kGateMin * sigmoid_fast(ea * gv[x]) : 0.f;
+      }
 #pragma unroll
       for (int x = 0; x < VE; x += 4)
-        *reinterpret_cast<f32x4*>(sG + r * L::LG + c + x) =
-            f32x4{raw_elem<TIn>(in.g[i], x), raw_elem<TIn>(in.g[i], x + 1), raw_elem<TIn>(in.g[i], x + 2),
-                  raw_elem<TIn>(in.g[i], x + 3)};
+        *reinterpret_cast<f32x4*>(sG + r * L::LG + c + x) = f32x4{gv[x], gv[x + 1], gv[x + 2], gv[x + 3]};
     }
   }
   if (tid < kC) sBeta[tid] = in.beta;
@@ -791,7 +847,11 @@ struct ConsumerLds {
   static constexpr size_t SH = R::U_OFF_BYTES;
   static constexpr size_t UPART = (size_t)kC * (DV / NS) * sizeof(Op);
   static constexpr size_t USED = SH + UPART;
-  static constexpr size_t BUF = (USED + 255) / 256 * 256;
+  // output-gate values of the chunk's rows and this work-group's columns
+  // (input type, row-major [C][dv / NS]), staged after the record
+  static constexpr size_t OGB = (size_t)kC * (DV / NS) * sizeof(TIn);
+  static constexpr size_t OG_OFF = (USED + 15) / 16 * 16;
+  static constexpr size_t BUF = (OG_OFF + OGB + 255) / 256 * 256;
   static constexpr int NBUF = 2 * BUF + 16 <= kLdsMax ? 2 : 1;
   static constexpr size_t BYTES = NBUF * BUF + 16;
   static_assert(BUF + 16 <= kLdsMax, "record does not fit in LDS");
@@ -812,7 +872,7 @@ template <typename TIn, int DK, int DV, bool kRing>
 __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
                                               const float* __restrict__ h0, float* __restrict__ ht,
                                               float* __restrict__ o, int b, int h, int T_len, int H,
-                                              int nchunks, Snap snap) {
+                                              int nchunks, Snap snap, Layer lay = Layer{nullptr, nullptr, 0}) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using R = Rec<TIn, DK, DV>;
@@ -858,6 +918,10 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   if (!owner) {
     const int htid = tid - 64 * kOwners;
     raw16 pre[PPT];
+    // output gate rows of a chunk: 16-byte pieces, row-major over the columns
+    constexpr int OGV = DV / CL::NS * (int)sizeof(TIn) / 16;   // pieces per row
+    constexpr int OGN = (kC * OGV + kHelpers - 1) / kHelpers;
+    raw16 preg[OGN];
     bool ok = true;
     // true once chunk c is published and may be read
     auto ready_wait = [&](int c) -> bool {
@@ -877,6 +941,18 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         const int n = htid + kHelpers * i;
         if (n < NV16) pre[i] = rec[n < NSH16 ? n : n + uoff16];
       }
+      if (lay.og) {
+        const TIn* ogc = reinterpret_cast<const TIn*>(lay.og) + (((size_t)b * T_len + c * kC) * H + h) * DV +
+                         (size_t)vb * (DV / CL::NS);
+#pragma unroll
+        for (int i = 0; i < OGN; ++i) {
+          const int n = htid + kHelpers * i, r = n / OGV, pc = n % OGV;
+          if (n < kC * OGV)
+            preg[i] = c * kC + r < T_len ? *reinterpret_cast<const raw16*>(ogc + (size_t)r * H * DV +
+                                                                           pc * (16 / sizeof(TIn)))
+                                         : raw16{0.f, 0.f, 0.f, 0.f};
+        }
+      }
     };
     auto stage = [&](int c) {
       char* buf = buf_of(c);
@@ -884,6 +960,13 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       for (int i = 0; i < PPT; ++i) {
         const int n = htid + kHelpers * i;
         if (n < NV16) reinterpret_cast<raw16*>(buf)[n] = pre[i];
+      }
+      if (lay.og) {
+#pragma unroll
+        for (int i = 0; i < OGN; ++i) {
+          const int n = htid + kHelpers * i;
+          if (n < kC * OGV) reinterpret_cast<raw16*>(buf + CL::OG_OFF)[n] = preg[i];
+        }
       }
       // every load of chunk c has returned its data before its slot is
       // handed back (after the next X)
@@ -1027,6 +1110,17 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) Ov[rt][jj] = accQ[rt][jj] * iss + accM[jj] * ius;
     }
+    if (lay.og) {   // output gate: o <- Sigmoid(og) o, og staged with the record
+      const TIn* sOg = reinterpret_cast<const TIn*>(buf + CL::OG_OFF);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const f32x4 gz = widen4(load4(sOg + (16 * rt + l16) * (DV / CL::NS) + 16 * (jl0 + jj) + g4));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Ov[rt][jj][i] *= sigmoid_fast(gz[i]);
+        }
+    }
     if (full) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
@@ -1147,7 +1241,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
                                                              const float* __restrict__ h0, float* __restrict__ ht,
                                                              float* __restrict__ o, int T_len, int H, int nchunks,
                                                              int head0, int nheads, char* __restrict__ ring,
-                                                             int* __restrict__ ctrl, int R, Snap snap) {
+                                                             int* __restrict__ ctrl, int R, Snap snap, Layer lay) {
   using Rc = Rec<TIn, DK, DV>;
   __shared__ __align__(16) char smem[FusedLds<TIn, DK, DV>::BYTES];
   int* sWord = reinterpret_cast<int*>(smem + FusedLds<TIn, DK, DV>::BYTES - 16);
@@ -1163,7 +1257,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     const int jh = xcd + 8 * (li / NS), vb = li % NS, bh = head0 + jh;
     consume_chain<TIn, DK, DV, true>(smem, ring + (size_t)jh * R * Rc::BYTES,
                                      Ring{ready + jh * R, done + jh * NS + vb, err, cxcc + jh * NS + vb, R}, vb, h0,
-                                     ht, o, bh / H, bh % H, T_len, H, nchunks, snap);
+                                     ht, o, bh / H, bh % H, T_len, H, nchunks, snap, lay);
     return;
   }
 
@@ -1237,7 +1331,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
       }
     };
     if (!produce_chunk<TIn, DK, DV, kUnb>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
-                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage, prefetch))
+                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage, prefetch, lay))
       return;
     pending = it;
     if (nxt >= total) {
@@ -1282,7 +1376,8 @@ static size_t fused_ws_bytes(int nbh) {
 template <typename TIn, int DK, int DV>
 static hipError_t go_fused(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                            const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
-                           int H, void* ws, size_t ws_bytes, bool unb, float* snap, int snap_every, hipStream_t st) {
+                           int H, void* ws, size_t ws_bytes, bool unb, float* snap, int snap_every, Layer lay,
+                           hipStream_t st) {
   const int nchunks = (T_len + kC - 1) / kC;
   const int nbh = B * H;
   int dev = 0, cus = 0;
@@ -1307,7 +1402,7 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
     auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true> : fused_fwd_kernel<TIn, DK, DV, false>;
     hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q, (const TIn*)k, (const TIn*)v,
                        (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len, H, nchunks, head0, nh, ring,
-                       ctrl, kRingSlots, Snap{snap, snap_every, nbh});
+                       ctrl, kRingSlots, Snap{snap, snap_every, nbh}, lay);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1364,8 +1459,9 @@ template <typename TIn>
 static hipError_t fused_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                           const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
                           int H, int dk, int dv, void* ws, size_t wsb, bool unb, float* snap, int snap_every,
-                          hipStream_t st) {
-  KDA_DISPATCH_D(go_fused, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, wsb, unb, snap, snap_every, st);
+                          Layer lay, hipStream_t st) {
+  KDA_DISPATCH_D(go_fused, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, wsb, unb, snap, snap_every,
+                 lay, st);
 }
 template <typename TIn>
 static hipError_t stages_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
@@ -1379,13 +1475,15 @@ static hipError_t stages_t(const void* q, const void* k, const void* v, const vo
 hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
                             int B, int T_len, int H, int dk, int dv, void* ws, size_t ws_bytes, int unbounded,
-                            float* snap, int snap_every, hipStream_t st) {
+                            float* snap, int snap_every, const float* A, const void* og, int layer_flags,
+                            hipStream_t st) {
   const bool u = unbounded != 0;
+  const Layer lay{A, og, layer_flags};
   if (is_bf16)
     return fused_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, snap,
-                         snap_every, st);
+                         snap_every, lay, st);
   return fused_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, snap,
-                        snap_every, st);
+                        snap_every, lay, st);
 }
 
 hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,

@@ -22,10 +22,13 @@ size_t fwd_fused_workspace_bytes(int is_bf16, int nbh, int dk, int dv);
 // unbounded != 0: the decay may go below -5 (diagonal tiles by position pairs).
 // snap != nullptr, snap_every > 0: states after every snap_every chunks
 // (excluding the end) to snap[j][b * H + h][dk][dv].
+// layer_flags (1: g is z, gate with A fused into the scan; 2: q/k rows L2
+// normalised in-kernel) and og (output gate pre-activation, nullable).
 hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
                             int B, int T, int H, int dk, int dv, void* workspace, size_t workspace_bytes,
-                            int unbounded, float* snap, int snap_every, hipStream_t stream);
+                            int unbounded, float* snap, int snap_every, const float* A, const void* og,
+                            int layer_flags, hipStream_t stream);
 
 // Chunked prefill, two-stage schedule: bit 0 intra-chunk kernel, bit 1 state pass.
 hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,

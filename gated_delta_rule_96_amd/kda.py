@@ -19,6 +19,7 @@ LIB_PATH = PKG / "libkda.so"
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_STAGES_UNBOUNDED = 4
+KDA_LAYER_QK_L2NORM = 1
 CHUNK = 64
 GMIN = -5.0
 
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_stages_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kda_fwd_chunked.restype = I
         L.kda_fwd_chunked.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, P]
+        L.kda_fwd_chunked_layer.restype = I
+        L.kda_fwd_chunked_layer.argtypes = [P, P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P, S, P]
         L.kda_fwd_chunked_varlen.restype = I
         L.kda_fwd_chunked_varlen.argtypes = [P, P, P, P, P, P, F, P, I, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
         L.kda_fwd_varlen_snapshots.restype = ctypes.c_longlong
@@ -186,6 +189,35 @@ def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state
     else:
         mask = int(stages) | (KDA_STAGES_UNBOUNDED if unbounded else 0)
         _check(lib().kda_fwd_chunked_stages(*args, mask, _stream(q.device)), "kda_fwd_chunked_stages")
+    return o, (ht if final_state else None)
+
+
+def fwd_chunked_layer(q, k, v, z, A, beta, h0=None, *, og=None, qk_l2norm=False, scale=None, final_state=True,
+                      ht=None, workspace=None, out=None, chunk=CHUNK):
+    """o, ht = fwd_chunked_layer(q, k, v, z, A, beta, h0): kda_fwd_chunked with
+    the decay gate of z (A [H] fp32) fused into the kernel's scan, optional
+    in-kernel q/k row L2 normalisation and optional sigmoid output gate og
+    [B,T,H,dv] (same dtype as q)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("z", z), ("beta", beta)) + ((("og", og),) if og is not None else ()):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+    if A.dtype != torch.float32 or A.shape != (H,):
+        raise ValueError("A must be fp32 [H]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if workspace is None:
+        workspace = alloc_workspace(B, T, H, dk, dv, q.dtype, q.device, chunk)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device) if out is None else out
+    if final_state and ht is None:
+        ht = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    flags = KDA_LAYER_QK_L2NORM if qk_l2norm else 0
+    _check(lib().kda_fwd_chunked_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(og),
+                                       float(scale), _ptr(h0), _ptr(ht if final_state else None), _ptr(o), flags,
+                                       dt, B, T, H, dk, dv, chunk, _ptr(workspace), workspace.numel(),
+                                       _stream(q.device)), "kda_fwd_chunked_layer")
     return o, (ht if final_state else None)
 
 

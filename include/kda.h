@@ -176,6 +176,29 @@ int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const vo
                            void* stream);
 
 /*
+ * Chunked prefill with the layer's steps on either side fused in (the
+ * prologue and epilogue of the path):
+ *   - the decay gate: z (instead of g, same layout) and A [H] fp32 are
+ *     given; g = -5 Sigmoid(exp(A[h]) z) is formed in fp32 inside the
+ *     kernel's scan ("Key claims", section 2.1.1; "Method", section 2.1);
+ *   - flags & KDA_LAYER_QK_L2NORM: q and k rows are divided by
+ *     sqrt(sum of squares + 1e-6) in the kernel, in fp32, then rounded to
+ *     dtype (keys of the delta rule are unit vectors);
+ *   - og != NULL ([B,T,H,dv] of dtype): output gate, o = Sigmoid(og) * o
+ *     (the pages mention KDA's output gating without defining it; this is
+ *     the elementwise sigmoid gate they name for MLA, section 2.1.2).
+ * Other arguments, layouts, workspace and errors as kda_fwd_chunked (g and
+ * gcum are replaced by z and A); KDA_ERR_NULL for z or A NULL,
+ * KDA_ERR_SHAPE for unknown flag bits.
+ */
+#define KDA_LAYER_QK_L2NORM 1
+int kda_fwd_chunked_layer(const void* q, const void* k, const void* v, const void* z,
+                          const float* A, const void* beta, const void* og, float scale,
+                          const float* h0, float* ht, float* o, int flags, int dtype, int B, int T,
+                          int H, int dk, int dv, int chunk, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Variable-length packed prefill with prefix-state snapshots ("Key claims",
  * Infrastructure: states kept at prefix boundaries for reuse; "Method",
  * section 2.1).  N sequences are packed along the token axis: q, k, g

@@ -142,3 +142,18 @@ def test_varlen_validation_and_snapshot_count():
     assert n(cu(0, 64, 200, 200, 1000), 4, 2, 64) == 0 + 1 + 0 + 6
     assert n(cu(0, 65), 1, 1, 64) == 1 and n(cu(0, 64), 1, 1, 64) == 0
     assert n(cu(0, 10), 1, 0, 64) == -1 and n(cu(0, 10), 1, 1, 32) == -1 and n(cu(5, 1), 1, 1, 64) == -1
+
+
+def test_layer_entry_validation():
+    L = kda.lib()
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, None, None, FAKE, 0, 1, 1, 64, 1, 128, 128, 64, FAKE,
+         1 << 40, None]
+    for i in (3, 4):                       # z, A required
+        bad = list(a); bad[i] = None
+        assert L.kda_fwd_chunked_layer(*bad) == 1
+    bad = list(a); bad[11] = 2             # unknown flag bit
+    assert L.kda_fwd_chunked_layer(*bad) == 2
+    bad = list(a); bad[6] = FAKE + 2       # misaligned output gate
+    assert L.kda_fwd_chunked_layer(*bad) == 4
+    bad = list(a); bad[20] = 1024
+    assert L.kda_fwd_chunked_layer(*bad) == 6
