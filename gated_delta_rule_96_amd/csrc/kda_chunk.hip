@@ -358,7 +358,9 @@ __constant__ signed char kWaveTile[8][2] = {{0, -1}, {1, -1}, {2, -1}, {3, -1}, 
 // at four points of the later phases, with kLoadK | kLoadBeta, kLoadQ,
 // kLoadG, kLoadV in turn (as std::integral_constant), e.g. to load the next
 // chunk's inputs into `in` in portions while this one is computed.
-template <typename TIn, int DK, int DV, bool kUnb, typename AfterStage, typename Prefetch>
+// kExt: the layer steps (Layer) may be requested; without it their code is
+// compiled out of the plain kernels.
+template <typename TIn, int DK, int DV, bool kUnb, bool kExt, typename AfterStage, typename Prefetch>
 __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& in, const float* __restrict__ gcum,
                                               float scale, int b, int h, int T_len, int H, int ch,
                                               char* __restrict__ rec, AfterStage after_stage, Prefetch prefetch,
@@ -405,8 +407,8 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   float* rUinv = reinterpret_cast<float*>(rec + R::UINV_OFF_BYTES);
 
   // ---- phase 0: stage k, q, beta (and g) from the input registers
-  const bool normqk = (lay.flags & kLayerNormQK) != 0;   // uniform
-  const bool gatez = (lay.flags & kLayerGateZ) != 0;
+  const bool normqk = kExt && (lay.flags & kLayerNormQK) != 0;   // uniform
+  const bool gatez = kExt && (lay.flags & kLayerGateZ) != 0;
   const float ea = gatez ? expf(lay.A[h]) : 0.f;   // exp(A), once per chunk
 #pragma unroll
   for (int i = 0; i < IR::NK; ++i) {
@@ -759,7 +761,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __rest
   const int ch = blockIdx.x % nchunks, bh = blockIdx.x / nchunks;
   InRegs<TIn, DK, DV> in;
   load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, ch);
-  produce_chunk<TIn, DK, DV, kUnb>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, ch,
+  produce_chunk<TIn, DK, DV, kUnb, false>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, ch,
                                    ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [] { return true; },
                                    [](auto) {});
 }
@@ -868,7 +870,9 @@ struct Snap {
   int nbh;
 };
 
-template <typename TIn, int DK, int DV, bool kRing>
+// kExt: snapshots and the output gate may be requested (compiled out
+// otherwise).
+template <typename TIn, int DK, int DV, bool kRing, bool kExt>
 __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
                                               const float* __restrict__ h0, float* __restrict__ ht,
                                               float* __restrict__ o, int b, int h, int T_len, int H,
@@ -941,7 +945,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         const int n = htid + kHelpers * i;
         if (n < NV16) pre[i] = rec[n < NSH16 ? n : n + uoff16];
       }
-      if (lay.og) {
+      if (kExt && lay.og) {
         const TIn* ogc = reinterpret_cast<const TIn*>(lay.og) + (((size_t)b * T_len + c * kC) * H + h) * DV +
                          (size_t)vb * (DV / CL::NS);
 #pragma unroll
@@ -961,7 +965,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         const int n = htid + kHelpers * i;
         if (n < NV16) reinterpret_cast<raw16*>(buf)[n] = pre[i];
       }
-      if (lay.og) {
+      if (kExt && lay.og) {
 #pragma unroll
         for (int i = 0; i < OGN; ++i) {
           const int n = htid + kHelpers * i;
@@ -1110,7 +1114,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) Ov[rt][jj] = accQ[rt][jj] * iss + accM[jj] * ius;
     }
-    if (lay.og) {   // output gate: o <- Sigmoid(og) o, og staged with the record
+    if (kExt && lay.og) {   // output gate: o <- Sigmoid(og) o, og staged with the record
       const TIn* sOg = reinterpret_cast<const TIn*>(buf + CL::OG_OFF);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
@@ -1162,7 +1166,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         for (int jj = 0; jj < NJ; ++jj) S[ct][jj] = S[ct][jj] * d + acc[jj] * ius;
       }
     }
-    if (snap.p && snap.every > 0 && (c + 1) % snap.every == 0 && (c + 1) * kC < T_len) {
+    if (kExt && snap.p && snap.every > 0 && (c + 1) % snap.every == 0 && (c + 1) * kC < T_len) {
       float* sp = snap.p + ((size_t)((c + 1) / snap.every - 1) * snap.nbh + bh) * DK * DV;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -1195,7 +1199,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
   using CL = ConsumerLds<TIn, DK, DV>;
   __shared__ __align__(16) char smem[CL::BYTES];
   const int bh = blockIdx.x / CL::NS, vb = blockIdx.x % CL::NS;
-  consume_chain<TIn, DK, DV, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
+  consume_chain<TIn, DK, DV, false, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
                                     Ring{nullptr, nullptr, nullptr, nullptr, 1}, vb, h0, ht, o, bh / H, bh % H,
                                     T_len, H, nchunks, snap);
 }
@@ -1233,7 +1237,7 @@ struct FusedLds {
   static constexpr size_t BYTES = (A > B ? A : B) + 16;
 };
 
-template <typename TIn, int DK, int DV, bool kUnb>
+template <typename TIn, int DK, int DV, bool kUnb, bool kExt>
 __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                              const TIn* __restrict__ v, const TIn* __restrict__ g,
                                                              const float* __restrict__ gcum,
@@ -1255,7 +1259,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
 
   if (li < nloc * NS) {   // consumer vb of head jh
     const int jh = xcd + 8 * (li / NS), vb = li % NS, bh = head0 + jh;
-    consume_chain<TIn, DK, DV, true>(smem, ring + (size_t)jh * R * Rc::BYTES,
+    consume_chain<TIn, DK, DV, true, kExt>(smem, ring + (size_t)jh * R * Rc::BYTES,
                                      Ring{ready + jh * R, done + jh * NS + vb, err, cxcc + jh * NS + vb, R}, vb, h0,
                                      ht, o, bh / H, bh % H, T_len, H, nchunks, snap, lay);
     return;
@@ -1330,7 +1334,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
                                                          nxt / nloc);
       }
     };
-    if (!produce_chunk<TIn, DK, DV, kUnb>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
+    if (!produce_chunk<TIn, DK, DV, kUnb, kExt>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
                                     ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage, prefetch, lay))
       return;
     pending = it;
@@ -1399,7 +1403,11 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
     const int nh = nbh - head0 < batch ? nbh - head0 : batch;
     const int nctrl = 16 + nh * kRingSlots + 2 * NS * nh;
     hipLaunchKernelGGL(clear_ints_kernel, dim3((nctrl + 255) / 256), dim3(256), 0, st, ctrl, nctrl);
-    auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true> : fused_fwd_kernel<TIn, DK, DV, false>;
+    // three variants: plain, unbounded decay, layer steps / snapshots
+    const bool ext = lay.flags != 0 || lay.og != nullptr || (snap != nullptr && snap_every > 0);
+    if (unb && ext) return hipErrorInvalidValue;
+    auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true, false>
+                    : (ext ? fused_fwd_kernel<TIn, DK, DV, false, true> : fused_fwd_kernel<TIn, DK, DV, false, false>);
     hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q, (const TIn*)k, (const TIn*)v,
                        (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len, H, nchunks, head0, nh, ring,
                        ctrl, kRingSlots, Snap{snap, snap_every, nbh}, lay);
