@@ -327,17 +327,28 @@ def main():
             o_ref, _ = seq.kda_seq(qn, kn, f(v), ogate.gate(f(z), d["A"][heads]), f(beta), d["h0"][:, heads],
                                    nthreads=seq.threads_default())
             o_ref = olayer.output_gate(o_ref, f(og))
-            o_gpu = o_l[:, :, heads].cpu().double().numpy()
+            err = lambda o, ref: float(np.max(np.abs(o[:, :, heads].cpu().double().numpy() - ref))
+                                       / math.sqrt(float(np.mean(ref ** 2))))
+            # the separate steps hand the recurrence g rounded to bf16 (the
+            # decay pass's output type); their oracle takes that g
+            gsep, _ = kda.prepare_decay(z, A, want_gcum=False)
+            o_ref_s, _ = seq.kda_seq(qn, kn, f(v), f(gsep), f(beta), d["h0"][:, heads], nthreads=seq.threads_default())
+            o_ref_s = olayer.output_gate(o_ref_s, f(og))
             l_parity = {"sample": f"o of heads {heads}, all {T} tokens, vs fp64 oracle (gate of z, row "
                                   "normalisation rounded to bf16, output gate)",
-                        "max_err_over_rms": float(np.max(np.abs(o_gpu - o_ref)) / math.sqrt(float(np.mean(o_ref ** 2)))),
-                        "tolerance": 2e-2}
+                        "max_err_over_rms": err(o_l, o_ref), "tolerance": 2e-2,
+                        "separate_steps_max_err_over_rms": err(o_sep, o_ref_s)}
         layer_res = {"workload": "same prefill with z + A (decay gate in the scan), q/k row L2 normalisation in "
                                  "the kernel and a sigmoid output gate og [B,T,H,dv] bf16",
                      "fused_ms": round(ms_fused_l, 4), "separate_steps_ms": round(ms_sep, 4),
-                     "fused_vs_separate_max_err_over_rms": agree, "parity": l_parity}
+                     "fused_vs_separate_max_err_over_rms": agree,
+                     "fused_vs_separate_note": "each path is held to 2e-2 of its own fp64 oracle (the fused kernel "
+                                               "keeps g in fp32, the separate steps round it to bf16), so the two "
+                                               "may differ by up to 4e-2",
+                     "parity": l_parity}
         log(f"layer: fused {ms_fused_l:.3f} ms vs separate steps {ms_sep:.3f} ms; agreement {agree:.2e}"
-            + (f"; parity {l_parity['max_err_over_rms']:.2e}" if l_parity else ""))
+            + (f"; parity {l_parity['max_err_over_rms']:.2e} (separate steps "
+               f"{l_parity['separate_steps_max_err_over_rms']:.2e})" if l_parity else ""))
         del og, o_l, ht_l, o_sep
 
     tok_s = B * T / (ms_step * 1e-3)
