@@ -30,6 +30,9 @@ def _load():
         L = ctypes.c_long
         f.argtypes = [P, P, P, P, P, P, ctypes.c_double, L, L, L, L, L, P, P, ctypes.c_int]
         lib.kda_oracle_threads.restype = ctypes.c_int
+        fb = lib.kda_oracle_seq_bwd
+        fb.restype = ctypes.c_int
+        fb.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_double, L, L, L, L, L, L, P, P, P, P, P, P, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -70,6 +73,38 @@ def kda_seq(q, k, v, g, beta, h0=None, scale=None, nthreads=None):
     if rc != 0:
         raise RuntimeError(f"kda_oracle_seq failed with code {rc}")
     return o, ht
+
+
+def kda_seq_bwd(q, k, v, g, beta, h0, do, dht=None, scale=None, seg: int = 64, nthreads=None):
+    """Gradient of the recurrence (the reverse-mode chain rule through each
+    token's decay, delta step and output, from the last token back).
+
+    do [B,T,H,dv] = dL/do, dht [B,H,dk,dv] = dL/dS_T or None (zero).
+    Returns dict of fp64 arrays dq, dk, dg [B,T,H,dk], dv [B,T,H,dv],
+    dbeta [B,T,H], dh0 [B,H,dk,dv].  States are recomputed from ones kept every
+    `seg` tokens; the arithmetic does not depend on seg.
+    Pinned by tests/test_oracle_pins.py (central finite differences of
+    kda_seq, linearity in (do, dht), the T = 1 closed form)."""
+    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(dk)
+    f64 = lambda x: np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    h0a = None if h0 is None else f64(h0)
+    doa = f64(do)
+    dhta = None if dht is None else f64(dht)
+    assert doa.shape == (B, T, H, dv)
+    out = {"dq": np.empty((B, T, H, dk)), "dk": np.empty((B, T, H, dk)), "dv": np.empty((B, T, H, dv)),
+           "dg": np.empty((B, T, H, dk)), "dbeta": np.empty((B, T, H)), "dh0": np.empty((B, H, dk, dv))}
+    ptr = lambda a: None if a is None else a.ctypes.data
+    nt = threads_default() if nthreads is None else int(nthreads)
+    rc = _load().kda_oracle_seq_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, g.ctypes.data, beta.ctypes.data,
+                                    ptr(h0a), doa.ctypes.data, ptr(dhta), float(scale), B, T, H, dk, dv, int(seg),
+                                    *(out[n].ctypes.data for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0")), nt)
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_seq_bwd failed with code {rc}")
+    return out
 
 
 def kda_decode_ref(q, k, v, g, beta, state, scale=None, nthreads=None):
