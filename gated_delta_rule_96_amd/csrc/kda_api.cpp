@@ -256,3 +256,72 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
 }
 
 }  // extern "C"
+
+namespace {
+
+// Backward workspace, in order: the forward's own workspace, its output and
+// final state (scratch), the states entering chunks 1.., per-chunk records,
+// the state gradient leaving every chunk and dU of every chunk.  Each part
+// starts on a 256-byte boundary.
+struct BwdLayout {
+  size_t fwd, o, ht, snap, rec, dn, du, total;
+};
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int dtype) {
+  const size_t nbh = (size_t)B * H, nch = ((size_t)T + kChunk - 1) / kChunk;
+  BwdLayout L{};
+  size_t off = 0;
+  auto put = [&](size_t bytes) {
+    const size_t at = off;
+    off += up256(bytes);
+    return at;
+  };
+  L.fwd = put(kda_fwd_workspace_bytes(B, T, H, dk, dv, kChunk, dtype));
+  L.o = put((size_t)B * T * H * dv * 4);
+  L.ht = put(nbh * dk * dv * 4);
+  L.snap = put((nch - 1) * nbh * dk * dv * 4);
+  L.rec = put(nch * nbh * kda::bwd_record_words(dk, dv) * 4);
+  L.dn = put(nch * nbh * dk * dv * 4);
+  L.du = put(nch * nbh * kChunk * dv * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || !supported_d(dk) || !supported_d(dv) || chunk != kChunk || !valid_dtype(dtype))
+    return 0;
+  return bwd_layout(B, T, H, dk, dv, dtype).total;
+}
+
+int kda_bwd_chunked(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                    const float* h0, const float* dout, const float* dht, float* dq, float* dk_, float* dv_,
+                    float* dg, float* dbeta, float* dh0, int dtype, int B, int T, int H, int dk, int dv, int chunk,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_fwd(q, k, v, g, nullptr, beta, h0, nullptr, dout, dtype, B, T, H, dk, dv, chunk, workspace, 3);
+  if (st != KDA_OK) return st;
+  if (!g || !dout || !dq || !dk_ || !dv_ || !dg || !dbeta) return KDA_ERR_NULL;
+  for (const void* p : {(const void*)dht, (const void*)dq, (const void*)dk_, (const void*)dv_, (const void*)dg,
+                        (const void*)dbeta, (const void*)dh0})
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  const BwdLayout lay = bwd_layout(B, T, H, dk, dv, dtype);
+  if (workspace_bytes < lay.total) return KDA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const int nch = (T + kChunk - 1) / kChunk;
+  float* snap = nch > 1 ? reinterpret_cast<float*>(ws + lay.snap) : nullptr;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, nullptr, beta, scale, h0,
+                                       reinterpret_cast<float*>(ws + lay.ht), reinterpret_cast<float*>(ws + lay.o), B,
+                                       T, H, dk, dv, ws + lay.fwd, lay.o - lay.fwd, 0, snap, snap ? 1 : 0, nullptr,
+                                       nullptr, 0, s);
+  if (e != hipSuccess) return KDA_ERR_HIP;
+  e = kda::launch_bwd_chunks(dtype == KDA_BF16, q, k, v, g, beta, dout, scale, h0, dht, snap,
+                             reinterpret_cast<float*>(ws + lay.rec), reinterpret_cast<float*>(ws + lay.dn),
+                             reinterpret_cast<float*>(ws + lay.du), B, T, H, dk, dv, dq, dk_, dv_, dg, dbeta, dh0, s);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

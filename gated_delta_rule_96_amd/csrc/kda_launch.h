@@ -44,4 +44,15 @@ hipError_t launch_decode_step(int is_bf16, const void* q, const void* k, const v
                               const void* g, const void* beta, float scale, float* state, float* o,
                               int B, int H, int dk, int dv, hipStream_t stream);
 
+// Backward: fp32 words of one per-chunk record, and the three kernels after
+// a forward pass that kept the state entering every chunk in snap
+// ([chunk - 1][b * H + h][dk][dv]).  rec, dN ([chunk][dk][dv] per head) and
+// dU ([chunk][64][dv] per head) are workspace.
+size_t bwd_record_words(int dk, int dv);
+hipError_t launch_bwd_chunks(int is_bf16, const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, const float* dO, float scale, const float* h0, const float* dht,
+                             const float* snap, float* rec, float* dN, float* dU, int B, int T, int H, int dk,
+                             int dv, float* dq, float* dk_, float* dv_, float* dg, float* dbeta, float* dh0,
+                             hipStream_t st);
+
 }  // namespace kda

@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked_stages.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, I, P]
         L.kda_decode_step.restype = I
         L.kda_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, I, P]
+        L.kda_bwd_workspace_bytes.restype = S
+        L.kda_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.kda_bwd_chunked.argtypes = [P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
         _lib = L
     return _lib
 
@@ -267,6 +270,50 @@ def fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, h0=None, *, gcum=None, scal
     if snaps is not None:
         snaps = snaps[:varlen_snapshots(cu_seqlens, snap_every, chunk)]
     return o, ht, snaps
+
+
+def bwd_workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16, chunk=CHUNK) -> int:
+    dt = _dtype_code(torch.empty(0, dtype=dtype))
+    n = int(lib().kda_bwd_workspace_bytes(B, T, H, dk, dv, chunk, dt))
+    if n == 0:
+        raise KDAError(5, "kda_bwd_workspace_bytes")
+    return n
+
+
+def bwd_chunked(q, k, v, g, beta, h0, do, dht=None, *, scale=None, want_dh0=True, workspace=None, out=None,
+                chunk=CHUNK):
+    """Gradients of kda_fwd_chunked (kda_bwd_chunked): q, k, g [B,T,H,dk] and
+    v [B,T,H,dv], beta [B,T,H] (bf16 or fp32), h0 [B,H,dk,dv] fp32 or None;
+    do = dL/do [B,T,H,dv] fp32, dht = dL/dht [B,H,dk,dv] fp32 or None.
+    Returns a dict of fp32 tensors dq, dk, dv, dg, dbeta and dh0 (None unless
+    want_dh0).  `out` may supply that dict to be filled in place."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+    for name, t, shape in (("do", do, (B, T, H, dv)), ("dht", dht, (B, H, dk, dv)), ("h0", h0, (B, H, dk, dv))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape):
+            raise ValueError(f"{name} must be fp32 {list(shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if workspace is None:
+        n = bwd_workspace_bytes(B, T, H, dk, dv, q.dtype, chunk)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    dev = q.device
+    if out is None:
+        out = {"dq": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+               "dk": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+               "dv": torch.empty((B, T, H, dv), dtype=torch.float32, device=dev),
+               "dg": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+               "dbeta": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+               "dh0": torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None}
+    _check(lib().kda_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(h0), _ptr(do),
+                                 _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                                 _ptr(out["dbeta"]), _ptr(out.get("dh0")), dt, B, T, H, dk, dv, chunk,
+                                 _ptr(workspace), workspace.numel(), _stream(dev)), "kda_bwd_chunked")
+    return out
 
 
 def decode_step(q, k, v, g, beta, state, *, scale=None, out=None):

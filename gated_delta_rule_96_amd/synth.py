@@ -31,7 +31,7 @@ from __future__ import annotations
 
 import numpy as np
 
-TENSOR_ID = {"q": 0, "k": 1, "v": 2, "beta": 3, "z": 4, "A": 5, "h0": 6}
+TENSOR_ID = {"q": 0, "k": 1, "v": 2, "beta": 3, "z": 4, "A": 5, "h0": 6, "do": 7, "dht": 8}
 VARIANTS = ("base", "extreme", "slow")
 
 
@@ -91,6 +91,18 @@ def initial_state(seed: int, B: int, H: int, dk: int, dv: int, std: float = 0.02
         for h in range(H):
             out[b, h] = _normal(seed, 0, "h0", b, h, (dk, dv), std=std)
     return out
+
+
+def output_grads(seed: int, B: int, T: int, H: int, dk: int, dv: int, std_ht: float = 1.0):
+    """Seeded upstream gradients for the backward: do [B,T,H,dv] and dht
+    [B,H,dk,dv], fp32 N(0, 1) (dht N(0, std_ht))."""
+    do = np.empty((B, T, H, dv), np.float32)
+    dht = np.empty((B, H, dk, dv), np.float32)
+    for b in range(B):
+        for h in range(H):
+            do[b, :, h, :] = _normal(seed, 0, "do", b, h, (T, dv))
+            dht[b, h] = _normal(seed, 0, "dht", b, h, (dk, dv), std=std_ht)
+    return do, dht
 
 
 def make_inputs(B: int, T: int, H: int, dk: int, dv: int, seed: int, part: int = 0,

@@ -242,6 +242,33 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
                     const void* beta, float scale, float* state, float* o, int dtype,
                     int B, int H, int dk, int dv, void* stream);
 
+/*
+ * Backward of the chunked prefill: gradients of a loss L with respect to the
+ * inputs of kda_fwd_chunked, given dout = dL/do and dht = dL/dht (Kimi K3
+ * technical report summary, "Method", section 2.1: the chunkwise form; its
+ * gradient by the reverse-mode chain rule, chunk by chunk from the last).
+ *
+ * Inputs as kda_fwd_chunked (q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H];
+ * dtype KDA_F32 or KDA_BF16; g in [-5, 0), the bounded gate) plus dout
+ * [B,T,H,dv] fp32 and dht [B,H,dk,dv] fp32 (NULL = no gradient reaches the
+ * final state); h0 NULL = zero initial state.
+ * Outputs, all fp32, overwritten: dq, dk, dg [B,T,H,dk]; dv [B,T,H,dv];
+ * dbeta [B,T,H]; dh0 [B,H,dk,dv] (NULL = not written).  dg is the gradient
+ * with respect to the per-token decay g (apply the gate's own derivative
+ * for z and A).
+ * The call recomputes the forward pass (keeping the state entering every
+ * chunk) inside `workspace` of at least kda_bwd_workspace_bytes bytes
+ * (256-byte aligned, owned by the caller, contents undefined afterwards);
+ * it allocates nothing and returns without synchronising.
+ * Errors: as kda_fwd_chunked, KDA_ERR_NULL also for a NULL dout or output.
+ */
+size_t kda_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
+int kda_bwd_chunked(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                    float scale, const float* h0, const float* dout, const float* dht, float* dq,
+                    float* dk_, float* dv_, float* dg, float* dbeta, float* dh0, int dtype, int B,
+                    int T, int H, int dk, int dv, int chunk, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -157,3 +157,33 @@ def test_layer_entry_validation():
     assert L.kda_fwd_chunked_layer(*bad) == 4
     bad = list(a); bad[20] = 1024
     assert L.kda_fwd_chunked_layer(*bad) == 6
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.1, h0=None, do=FAKE, dht=None, dq=FAKE, dk_=FAKE,
+             dv_=FAKE, dg=FAKE, dbeta=FAKE, dh0=None, dtype=1, B=1, T=200, H=2, dk=128, dv=128, chunk=64, ws=FAKE,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return kda.lib().kda_bwd_chunked(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(g=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dbeta=None), 1),
+    (dict(T=0), 2), (dict(B=0), 2), (dict(dtype=5), 3),
+    (dict(dg=FAKE + 4), 4), (dict(dht=FAKE + 8), 4), (dict(dh0=FAKE + 4), 4), (dict(ws=FAKE + 64), 4),
+    (dict(dk=32), 5), (dict(chunk=16), 5),
+    (dict(ws=None), 6), (dict(wsb=4096), 6),
+])
+def test_bwd_validation(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_workspace_bytes():
+    L = kda.lib()
+    n1 = L.kda_bwd_workspace_bytes(1, 64, 2, 128, 128, 64, 1)
+    n2 = L.kda_bwd_workspace_bytes(1, 6400, 2, 128, 128, 64, 1)
+    assert n1 > 0 and n1 % 256 == 0 and n2 > n1
+    # per chunk and head the backward keeps a state, its gradient and a record
+    assert n2 - n1 >= 99 * 2 * (3 * 128 * 128 * 4)
+    assert L.kda_bwd_workspace_bytes(1, 64, 2, 96, 128, 64, 1) == 0
+    assert L.kda_bwd_workspace_bytes(1, 64, 2, 128, 128, 32, 1) == 0
