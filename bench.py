@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 METRIC = "KDA chunked prefill tokens/s + % bf16 MFMA peak (T=64K); decode % HBM peak"
 
 # prefill workload
@@ -75,6 +76,18 @@ def measured_traffic():
         return None
 
 
+def bwd_alg_counts(B, T, H, dk, dv, C=64):
+    """Algorithmic flop of one backward call (chunkwise gradient, lower
+    triangles only, excluding the forward recompute): per token-head
+    14 dk dv + 8.5 C dk + 5.5 C dv + C^2/3; HBM bytes: bf16 q, k, v, g, beta
+    and fp32 do read, fp32 dq, dk, dv, dg, dbeta written, h0/dht read and dh0
+    written."""
+    th = B * T * H
+    flop = th * (14 * dk * dv + 8.5 * C * dk + 5.5 * C * dv + C * C / 3.0)
+    bytes_ = th * (2 * (3 * dk + dv) + 2 + 4 * dv + 4 * (3 * dk + dv) + 4) + B * H * 3 * 4 * dk * dv
+    return flop, bytes_
+
+
 def decode_alg_bytes(B, H, dk, dv):
     """fp32 state read + written, bf16 q, k, g, v, beta read, fp32 o written."""
     return B * H * (2 * 4 * dk * dv + 2 * (3 * dk + dv) + 2 + 4 * dv)
@@ -91,6 +104,7 @@ def main():
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards by "
@@ -351,6 +365,64 @@ def main():
                f"{l_parity['separate_steps_max_err_over_rms']:.2e})" if l_parity else ""))
         del og, o_l, ht_l, o_sep
 
+    # ---------------- backward of the same prefill (forward recompute included)
+    bwd = None
+    if not args.no_backward:
+        do_h, dht_h = synth.output_grads(4, B, T, H, DK, DV)
+        do_d, dht_d = torch.from_numpy(do_h).to(dev), torch.from_numpy(dht_h).to(dev)
+        ws_b = torch.empty(kda.bwd_workspace_bytes(B, T, H, DK, DV, torch.bfloat16), dtype=torch.uint8, device=dev)
+        grads = kda.bwd_chunked(q, k, v, g, beta, h0, do_d, dht_d, workspace=ws_b)
+
+        def bwd_call():
+            kda.bwd_chunked(q, k, v, g, beta, h0, do_d, dht_d, workspace=ws_b, out=grads)
+
+        bwd_call()
+        torch.cuda.synchronize()
+        nb = max(3, args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(nb):
+            bwd_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_b = e0.elapsed_time(e1) / nb
+        bflop, bbytes = bwd_alg_counts(B, T, H, DK, DV)
+        fflop, _ = prefill_alg_counts(B, T, H, DK, DV)
+        b_tf = bflop / (ms_b * 1e-3) / 1e12
+        # lower bound of the call: backward flops on fp32 MFMA, the recompute on bf16 MFMA
+        b_bound = max(bflop / (FP32_PEAK_TFLOPS * 1e12) + fflop / (BF16_PEAK_TFLOPS * 1e12),
+                      bbytes / (HBM_PEAK_GBS * 1e9)) * 1e3
+        b_parity = None
+        if not args.no_cpu_baseline:
+            from oracle import seq
+
+            heads = [3, 28]
+            f = lambda t: t[:, :, heads].float().cpu().numpy()
+            gb = g[:, :, heads].float().cpu().numpy()
+            ref = seq.kda_seq_bwd(f(q), f(k), f(v), gb, f(beta), d["h0"][:, heads], do_h[:, :, heads],
+                                  dht_h[:, heads], nthreads=2)
+            worst = {}
+            for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+                x = (grads[n][:, heads] if n == "dh0" else grads[n][:, :, heads]).double().cpu().numpy()
+                r = ref[n]
+                rms = math.sqrt(float(np.mean(r * r)))
+                worst[n] = float(np.max(np.abs(x - r) / (rms + np.abs(r))))
+            b_parity = {"sample": f"gradients of heads {heads}, all {T} tokens, vs the fp64 oracle gradient",
+                        "max_elementwise_err": worst, "rule": "|x - ref| <= tau (rms(ref) + |ref|)",
+                        "tolerance": 2e-2}
+        bwd = {"workload": f"gradients of the same prefill (dq, dk, dv, dg, dbeta, dh0; fp32 out) given seeded "
+                           f"do [B,T,H,dv] and dht, kda_bwd_chunked (recomputes the forward)",
+               "ms_per_call": round(ms_b, 4), "tokens_per_s": round(B * T / (ms_b * 1e-3), 1),
+               "alg_flop_per_call": int(bflop), "recompute_flop_per_call": int(fflop),
+               "roofline": {"bound": "mfma", "achieved": round(b_tf, 2), "peak": FP32_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(b_tf / FP32_PEAK_TFLOPS, 4), "traffic": None,
+                            "note": "backward flops (fp32 MFMA) over the whole call's time"},
+               "binding_roofline_frac": round(b_bound / ms_b, 4),
+               "parity": b_parity}
+        log(f"backward: {ms_b:.3f} ms per call, {b_tf:.1f} TFLOP/s fp32 ({b_tf / FP32_PEAK_TFLOPS:.1%})"
+            + (f"; parity {max(b_parity['max_elementwise_err'].values()):.2e}" if b_parity else ""))
+        del ws_b, grads, do_d, dht_d
+
     tok_s = B * T / (ms_step * 1e-3)
     gbs = abytes / (ms_step * 1e-3) / 1e9
     tflops = flop / (ms_step * 1e-3) / 1e12
@@ -449,6 +521,7 @@ def main():
         "unbounded_decay_ablation": ablation,
         "varlen_snapshots": varlen,
         "layer_prologue_epilogue": layer_res,
+        "backward": bwd,
         "parity": parity,
         "cpu_baseline": cpu,
     }

@@ -25,11 +25,11 @@ import sqlite3
 import sys
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-SOURCES = ("kda_chunk.hip", "kda_device.h", "kda_launch.h")
+SOURCES = ("kda_chunk.hip", "kda_device.h")
 
 
 def source_sha256() -> str:
-    """sha256 over the prefill kernel sources (the code the counters describe)."""
+    """sha256 over the fused prefill kernel's sources (the code the counters describe)."""
     h = hashlib.sha256()
     for name in SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
