@@ -125,6 +125,27 @@ struct Rec {
 template <typename T>
 __device__ __forceinline__ float ldf(const T* p, size_t i) { return to_f32(p[i]); }
 
+// 8 (4) consecutive elements as fp32, one or two 16-byte loads (8-byte for 4 bf16)
+__device__ __forceinline__ void ld8(const float* p, float* o) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[i] = a[i];
+    o[4 + i] = b[i];
+  }
+}
+__device__ __forceinline__ void ld8(const bf16* p, float* o) {
+  const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
+}
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 ld4(const bf16* p) { return widen4(*(const bf16x4*)p); }
+__device__ __forceinline__ void st8(float* p, const float* v) {
+  *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+  *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
 // ---------------------------------------------------------------------------
 // Per-chunk preparation.
 template <typename TIn, int DK, int DV>
@@ -167,12 +188,30 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   auto gam_minus = [&](int a, int cc) { return (float)(sGam[cc] - sRef[a * DK + cc]); };
   auto ref_plus = [&](int a, int cc, float gl) { return (float)(sRef[a * DK + cc] + (double)gl); };
 
-  // decay scan (fp64) per channel, beta
+  constexpr int V8 = DK / 8;
+  // stage g, k and q with 16-byte loads (rows past the end are zero)
+  float* sKe = sm + LD::R1;
+  float* sQe = sm + LD::R2;
+  float* sKF = sm + LD::R3;
+  for (int e = tid; e < kCh * V8; e += 256) {
+    const int r = e / V8, c0 = (e % V8) * 8;
+    float x[8] = {}, kk[8] = {}, qq[8] = {};
+    if (r < L) {
+      ld8(g + row(r) * DK + c0, x);
+      ld8(k + row(r) * DK + c0, kk);
+      ld8(q + row(r) * DK + c0, qq);
+    }
+    st8(sGl + r * PK + c0, x);
+    st8(sKe + r * PK + c0, kk);
+    st8(sQe + r * PK + c0, qq);
+  }
+  if (tid < kCh) sBeta[tid] = tid < L ? ldf(beta, row(tid)) : 0.f;
+  __syncthreads();
+  // decay scan (fp64) per channel, in place: Gamma - ref of the row's block
   if (tid < DK) {
     double acc = 0.0, ref[4] = {0.0, 0.0, 0.0, 0.0};
     for (int r = 0; r < kCh; ++r) {
-      const double x = r < L ? (double)ldf(g, row(r) * DK + tid) : 0.0;
-      acc += x;
+      acc += (double)sGl[r * PK + tid];
       sGl[r * PK + tid] = (float)(acc - ref[r >> 4]);
       if ((r & 15) == 15 && r < kCh - 1) ref[(r + 1) >> 4] = acc;
     }
@@ -180,18 +219,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
     for (int a = 0; a < 4; ++a) sRef[a * DK + tid] = ref[a];
     sGam[tid] = acc;
   }
-  if (tid < kCh) sBeta[tid] = tid < L ? ldf(beta, row(tid)) : 0.f;
   __syncthreads();
-
-  // Ke = k e^(Gamma - ref), Qe = q e^(Gamma - ref)
-  float* sKe = sm + LD::R1;
-  float* sQe = sm + LD::R2;
-  float* sKF = sm + LD::R3;
-  for (int e = tid; e < kCh * DK; e += 256) {
-    const int r = e / DK, cc = e % DK;
-    const float f = ex(sGl[r * PK + cc]);
-    sKe[r * PK + cc] = r < L ? ldf(k, row(r) * DK + cc) * f : 0.f;
-    sQe[r * PK + cc] = r < L ? ldf(q, row(r) * DK + cc) * f : 0.f;
+  // Ke = k e^(Gamma - ref), Qe = q e^(Gamma - ref), in place
+  for (int e = tid; e < kCh * V8; e += 256) {
+    const int r = e / V8, c0 = (e % V8) * 8;
+    float gl[8], kk[8], qq[8];
+    ld8(sGl + r * PK + c0, gl);
+    ld8(sKe + r * PK + c0, kk);
+    ld8(sQe + r * PK + c0, qq);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float f = ex(gl[i]);
+      kk[i] *= f;
+      qq[i] *= f;
+    }
+    st8(sKe + r * PK + c0, kk);
+    st8(sQe + r * PK + c0, qq);
   }
 
   // Gram tiles: G(a, bb) = sum_c Ke[r][c] KF_a[s][c] (bb <= a), same for M with Qe;
@@ -200,10 +243,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     __syncthreads();
-    for (int e = tid; e < 16 * (a + 1) * DK; e += 256) {
-      const int s = e / DK, cc = e % DK, bs = s >> 4;
-      const float d = (a == bs) ? 0.f : dref(a, bs, cc);
-      sKF[s * PK + cc] = s < L ? ldf(k, row(s) * DK + cc) * ex(d - sGl[s * PK + cc]) : 0.f;
+    for (int e = tid; e < 16 * (a + 1) * V8; e += 256) {
+      const int s = e / V8, c0 = (e % V8) * 8, bs = s >> 4;
+      float kk[8] = {}, gl[8];
+      if (s < L) ld8(k + row(s) * DK + c0, kk);
+      ld8(sGl + s * PK + c0, gl);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kk[i] *= ex((a == bs ? 0.f : dref(a, bs, c0 + i)) - gl[i]);
+      st8(sKF + s * PK + c0, kk);
     }
     __syncthreads();
 #pragma unroll
@@ -269,9 +316,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
       sLi[ri * kP64 + 16 * a + j] = x[i];
     }
   } else {
-    for (int e = tid - 64; e < kCh * DK; e += 192) {
-      const int s = e / DK, cc = e % DK;
-      sKbT[cc * kP64 + s] = s < L ? sBeta[s] * ldf(k, row(s) * DK + cc) * ex(ref_plus(s >> 4, cc, sGl[s * PK + cc])) : 0.f;
+    for (int e = tid - 64; e < kCh * V8; e += 192) {
+      const int s = e / V8, c0 = (e % V8) * 8;
+      float kk[8] = {}, gl[8];
+      if (s < L) ld8(k + row(s) * DK + c0, kk);
+      ld8(sGl + s * PK + c0, gl);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sKbT[(c0 + i) * kP64 + s] = sBeta[s] * kk[i] * ex(ref_plus(s >> 4, c0 + i, gl[i]));
     }
   }
   __syncthreads();
@@ -305,9 +356,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
     wt[T_] = mm_nt(zero4(), sLi + 16 * w * kP64, kP64, sKbT + 16 * T_ * kP64, kP64, 0, 16 * (w + 1));
   // dO^T scaled (R3; the inverse's scratch is no longer read)
   float* sdOT = sm + LD::R3;
-  for (int e = tid; e < kCh * DV; e += 256) {
-    const int r = e / DV, j = e % DV;
-    sdOT[j * kP64 + r] = r < L ? scale * dO[row(r) * DV + j] : 0.f;
+  for (int e = tid; e < kCh * DV / 8; e += 256) {
+    const int r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
+    float x[8] = {};
+    if (r < L) ld8(dO + row(r) * DV + j0, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sdOT[(j0 + i) * kP64 + r] = scale * x[i];
   }
   __syncthreads();
   float* sWT = sm + LD::R2;
@@ -324,19 +378,29 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
 #pragma unroll
   for (int J = 0; J < NV; ++J) pt[J] = mm_nt(zero4(), sMT + 16 * w * kP64, kP64, sdOT + 16 * J * kP64, kP64, 16 * w, kCh);
   // Kh to the record; gather Gamma offsets for Qb (R0 is rewritten next)
-  for (int e = tid; e < kCh * DK; e += 256) {
-    const int r = e / DK, cc = e % DK;
-    const float gl = sGl[r * PK + cc];
-    out[RC::GLOC + e] = gl;
-    out[RC::KH + e] = r < L ? ldf(k, row(r) * DK + cc) * ex(gam_minus(r >> 4, cc) - gl) : 0.f;
+  for (int e = tid; e < kCh * V8; e += 256) {
+    const int r = e / V8, c0 = (e % V8) * 8;
+    float kk[8] = {}, gl[8];
+    if (r < L) ld8(k + row(r) * DK + c0, kk);
+    ld8(sGl + r * PK + c0, gl);
+    st8(out + RC::GLOC + r * DK + c0, gl);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kk[i] *= ex(gam_minus(r >> 4, c0 + i) - gl[i]);
+    st8(out + RC::KH + r * DK + c0, kk);
   }
   for (int e = tid; e < 10 * DK; e += 256) out[RC::REF + e] = sm[LD::REF + e];   // fp64 refs and gamma
-  constexpr int PER = kCh * DK / 256;
-  float qb[PER];
+  constexpr int PER = kCh * V8 / 256;   // groups of 8 per thread
+  float qb[PER][8];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = tid + 256 * i, r = e / DK, cc = e % DK;
-    qb[i] = r < L ? ldf(q, row(r) * DK + cc) * ex(ref_plus(r >> 4, cc, sGl[r * PK + cc])) : 0.f;
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid + 256 * j, r = e / V8, c0 = (e % V8) * 8;
+    float gl[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qb[j][i] = 0.f;
+    if (r < L) ld8(q + row(r) * DK + c0, qb[j]);
+    ld8(sGl + r * PK + c0, gl);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qb[j][i] *= ex(ref_plus(r >> 4, c0 + i, gl[i]));
   }
   __syncthreads();
   float* sQbT = sm + LD::R0;
@@ -350,9 +414,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
     }
   }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = tid + 256 * i, r = e / DK, cc = e % DK;
-    sQbT[cc * kP64 + r] = qb[i];
+  for (int j = 0; j < PER; ++j) {
+    const int e = tid + 256 * j, r = e / V8, c0 = (e % V8) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sQbT[(c0 + i) * kP64 + r] = qb[j][i];
   }
   __syncthreads();
   // C = scale Qb^T dO   [DK][DV] (dO^T carries the scale); wave w owns tiles w, w+4, ...
@@ -517,26 +582,26 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   }
   // dU^T (R3)
   float* sdUT = sm + LD::R3;
-  for (int e = tid; e < kCh * DV; e += 256) {
-    const int r = e / DV, j = e % DV;
-    sdUT[j * kP64 + r] = dUb[((size_t)n * kCh + r) * DV + j];
+  for (int e = tid; e < kCh * DV / 8; e += 256) {
+    const int r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
+    float x[8];
+    ld8(dUb + ((size_t)n * kCh + r) * DV + j0, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sdUT[(j0 + i) * kP64 + r] = x[i];
   }
   // this wave's rows of Kb and scale * dO as left operands
   const int ra = 16 * w + cl;   // operand row of this lane
   f32x4 kba[NT], doa[NV];
 #pragma unroll
   for (int J = 0; J < NT; ++J) {
+    const int c0 = 16 * J + 4 * g4;
+    const f32x4 kk = ra < L ? ld4(k + row(ra) * DK + c0) : zero4();
+    const f32x4 gl4 = ld4(rc + RC::GLOC + ra * DK + c0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cc = 16 * J + 4 * g4 + i;
-      kba[J][i] = ra < L ? ldf(k, row(ra) * DK + cc) * ex(ref_plus(w, cc, rc[RC::GLOC + ra * DK + cc])) : 0.f;
-    }
+    for (int i = 0; i < 4; ++i) kba[J][i] = kk[i] * ex(ref_plus(w, c0 + i, gl4[i]));
   }
 #pragma unroll
-  for (int J = 0; J < NV; ++J) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) doa[J][i] = ra < L ? scale * dO[row(ra) * DV + 16 * J + 4 * g4 + i] : 0.f;
-  }
+  for (int J = 0; J < NV; ++J) doa[J] = ra < L ? scale * ld4(dO + row(ra) * DV + 16 * J + 4 * g4) : zero4();
   __syncthreads();
 
   // e^gamma sum_j N S per key row (threads: row = tid / 2, half of the columns)
@@ -717,16 +782,28 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     __syncthreads();
-    for (int e = tid; e < 16 * (a + 1) * DK; e += 256) {
-      const int s = e / DK, cc = e % DK, bs = s >> 4;
-      const float d = (a == bs) ? 0.f : dref(a, bs, cc);
-      sKFT[cc * kP64 + s] = s < L ? ldf(k, row(s) * DK + cc) * ex(d - rc[RC::GLOC + (size_t)s * DK + cc]) : 0.f;
+    for (int e = tid; e < 16 * (a + 1) * (DK / 8); e += 256) {
+      const int s = e / (DK / 8), c0 = (e % (DK / 8)) * 8, bs = s >> 4;
+      float kk[8] = {}, gl[8];
+      if (s < L) ld8(k + row(s) * DK + c0, kk);
+      ld8(rc + RC::GLOC + (size_t)s * DK + c0, gl);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sKFT[(c0 + i) * kP64 + s] = kk[i] * ex((a == bs ? 0.f : dref(a, bs, c0 + i)) - gl[i]);
     }
-    for (int e = tid; e < 16 * DK; e += 256) {
-      const int r = 16 * a + e / DK, cc = e % DK;
-      const float f = ex(rc[RC::GLOC + (size_t)r * DK + cc]);
-      sKeT[cc * 20 + (r - 16 * a)] = r < L ? ldf(k, row(r) * DK + cc) * f : 0.f;
-      sQeT[cc * 20 + (r - 16 * a)] = r < L ? ldf(q, row(r) * DK + cc) * f : 0.f;
+    for (int e = tid; e < 16 * (DK / 8); e += 256) {
+      const int rl = e / (DK / 8), r = 16 * a + rl, c0 = (e % (DK / 8)) * 8;
+      float kk[8] = {}, qq[8] = {}, gl[8];
+      if (r < L) {
+        ld8(k + row(r) * DK + c0, kk);
+        ld8(q + row(r) * DK + c0, qq);
+      }
+      ld8(rc + RC::GLOC + (size_t)r * DK + c0, gl);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float f = ex(gl[i]);
+        sKeT[(c0 + i) * 20 + rl] = kk[i] * f;
+        sQeT[(c0 + i) * 20 + rl] = qq[i] * f;
+      }
     }
     __syncthreads();
     if (w == a) {   // row side: rows of block a
