@@ -465,15 +465,61 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const float* __restrict_
     const int cc = e / 16, j = e % 16;
     sNT[j * PK + cc] = dht ? dht[((size_t)bh * DK + cc) * DV + j0 + j] : 0.f;
   }
+  // Chunk c - 1's record slices are loaded into registers while chunk c is
+  // computed, so the step does not wait for a memory round trip: Kh and W^T
+  // (16-byte pieces of the whole matrices), this lane's P and C values and
+  // the fp64 gamma of its key rows.
+  constexpr int NKW = kCh * DK / 4 / 256;   // 16-byte pieces per thread
+  constexpr int NM = DK / 64;               // key-row tiles per wave
+  static_assert(NKW * 256 * 4 == kCh * DK && NM * 64 == DK, "record slices split evenly over the threads");
+  f32x4 pkh[NKW], pwt[NKW];
+  float pp[4], pcv[NM][4];
+  double pg[NM][4];
+  auto load_rec = [&](int c) {
+    const float* rc = rec + ((size_t)bh * nch + c) * RC::WORDS;
+#pragma unroll
+    for (int i = 0; i < NKW; ++i) {
+      const int e = tid + 256 * i;
+      pkh[i] = *(const f32x4*)(rc + RC::KH + 4 * e);
+      pwt[i] = *(const f32x4*)(rc + RC::WT + 4 * e);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pp[i] = rc[RC::P + (size_t)(16 * w + r0 + i) * DV + j0 + cl];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int cc = 16 * (w + 4 * m) + r0 + i;
+        pcv[m][i] = rc[RC::C + (size_t)cc * DV + j0 + cl];
+        pg[m][i] = reinterpret_cast<const double*>(rc + RC::GAM)[cc];
+      }
+  };
+  load_rec(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
     const size_t n = (size_t)bh * nch + c;
-    const float* rc = rec + n * RC::WORDS;
-    for (int e = tid; e < kCh * DK / 4; e += 256) {
+    // the previous step's readers of Kh and W^T passed its last barrier
+#pragma unroll
+    for (int i = 0; i < NKW; ++i) {
+      const int e = tid + 256 * i;
       const int r = (4 * e) / DK, cc = (4 * e) % DK;
-      *(f32x4*)(sKh + r * PK + cc) = *(const f32x4*)(rc + RC::KH + 4 * e);
+      *(f32x4*)(sKh + r * PK + cc) = pkh[i];
       const int cw = (4 * e) / kCh, rw = (4 * e) % kCh;
-      *(f32x4*)(sWT + cw * kP64 + rw) = *(const f32x4*)(rc + RC::WT + 4 * e);
+      *(f32x4*)(sWT + cw * kP64 + rw) = pwt[i];
     }
+    f32x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = pp[i];
+    f32x4 base[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) base[m][i] = pcv[m][i];
+    float eg[NM][4];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) eg[m][i] = ex((float)pg[m][i]);
+    if (c > 0) load_rec(c - 1);
     __syncthreads();   // also orders the previous iteration's N^T writes
     // the gradient leaving chunk c
     for (int e = tid; e < 16 * DK; e += 256) {
@@ -481,32 +527,24 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(const float* __restrict_
       dN[(n * DK + cc) * DV + j0 + j] = sNT[j * PK + cc];
     }
     // dU rows of block w: P + Kh N
-    f32x4 x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = rc[RC::P + (size_t)(16 * w + r0 + i) * DV + j0 + cl];
     x = mm_nt(x, sKh + 16 * w * PK, PK, sNT, PK, 0, DK);
     st_tr(sXT + 16 * w, kP64, x);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dU[(n * kCh + 16 * w + r0 + i) * DV + j0 + cl] = x[i];
     __syncthreads();
     // N <- e^gamma N + C - W^T dU, rows of tiles w, w+4
-    f32x4 nn[DK / 64];
+    f32x4 nn[NM];
 #pragma unroll
-    for (int m = 0; m < DK / 64; ++m) {
+    for (int m = 0; m < NM; ++m) {
       const int Tc = w + 4 * m;
       const f32x4 old = *(const f32x4*)(sNT + cl * PK + 16 * Tc + r0);
-      f32x4 base;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int cc = 16 * Tc + r0 + i;
-        base[i] = ex((float)reinterpret_cast<const double*>(rc + RC::GAM)[cc]) * old[i] +
-                  rc[RC::C + (size_t)cc * DV + j0 + cl];
-      }
-      nn[m] = base - mm_nt(zero4(), sWT + 16 * Tc * kP64, kP64, sXT, kP64, 0, kCh);
+      for (int i = 0; i < 4; ++i) base[m][i] += eg[m][i] * old[i];
+      nn[m] = base[m] - mm_nt(zero4(), sWT + 16 * Tc * kP64, kP64, sXT, kP64, 0, kCh);
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < DK / 64; ++m) st_tr(sNT + 16 * (w + 4 * m), PK, nn[m]);
+    for (int m = 0; m < NM; ++m) st_tr(sNT + 16 * (w + 4 * m), PK, nn[m]);
   }
   __syncthreads();
   if (dh0)
