@@ -605,27 +605,45 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   float* sDgs = sm + LD::DGS;
   float* sS = sm + LD::R0;     // [DK][PV] over R0..R1
   float* sLi = sm + LD::RL;    // [64][68]
-  for (int e = tid; e < 10 * DK; e += 256) sm[LD::REF + e] = rc[RC::REF + e];
-  if (tid < kCh) {
-    sBeta[tid] = tid < L ? ldf(beta, row(tid)) : 0.f;
-    sDb[tid] = 0.f;
-  }
-  for (int e = tid; e < DK * DV / 4; e += 256) {
-    const int cc = (4 * e) / DV, j = (4 * e) % DV;
-    *(f32x4*)(sS + cc * PV + j) = S ? *(const f32x4*)(S + 4 * e) : zero4();
-  }
-  for (int e = tid; e < kCh * kCh / 4; e += 256) {
-    const int r = (4 * e) / kCh, s = (4 * e) % kCh;
-    *(f32x4*)(sLi + r * kP64 + s) = *(const f32x4*)(rc + RC::LINV + 4 * e);
-  }
-  // dU^T (R3)
-  float* sdUT = sm + LD::R3;
-  for (int e = tid; e < kCh * DV / 8; e += 256) {
-    const int r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
-    float x[8];
-    ld8(dUb + ((size_t)n * kCh + r) * DV + j0, x);
+  // The chunk's state S, L^-1 and dU^T go to LDS; every load is issued
+  // before the first LDS write, so the work-group waits for one round trip
+  // (its 4 waves cannot hide a chain of them).
+  constexpr int NSS = DK * DV / 4 / 256, NLI = kCh * kCh / 4 / 256, NDU = kCh * DV / 8 / 256;
+  static_assert(NSS * 1024 == DK * DV && NLI * 1024 == kCh * kCh && NDU * 2048 == kCh * DV, "pieces per thread");
+  float* sdUT = sm + LD::R3;   // dU^T
+  {
+    f32x4 sv[NSS], li[NLI];
+    float du[NDU][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sdUT[(j0 + i) * kP64 + r] = x[i];
+    for (int i = 0; i < NSS; ++i) sv[i] = S ? *(const f32x4*)(S + 4 * (tid + 256 * i)) : zero4();
+#pragma unroll
+    for (int i = 0; i < NLI; ++i) li[i] = *(const f32x4*)(rc + RC::LINV + 4 * (tid + 256 * i));
+#pragma unroll
+    for (int i = 0; i < NDU; ++i) {
+      const int e = tid + 256 * i, r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
+      ld8(dUb + ((size_t)n * kCh + r) * DV + j0, du[i]);
+    }
+    for (int e = tid; e < 10 * DK; e += 256) sm[LD::REF + e] = rc[RC::REF + e];
+    if (tid < kCh) {
+      sBeta[tid] = tid < L ? ldf(beta, row(tid)) : 0.f;
+      sDb[tid] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NSS; ++i) {
+      const int e = tid + 256 * i, cc = (4 * e) / DV, j = (4 * e) % DV;
+      *(f32x4*)(sS + cc * PV + j) = sv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NLI; ++i) {
+      const int e = tid + 256 * i, r = (4 * e) / kCh, s = (4 * e) % kCh;
+      *(f32x4*)(sLi + r * kP64 + s) = li[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NDU; ++i) {
+      const int e = tid + 256 * i, r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) sdUT[(j0 + x) * kP64 + r] = du[i][x];
+    }
   }
   // this wave's rows of Kb and scale * dO as left operands
   const int ra = 16 * w + cl;   // operand row of this lane
@@ -646,13 +664,30 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   {
     const int cc = tid >> 1, half = tid & 1;
     float s = 0.f;
-    if (cc < DK)
-      for (int j = half * (DV / 2); j < (half + 1) * (DV / 2); ++j) s += Nn[(size_t)cc * DV + j] * sS[cc * PV + j];
+    if (cc < DK) {
+      const float* np = Nn + (size_t)cc * DV + half * (DV / 2);
+      f32x4 nv[DV / 8];
+#pragma unroll
+      for (int i = 0; i < DV / 8; ++i) nv[i] = *(const f32x4*)(np + 4 * i);
+#pragma unroll
+      for (int i = 0; i < DV / 8; ++i) {
+        const f32x4 sv = *(const f32x4*)(sS + cc * PV + half * (DV / 2) + 4 * i);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) s += nv[i][x] * sv[x];
+      }
+    }
     s += __shfl_xor(s, 1);
     if (cc < DK && half == 0) sDgs[cc] = ex((float)sGam[cc]) * s;
   }
   // R = V - Kb S, dQb = scale dO S^T (rows of block w)
   f32x4 R[NV], dQb[NT];
+#pragma unroll
+  for (int J = 0; J < NV; ++J)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + r0 + i;
+      R[J][i] = r < L ? ldf(v, row(r) * DV + 16 * J + cl) : 0.f;
+    }
 #pragma unroll
   for (int J = 0; J < NV; ++J) {
     f32x4 acc = zero4();
@@ -662,11 +697,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       const float* bk = b0 + 16 * K * PV;
       acc = mfma4(kba[K], f32x4{bk[0], bk[PV], bk[2 * PV], bk[3 * PV]}, acc);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + r0 + i;
-      R[J][i] = (r < L ? ldf(v, row(r) * DV + 16 * J + cl) : 0.f) - acc[i];
-    }
+    R[J] -= acc;
   }
 #pragma unroll
   for (int K = 0; K < NT; ++K) {
@@ -820,27 +851,46 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     __syncthreads();
-    for (int e = tid; e < 16 * (a + 1) * (DK / 8); e += 256) {
-      const int s = e / (DK / 8), c0 = (e % (DK / 8)) * 8, bs = s >> 4;
-      float kk[8] = {}, gl[8];
-      if (s < L) ld8(k + row(s) * DK + c0, kk);
-      ld8(rc + RC::GLOC + (size_t)s * DK + c0, gl);
+    // Pieces e = tid + 256 j (row s = e / (DK / 8), 8 channels from c0) with
+    // s < 16 (a + 1): k and the decay offsets, plus q for the rows of block
+    // a (piece jq); all loads are issued before the LDS writes.
+    {
+      constexpr int NPC = kCh * (DK / 8) / 256;
+      static_assert(NPC * 256 == kCh * (DK / 8), "pieces per thread");
+      const int lo = 16 * a * (DK / 8), hi = lo + 16 * (DK / 8), jq = lo / 256;
+      float kk[NPC][8], gv[NPC][8], qq[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sKFT[(c0 + i) * kP64 + s] = kk[i] * ex((a == bs ? 0.f : dref(a, bs, c0 + i)) - gl[i]);
-    }
-    for (int e = tid; e < 16 * (DK / 8); e += 256) {
-      const int rl = e / (DK / 8), r = 16 * a + rl, c0 = (e % (DK / 8)) * 8;
-      float kk[8] = {}, qq[8] = {}, gl[8];
-      if (r < L) {
-        ld8(k + row(r) * DK + c0, kk);
-        ld8(q + row(r) * DK + c0, qq);
+      for (int j = 0; j < NPC; ++j) {
+        const int e = tid + 256 * j, s = e / (DK / 8), c0 = (e % (DK / 8)) * 8;
+        if (e < hi) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) kk[j][i] = 0.f;
+          if (s < L) ld8(k + row(s) * DK + c0, kk[j]);
+          ld8(rc + RC::GLOC + (size_t)s * DK + c0, gv[j]);
+          if (j == jq && e >= lo) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qq[i] = 0.f;
+            if (s < L) ld8(q + row(s) * DK + c0, qq);
+          }
+        }
       }
-      ld8(rc + RC::GLOC + (size_t)r * DK + c0, gl);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float f = ex(gl[i]);
-        sKeT[(c0 + i) * 20 + rl] = kk[i] * f;
-        sQeT[(c0 + i) * 20 + rl] = qq[i] * f;
+      for (int j = 0; j < NPC; ++j) {
+        const int e = tid + 256 * j, s = e / (DK / 8), c0 = (e % (DK / 8)) * 8, bs = s >> 4;
+        if (e < hi) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            sKFT[(c0 + i) * kP64 + s] = kk[j][i] * ex((a == bs ? 0.f : dref(a, bs, c0 + i)) - gv[j][i]);
+          if (j == jq && e >= lo) {   // k_r e^(Gamma_r - ref_a), q_r e^(Gamma_r - ref_a), r in block a
+            const int rl = s - 16 * a;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float f = ex(gv[j][i]);
+              sKeT[(c0 + i) * 20 + rl] = kk[j][i] * f;
+              sQeT[(c0 + i) * 20 + rl] = qq[i] * f;
+            }
+          }
+        }
       }
     }
     __syncthreads();
@@ -871,6 +921,31 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     }
   }
   __syncthreads();
+  // q and k rows of the chunk as fp32 (zero past the end) into R2 / R3, free
+  // after the decayed products, for the own-row terms below
+  float* sQr = sm + LD::R2;
+  float* sKr = sm + LD::R3;
+  {
+    constexpr int NPC = kCh * (DK / 8) / 256;
+    float qv[NPC][8], kv[NPC][8];
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+      const int e = tid + 256 * j, s = e / (DK / 8), c0 = (e % (DK / 8)) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[j][i] = kv[j][i] = 0.f;
+      if (s < L) {
+        ld8(q + row(s) * DK + c0, qv[j]);
+        ld8(k + row(s) * DK + c0, kv[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+      const int e = tid + 256 * j, s = e / (DK / 8), c0 = (e % (DK / 8)) * 8;
+      st8(sQr + s * PK + c0, qv[j]);
+      st8(sKr + s * PK + c0, kv[j]);
+    }
+  }
+  __syncthreads();
   // combine.  dg_r = sum_{r' >= r} (q dq + k dk_plus - k dk_col)_{r'}
   //              + sum_{r' < r} k e^(gamma - Gamma) dKh_{r'} + e^gamma sum_j N S:
   // the Kh term, which enters both dGamma (-) and dgamma (+), is summed over
@@ -887,8 +962,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       const int r = 16 * w + r0 + i;
       const float E = ex(ref_plus(w, cc, gl[K][i]));
       const float Eh = ex(gam_minus(w, cc) - gl[K][i]);
-      const float qv = r < L ? ldf(q, row(r) * DK + cc) : 0.f;
-      const float kv = r < L ? ldf(k, row(r) * DK + cc) : 0.f;
+      const float qv = sQr[r * PK + cc];
+      const float kv = sKr[r * PK + cc];
       const float dqv = E * dQb[K][i] + dqm[K][i];
       const float dkp = -sBeta[r] * E * dKb[K][i] + dkrow[K][i];
       const float hk = Eh * dKh[K][i];
