@@ -145,6 +145,27 @@ __device__ __forceinline__ void st8(float* p, const float* v) {
   *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
   *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
+// Loads of rows that may lie past the end of the sequence: the caller
+// points p at row 0 instead of such a row (always a valid address) and
+// passes ok = false, and the values become zero.  The load itself is not
+// inside a branch, so a run of them is issued together; behind a branch
+// every load was followed by its own wait for memory.
+template <typename T>
+__device__ __forceinline__ void ld8z(const T* p, bool ok, float* o) {
+  ld8(p, o);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = ok ? o[i] : 0.f;
+}
+template <typename T>
+__device__ __forceinline__ f32x4 ld4z(const T* p, bool ok) {
+  const f32x4 x = ld4(p);
+  return f32x4{ok ? x[0] : 0.f, ok ? x[1] : 0.f, ok ? x[2] : 0.f, ok ? x[3] : 0.f};
+}
+template <typename T>
+__device__ __forceinline__ float ldfz(const T* p, size_t i, bool ok) {
+  const float x = ldf(p, i);
+  return ok ? x : 0.f;
+}
 
 // ---------------------------------------------------------------------------
 // Per-chunk preparation.
@@ -178,6 +199,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   const int t0 = c * kCh, L = min(kCh, T - t0);
   float* out = rec + (size_t)n * RC::WORDS;
   auto row = [&](int r) { return ((size_t)b * T + t0 + r) * H + h; };   // token-major row index
+  auto rowc = [&](int r) { return row(r < L ? r : 0); };   // row 0 stands in past the end
 
   float* sGl = sm + LD::R0;   // Gamma - ref [64][PK]
   double* sRef = reinterpret_cast<double*>(sm + LD::REF);
@@ -193,19 +215,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   float* sKe = sm + LD::R1;
   float* sQe = sm + LD::R2;
   float* sKF = sm + LD::R3;
+#pragma unroll
   for (int e = tid; e < kCh * V8; e += 256) {
     const int r = e / V8, c0 = (e % V8) * 8;
-    float x[8] = {}, kk[8] = {}, qq[8] = {};
-    if (r < L) {
-      ld8(g + row(r) * DK + c0, x);
-      ld8(k + row(r) * DK + c0, kk);
-      ld8(q + row(r) * DK + c0, qq);
-    }
+    float x[8], kk[8], qq[8];
+    ld8z(g + rowc(r) * DK + c0, r < L, x);
+    ld8z(k + rowc(r) * DK + c0, r < L, kk);
+    ld8z(q + rowc(r) * DK + c0, r < L, qq);
     st8(sGl + r * PK + c0, x);
     st8(sKe + r * PK + c0, kk);
     st8(sQe + r * PK + c0, qq);
   }
-  if (tid < kCh) sBeta[tid] = tid < L ? ldf(beta, row(tid)) : 0.f;
+  if (tid < kCh) sBeta[tid] = ldfz(beta, rowc(tid), tid < L);
   __syncthreads();
   // decay scan (fp64) per channel, in place: Gamma - ref of the row's block
   if (tid < DK) {
@@ -245,8 +266,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
     __syncthreads();
     for (int e = tid; e < 16 * (a + 1) * V8; e += 256) {
       const int s = e / V8, c0 = (e % V8) * 8, bs = s >> 4;
-      float kk[8] = {}, gl[8];
-      if (s < L) ld8(k + row(s) * DK + c0, kk);
+      float kk[8], gl[8];
+      ld8z(k + rowc(s) * DK + c0, s < L, kk);
       ld8(sGl + s * PK + c0, gl);
 #pragma unroll
       for (int i = 0; i < 8; ++i) kk[i] *= ex((a == bs ? 0.f : dref(a, bs, c0 + i)) - gl[i]);
@@ -318,8 +339,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   } else {
     for (int e = tid - 64; e < kCh * V8; e += 192) {
       const int s = e / V8, c0 = (e % V8) * 8;
-      float kk[8] = {}, gl[8];
-      if (s < L) ld8(k + row(s) * DK + c0, kk);
+      float kk[8], gl[8];
+      ld8z(k + rowc(s) * DK + c0, s < L, kk);
       ld8(sGl + s * PK + c0, gl);
 #pragma unroll
       for (int i = 0; i < 8; ++i) sKbT[(c0 + i) * kP64 + s] = sBeta[s] * kk[i] * ex(ref_plus(s >> 4, c0 + i, gl[i]));
@@ -358,8 +379,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   float* sdOT = sm + LD::R3;
   for (int e = tid; e < kCh * DV / 8; e += 256) {
     const int r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
-    float x[8] = {};
-    if (r < L) ld8(dO + row(r) * DV + j0, x);
+    float x[8];
+    ld8z(dO + rowc(r) * DV + j0, r < L, x);
 #pragma unroll
     for (int i = 0; i < 8; ++i) sdOT[(j0 + i) * kP64 + r] = scale * x[i];
   }
@@ -380,8 +401,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   // Kh to the record; gather Gamma offsets for Qb (R0 is rewritten next)
   for (int e = tid; e < kCh * V8; e += 256) {
     const int r = e / V8, c0 = (e % V8) * 8;
-    float kk[8] = {}, gl[8];
-    if (r < L) ld8(k + row(r) * DK + c0, kk);
+    float kk[8], gl[8];
+    ld8z(k + rowc(r) * DK + c0, r < L, kk);
     ld8(sGl + r * PK + c0, gl);
     st8(out + RC::GLOC + r * DK + c0, gl);
 #pragma unroll
@@ -395,9 +416,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   for (int j = 0; j < PER; ++j) {
     const int e = tid + 256 * j, r = e / V8, c0 = (e % V8) * 8;
     float gl[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qb[j][i] = 0.f;
-    if (r < L) ld8(q + row(r) * DK + c0, qb[j]);
+    ld8z(q + rowc(r) * DK + c0, r < L, qb[j]);
     ld8(sGl + r * PK + c0, gl);
 #pragma unroll
     for (int i = 0; i < 8; ++i) qb[j][i] *= ex(ref_plus(r >> 4, c0 + i, gl[i]));
@@ -592,6 +611,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   const int nbh = (int)(gridDim.x / nch);
   const float* rc = rec + (size_t)n * RC::WORDS;
   auto row = [&](int r) { return ((size_t)b * T + t0 + r) * H + h; };
+  auto rowc = [&](int r) { return row(r < L ? r : 0); };   // row 0 stands in past the end
   const float* S = c == 0 ? (h0 ? h0 + (size_t)bh * DK * DV : nullptr) : snap + ((size_t)(c - 1) * nbh + bh) * DK * DV;
   const float* Nn = dNb + (size_t)n * DK * DV;
 
@@ -625,7 +645,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     }
     for (int e = tid; e < 10 * DK; e += 256) sm[LD::REF + e] = rc[RC::REF + e];
     if (tid < kCh) {
-      sBeta[tid] = tid < L ? ldf(beta, row(tid)) : 0.f;
+      sBeta[tid] = ldfz(beta, rowc(tid), tid < L);
       sDb[tid] = 0.f;
     }
 #pragma unroll
@@ -651,13 +671,13 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
   for (int J = 0; J < NT; ++J) {
     const int c0 = 16 * J + 4 * g4;
-    const f32x4 kk = ra < L ? ld4(k + row(ra) * DK + c0) : zero4();
+    const f32x4 kk = ld4z(k + rowc(ra) * DK + c0, ra < L);
     const f32x4 gl4 = ld4(rc + RC::GLOC + ra * DK + c0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) kba[J][i] = kk[i] * ex(ref_plus(w, c0 + i, gl4[i]));
   }
 #pragma unroll
-  for (int J = 0; J < NV; ++J) doa[J] = ra < L ? scale * ld4(dO + row(ra) * DV + 16 * J + 4 * g4) : zero4();
+  for (int J = 0; J < NV; ++J) doa[J] = scale * ld4z(dO + rowc(ra) * DV + 16 * J + 4 * g4, ra < L);
   __syncthreads();
 
   // e^gamma sum_j N S per key row (threads: row = tid / 2, half of the columns)
@@ -686,7 +706,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + r0 + i;
-      R[J][i] = r < L ? ldf(v, row(r) * DV + 16 * J + cl) : 0.f;
+      R[J][i] = ldfz(v, rowc(r) * DV + 16 * J + cl, r < L);
     }
 #pragma unroll
   for (int J = 0; J < NV; ++J) {
@@ -863,14 +883,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       for (int j = 0; j < NPC; ++j) {
         const int e = tid + 256 * j, s = e / (DK / 8), c0 = (e % (DK / 8)) * 8;
         if (e < hi) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) kk[j][i] = 0.f;
-          if (s < L) ld8(k + row(s) * DK + c0, kk[j]);
+          ld8z(k + rowc(s) * DK + c0, s < L, kk[j]);
           ld8(rc + RC::GLOC + (size_t)s * DK + c0, gv[j]);
           if (j == jq && e >= lo) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qq[i] = 0.f;
-            if (s < L) ld8(q + row(s) * DK + c0, qq);
+            ld8z(q + rowc(s) * DK + c0, s < L, qq);
           }
         }
       }
@@ -931,12 +947,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
 #pragma unroll
     for (int j = 0; j < NPC; ++j) {
       const int e = tid + 256 * j, s = e / (DK / 8), c0 = (e % (DK / 8)) * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qv[j][i] = kv[j][i] = 0.f;
-      if (s < L) {
-        ld8(q + row(s) * DK + c0, qv[j]);
-        ld8(k + row(s) * DK + c0, kv[j]);
-      }
+      ld8z(q + rowc(s) * DK + c0, s < L, qv[j]);
+      ld8z(k + rowc(s) * DK + c0, s < L, kv[j]);
     }
 #pragma unroll
     for (int j = 0; j < NPC; ++j) {
