@@ -631,9 +631,12 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   constexpr int NSS = DK * DV / 4 / 256, NLI = kCh * kCh / 4 / 256, NDU = kCh * DV / 8 / 256;
   static_assert(NSS * 1024 == DK * DV && NLI * 1024 == kCh * kCh && NDU * 2048 == kCh * DV, "pieces per thread");
   float* sdUT = sm + LD::R3;   // dU^T
+  constexpr int NREF = (10 * DK + 255) / 256;   // fp64 block references and gamma, as words
   {
     f32x4 sv[NSS], li[NLI];
-    float du[NDU][8];
+    float du[NDU][8], refv[NREF];
+#pragma unroll
+    for (int i = 0; i < NREF; ++i) refv[i] = rc[RC::REF + min(tid + 256 * i, 10 * DK - 1)];
 #pragma unroll
     for (int i = 0; i < NSS; ++i) sv[i] = S ? *(const f32x4*)(S + 4 * (tid + 256 * i)) : zero4();
 #pragma unroll
@@ -643,7 +646,9 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       const int e = tid + 256 * i, r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
       ld8(dUb + ((size_t)n * kCh + r) * DV + j0, du[i]);
     }
-    for (int e = tid; e < 10 * DK; e += 256) sm[LD::REF + e] = rc[RC::REF + e];
+#pragma unroll
+    for (int i = 0; i < NREF; ++i)
+      if (tid + 256 * i < 10 * DK) sm[LD::REF + tid + 256 * i] = refv[i];
     if (tid < kCh) {
       sBeta[tid] = ldfz(beta, rowc(tid), tid < L);
       sDb[tid] = 0.f;
@@ -665,20 +670,23 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       for (int x = 0; x < 8; ++x) sdUT[(j0 + x) * kP64 + r] = du[i][x];
     }
   }
-  // this wave's rows of Kb and scale * dO as left operands
+  // this wave's rows of Kb and scale * dO as left operands (Kb takes the
+  // block references, which are in LDS only after the barrier)
   const int ra = 16 * w + cl;   // operand row of this lane
-  f32x4 kba[NT], doa[NV];
+  f32x4 kba[NT], doa[NV], gla[NT];
 #pragma unroll
   for (int J = 0; J < NT; ++J) {
     const int c0 = 16 * J + 4 * g4;
-    const f32x4 kk = ld4z(k + rowc(ra) * DK + c0, ra < L);
-    const f32x4 gl4 = ld4(rc + RC::GLOC + ra * DK + c0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kba[J][i] = kk[i] * ex(ref_plus(w, c0 + i, gl4[i]));
+    kba[J] = ld4z(k + rowc(ra) * DK + c0, ra < L);
+    gla[J] = ld4(rc + RC::GLOC + ra * DK + c0);
   }
 #pragma unroll
   for (int J = 0; J < NV; ++J) doa[J] = scale * ld4z(dO + rowc(ra) * DV + 16 * J + 4 * g4, ra < L);
   __syncthreads();
+#pragma unroll
+  for (int J = 0; J < NT; ++J)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kba[J][i] *= ex(ref_plus(w, 16 * J + 4 * g4 + i, gla[J][i]));
 
   // e^gamma sum_j N S per key row (threads: row = tid / 2, half of the columns)
   {
