@@ -1084,6 +1084,33 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) Ub[st][jj] = narrow4<Op>(U[st][jj] * us);
 
+    // S <- e^{Gamma_C} S + Khat^T U, ahead of the output: only S feeds the
+    // next chunk, so its products overlap the output work below
+#pragma unroll
+    for (int cp = 0; cp < NCT; cp += 2) {   // two column tiles of S per LDS batch
+      Slab<Op> Ka[2][2];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+          Ka[cc][sl] = slab_of<Op>(load4(sK + tile_k<NCT>(2 * sl, cp + cc) * 256 + 4 * lane),
+                                   load4(sK + tile_k<NCT>(2 * sl + 1, cp + cc) * 256 + 4 * lane));
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int ct = cp + cc;
+        const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
+        f32x4 acc[NJ];
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) acc[jj] = zero4();
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) acc[jj] = mma(Ka[cc][sl], slab_of<Op>(Ub[2 * sl][jj], Ub[2 * sl + 1][jj]), acc[jj]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) S[ct][jj] = S[ct][jj] * d + acc[jj] * ius;
+      }
+    }
     // O = Qbar S + (scale M) U, stored as 16-byte non-temporal vectors
     // (written once, not re-read)
     const int t0 = c * kC;
@@ -1140,32 +1167,6 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
             __builtin_nontemporal_store(Ov[rt][jj], reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj));
     }
 
-    // S <- e^{Gamma_C} S + Khat^T U
-#pragma unroll
-    for (int cp = 0; cp < NCT; cp += 2) {   // two column tiles of S per LDS batch
-      Slab<Op> Ka[2][2];
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl)
-          Ka[cc][sl] = slab_of<Op>(load4(sK + tile_k<NCT>(2 * sl, cp + cc) * 256 + 4 * lane),
-                                   load4(sK + tile_k<NCT>(2 * sl + 1, cp + cc) * 256 + 4 * lane));
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ct = cp + cc;
-        const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
-        f32x4 acc[NJ];
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) acc[jj] = zero4();
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-#pragma unroll
-          for (int jj = 0; jj < NJ; ++jj) acc[jj] = mma(Ka[cc][sl], slab_of<Op>(Ub[2 * sl][jj], Ub[2 * sl + 1][jj]), acc[jj]);
-        }
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) S[ct][jj] = S[ct][jj] * d + acc[jj] * ius;
-      }
-    }
     if (kExt && snap.p && snap.every > 0 && (c + 1) % snap.every == 0 && (c + 1) * kC < T_len) {
       float* sp = snap.p + ((size_t)((c + 1) / snap.every - 1) * snap.nbh + bh) * DK * DV;
 #pragma unroll
