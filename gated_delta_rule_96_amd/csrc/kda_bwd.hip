@@ -231,6 +231,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   // decay scan (fp64) per channel, in place: Gamma - ref of the row's block
   if (tid < DK) {
     double acc = 0.0, ref[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll   // (static block index of ref, no select chains)
     for (int r = 0; r < kCh; ++r) {
       acc += (double)sGl[r * PK + tid];
       sGl[r * PK + tid] = (float)(acc - ref[r >> 4]);
@@ -264,14 +265,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     __syncthreads();
-    for (int e = tid; e < 16 * (a + 1) * V8; e += 256) {
-      const int s = e / V8, c0 = (e % V8) * 8, bs = s >> 4;
-      float kk[8], gl[8];
-      ld8z(k + rowc(s) * DK + c0, s < L, kk);
-      ld8(sGl + s * PK + c0, gl);
+    {   // rows s < 16 (a + 1): every k load is issued before the first use
+      constexpr int NPC = kCh * V8 / 256;
+      float kk[NPC][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kk[i] *= ex((a == bs ? 0.f : dref(a, bs, c0 + i)) - gl[i]);
-      st8(sKF + s * PK + c0, kk);
+      for (int j = 0; j < NPC; ++j) {
+        const int e = tid + 256 * j, s = e / V8, c0 = (e % V8) * 8;
+        if (e < 16 * (a + 1) * V8) ld8z(k + rowc(s) * DK + c0, s < L, kk[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < NPC; ++j) {
+        const int e = tid + 256 * j, s = e / V8, c0 = (e % V8) * 8, bs = s >> 4;
+        if (e < 16 * (a + 1) * V8) {
+          float gl[8];
+          ld8(sGl + s * PK + c0, gl);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) kk[j][i] *= ex((a == bs ? 0.f : dref(a, bs, c0 + i)) - gl[i]);
+          st8(sKF + s * PK + c0, kk[j]);
+        }
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -337,13 +349,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
       sLi[ri * kP64 + 16 * a + j] = x[i];
     }
   } else {
-    for (int e = tid - 64; e < kCh * V8; e += 192) {
-      const int s = e / V8, c0 = (e % V8) * 8;
-      float kk[8], gl[8];
-      ld8z(k + rowc(s) * DK + c0, s < L, kk);
-      ld8(sGl + s * PK + c0, gl);
+    constexpr int NP = (kCh * V8 + 191) / 192;   // pieces per thread of waves 1-3
+    float kk[NP][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sKbT[(c0 + i) * kP64 + s] = sBeta[s] * kk[i] * ex(ref_plus(s >> 4, c0 + i, gl[i]));
+    for (int j = 0; j < NP; ++j) {
+      const int e = tid - 64 + 192 * j, s = e < kCh * V8 ? e / V8 : 0, c0 = (e % V8) * 8;
+      ld8z(k + rowc(s) * DK + c0, e < kCh * V8 && s < L, kk[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int e = tid - 64 + 192 * j, s = e / V8, c0 = (e % V8) * 8;
+      if (e < kCh * V8) {
+        float gl[8];
+        ld8(sGl + s * PK + c0, gl);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          sKbT[(c0 + i) * kP64 + s] = sBeta[s] * kk[j][i] * ex(ref_plus(s >> 4, c0 + i, gl[i]));
+      }
     }
   }
   __syncthreads();
@@ -377,12 +399,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
     wt[T_] = mm_nt(zero4(), sLi + 16 * w * kP64, kP64, sKbT + 16 * T_ * kP64, kP64, 0, 16 * (w + 1));
   // dO^T scaled (R3; the inverse's scratch is no longer read)
   float* sdOT = sm + LD::R3;
-  for (int e = tid; e < kCh * DV / 8; e += 256) {
-    const int r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
-    float x[8];
-    ld8z(dO + rowc(r) * DV + j0, r < L, x);
+  {
+    constexpr int NDO = kCh * DV / 8 / 256;
+    static_assert(NDO * 2048 == kCh * DV, "pieces per thread");
+    float x[NDO][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sdOT[(j0 + i) * kP64 + r] = scale * x[i];
+    for (int j = 0; j < NDO; ++j) {
+      const int e = tid + 256 * j, r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
+      ld8z(dO + rowc(r) * DV + j0, r < L, x[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NDO; ++j) {
+      const int e = tid + 256 * j, r = e / (DV / 8), j0 = (e % (DV / 8)) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sdOT[(j0 + i) * kP64 + r] = scale * x[j][i];
+    }
   }
   __syncthreads();
   float* sWT = sm + LD::R2;
@@ -399,15 +430,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
 #pragma unroll
   for (int J = 0; J < NV; ++J) pt[J] = mm_nt(zero4(), sMT + 16 * w * kP64, kP64, sdOT + 16 * J * kP64, kP64, 16 * w, kCh);
   // Kh to the record; gather Gamma offsets for Qb (R0 is rewritten next)
-  for (int e = tid; e < kCh * V8; e += 256) {
-    const int r = e / V8, c0 = (e % V8) * 8;
-    float kk[8], gl[8];
-    ld8z(k + rowc(r) * DK + c0, r < L, kk);
-    ld8(sGl + r * PK + c0, gl);
-    st8(out + RC::GLOC + r * DK + c0, gl);
+  {
+    constexpr int NPC = kCh * V8 / 256;
+    float kk[NPC][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kk[i] *= ex(gam_minus(r >> 4, c0 + i) - gl[i]);
-    st8(out + RC::KH + r * DK + c0, kk);
+    for (int j = 0; j < NPC; ++j) {
+      const int e = tid + 256 * j, r = e / V8, c0 = (e % V8) * 8;
+      ld8z(k + rowc(r) * DK + c0, r < L, kk[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+      const int e = tid + 256 * j, r = e / V8, c0 = (e % V8) * 8;
+      float gl[8];
+      ld8(sGl + r * PK + c0, gl);
+      st8(out + RC::GLOC + r * DK + c0, gl);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kk[j][i] *= ex(gam_minus(r >> 4, c0 + i) - gl[i]);
+      st8(out + RC::KH + r * DK + c0, kk[j]);
+    }
   }
   for (int e = tid; e < 10 * DK; e += 256) out[RC::REF + e] = sm[LD::REF + e];   // fp64 refs and gamma
   constexpr int PER = kCh * V8 / 256;   // groups of 8 per thread
