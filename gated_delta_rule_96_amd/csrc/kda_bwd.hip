@@ -906,13 +906,14 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     for (int i = 0; i < 4; ++i) gl[K][i] = rc[RC::GLOC + (size_t)(16 * w + r0 + i) * DK + 16 * K + cl];
   }
   // decayed products, one row block a at a time
-  f32x4 dqm[NT], dkrow[NT], dkcol[NT];
+  // Row side of row block a: every wave takes NT / 4 channel tiles of every
+  // block (rx1, rx2), handed to the block's owner wave through LDS after the
+  // loop; the column side stays with the owner of the column rows.
+  constexpr int NTW = NT / 4;
+  static_assert(NTW * 4 == NT, "dk must be a multiple of 64");
+  f32x4 dkcol[NT], rx1[4][NTW], rx2[4][NTW];
 #pragma unroll
-  for (int K = 0; K < NT; ++K) {
-    dqm[K] = zero4();
-    dkrow[K] = zero4();
-    dkcol[K] = zero4();
-  }
+  for (int K = 0; K < NT; ++K) dkcol[K] = zero4();
   float* sKFT = sm + LD::R0;                // [DK][68]: k_s e^(ref_a - Gamma_s), s < 16(a+1)
   float* sKeT = sm + LD::R1;                // [DK][20]: k_r e^(Gamma_r - ref_a), r in block a
   float* sQeT = sm + LD::R1 + DK * 20;      // [DK][20]: q_r e^(Gamma_r - ref_a)
@@ -958,15 +959,11 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       }
     }
     __syncthreads();
-    if (w == a) {   // row side: rows of block a
 #pragma unroll
-      for (int K = 0; K < NT; ++K) {
-        const f32x4 x1 = mm_nt(zero4(), sdG + 16 * a * kP64, kP64, sKFT + 16 * K * kP64, kP64, 0, 16 * (a + 1));
-        const f32x4 x2 = mm_nt(zero4(), sdM + 16 * a * kP64, kP64, sKFT + 16 * K * kP64, kP64, 0, 16 * (a + 1));
-        const f32x4 e4 = f32x4{ex(gl[K][0]), ex(gl[K][1]), ex(gl[K][2]), ex(gl[K][3])};
-        dkrow[K] += e4 * x1;
-        dqm[K] += e4 * x2;
-      }
+    for (int kk = 0; kk < NTW; ++kk) {   // row side: rows of block a, this wave's channel tiles
+      const int K = w * NTW + kk;
+      rx1[a][kk] = mm_nt(zero4(), sdG + 16 * a * kP64, kP64, sKFT + 16 * K * kP64, kP64, 0, 16 * (a + 1));
+      rx2[a][kk] = mm_nt(zero4(), sdM + 16 * a * kP64, kP64, sKFT + 16 * K * kP64, kP64, 0, 16 * (a + 1));
     }
     if (w <= a) {   // column side: rows s of block w against rows r of block a
 #pragma unroll
@@ -1005,7 +1002,28 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
       st8(sKr + s * PK + c0, kv[j]);
     }
   }
+  // row-side products to R0 / R1 ([64][PK], free after the loop), then each
+  // wave takes its own rows and applies their decay factors
+  float* sX1 = sm + LD::R0;
+  float* sX2 = sm + LD::R1;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int kk = 0; kk < NTW; ++kk) {
+      st_rm(sX1 + 16 * a * PK + 16 * (w * NTW + kk), PK, rx1[a][kk]);
+      st_rm(sX2 + 16 * a * PK + 16 * (w * NTW + kk), PK, rx2[a][kk]);
+    }
   __syncthreads();
+  f32x4 dqm[NT], dkrow[NT];
+#pragma unroll
+  for (int K = 0; K < NT; ++K) {
+    const f32x4 e4 = f32x4{ex(gl[K][0]), ex(gl[K][1]), ex(gl[K][2]), ex(gl[K][3])};
+    const float* x1 = sX1 + (16 * w + r0) * PK + 16 * K + cl;
+    const float* x2 = sX2 + (16 * w + r0) * PK + 16 * K + cl;
+    dkrow[K] = e4 * f32x4{x1[0], x1[PK], x1[2 * PK], x1[3 * PK]};
+    dqm[K] = e4 * f32x4{x2[0], x2[PK], x2[2 * PK], x2[3 * PK]};
+  }
+  __syncthreads();   // R0 and R1 are rewritten below
   // combine.  dg_r = sum_{r' >= r} (q dq + k dk_plus - k dk_col)_{r'}
   //              + sum_{r' < r} k e^(gamma - Gamma) dKh_{r'} + e^gamma sum_j N S:
   // the Kh term, which enters both dGamma (-) and dgamma (+), is summed over
