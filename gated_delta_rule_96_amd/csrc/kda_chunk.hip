@@ -341,13 +341,21 @@ struct IntraLds {
   static_assert(4 * 256 * 4 + 4 * (size_t)DK * 4 <= (size_t)kC * LA * 4, "M diagonal tiles and totals fit in X");
 };
 
+// Small per-wave tables are packed into 64-bit immediates, 4 bits per
+// entry, so a lookup with a wave-uniform index is scalar shifts.  (As
+// __constant__ arrays, each lookup was a vector load followed by a wait for
+// every outstanding vector access, the next chunk's input loads included.)
+__device__ __forceinline__ int nib(unsigned long long tab, int i) { return (int)((tab >> (4 * i)) & 0xfu); }
 // The 10 tiles (a, b) of the lower 4x4 block triangle: diagonal first.
-__constant__ signed char kTileA[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
-__constant__ signed char kTileB[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
+//   a: 0 1 2 3 1 2 3 2 3 3     b: 0 1 2 3 0 0 0 1 1 2
+constexpr unsigned long long kTileA = 0x3323213210ull;
+constexpr unsigned long long kTileB = 0x2110003210ull;
 // Gram tiles of wave w (-1: none): a diagonal tile (the costlier kind, with
 // split operands) for waves 0-3; two off-diagonal tiles of one row block for
 // waves 4 and 5 (they share the row operand); one for waves 6 and 7.
-__constant__ signed char kWaveTile[8][2] = {{0, -1}, {1, -1}, {2, -1}, {3, -1}, {5, 7}, {6, 8}, {4, -1}, {9, -1}};
+//   first tile: 0 1 2 3 5 6 4 9     second tile (15: none): - - - - 7 8 - -
+constexpr unsigned long long kWaveTile0 = 0x94653210ull;
+constexpr unsigned long long kWaveTile1 = 0xff87ffffull;
 
 // Builds the record of chunk `ch` of head (b, h) at `rec`.  Called by a
 // whole work-group of kThreads threads; `smem` holds IntraLds::BYTES.
@@ -542,7 +550,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
 
   // ---- phase 1: Gram tiles (A -> LDS, scale M -> record)
   {
-    const int t0i = kWaveTile[w][0], t1i = kWaveTile[w][1];
+    const int t0i = nib(kWaveTile0, w), t1i1 = nib(kWaveTile1, w), t1i = t1i1 == 15 ? -1 : t1i1;
     const int ntile = t0i < 0 ? 0 : (t1i < 0 ? 1 : 2);   // wave-uniform
     if (kUnb && t0i >= 0 && t0i < 4) {
       // diagonal tile from the position pairs of phase 0: scale M to the record
@@ -551,8 +559,8 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       store4<Op>(rM + tile_cr(t0i, t0i) * 256 + 4 * lane, narrow4<Op>(f32x4{md[0], md[1], md[2], md[3]}));
     } else if (ntile > 0) {
       // both tiles of a wave share the row block a, hence the row operand
-      const int a = kTileA[t0i];
-      const int bb0 = kTileB[t0i], bb1 = ntile > 1 ? kTileB[t1i] : bb0;
+      const int a = nib(kTileA, t0i);
+      const int bb0 = nib(kTileB, t0i), bb1 = ntile > 1 ? nib(kTileB, t1i) : bb0;
       const bool diag = a == bb0;   // only single-tile waves hold a diagonal tile
       const int r = 16 * a + l16, s0 = 16 * bb0 + l16, s1 = 16 * bb1 + l16;
       const float* d0p = sBlk + (diag ? kBlkM + a : kBlkD + t0i - 4) * DK;
@@ -605,7 +613,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   }
   if (w >= 2) {   // the six tiles above the diagonal of the record's M are zero
     // (the mirror of lower tile (a, b): row block b, column block a)
-    const int zt = w - 2, kt = kTileA[4 + zt], rt = kTileB[4 + zt];
+    const int zt = w - 2, kt = nib(kTileA, 4 + zt), rt = nib(kTileB, 4 + zt);
     store4<Op>(rM + tile_cr(kt, rt) * 256 + 4 * lane, narrow4<Op>(zero4()));
   }
   // V's range (for its fp16 staging): wave maxima of the chunk's v, combined
@@ -1306,16 +1314,13 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
       __hip_atomic_store(ready + pj * R + pc % R, ((pc + 1) << 4) | my_xcc, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   };
-  int pending = -1;   // item whose record is written but not yet published
   for (;;) {
     const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
     const int nxt = it + P;
-    // Runs once this chunk's inputs are in LDS: publish the previous item
-    // (its record stores drained while this item was staged), then wait
-    // until the ring slot of chunk c is free (it held chunk c - R, which the
-    // head's consumers must have read).
+    // Runs once this chunk's inputs are in LDS: wait until the ring slot of
+    // chunk c is free (it held chunk c - R, which the head's consumers must
+    // have read).
     auto after_stage = [&]() -> bool {
-      if (pending >= 0) publish(pending);
       if (c < R) return true;
       if (w == 0) {
         bool ok = true;
@@ -1338,11 +1343,12 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     if (!produce_chunk<TIn, DK, DV, kUnb, kExt>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
                                     ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage, prefetch, lay))
       return;
-    pending = it;
-    if (nxt >= total) {
-      publish(pending);
-      return;
-    }
+    // Published as soon as its stores are in the L2.  (Deferring this until
+    // the next item's inputs were staged let the stores drain in the
+    // background but made every record visible some 4-5k cycles later; the
+    // consumers then waited for records and the producers for ring slots.)
+    publish(it);
+    if (nxt >= total) return;
     it = nxt;
   }
 }
