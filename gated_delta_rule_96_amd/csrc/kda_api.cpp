@@ -43,18 +43,38 @@ const char* kda_status_str(int s) {
     case KDA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case KDA_ERR_UNSUPPORTED: return "unsupported dk/dv/chunk (dk, dv in {64,128}; chunk 64)";
     case KDA_ERR_WORKSPACE: return "workspace missing or smaller than kda_fwd_workspace_bytes";
-    case KDA_ERR_RANGE: return "input value out of range";
+    case KDA_ERR_RANGE: return "input value out of range (log-decay outside [gmin, 0], or gmin outside [-5, 0))";
     case KDA_ERR_HIP: return "HIP launch failed";
+    case KDA_ERR_INCOMPLETE:
+      return "the fused prefill gave up on a hand-off wait (GPU shared with other work?): outputs incomplete";
     default: return "unknown status";
   }
 }
 
 namespace {
+
+constexpr float kGmin = -5.0f;   // the gate's floor ("Key claims", section 2.1.1)
+
+// Opt-in range check (KDA_VALIDATE=1): the log-decay input of a bounded
+// call in [-5, 0] (bounded != 0), or <= 0 (unbounded call); finite.
+int check_range(int dtype, const void* g, const float* gcum, int bounded, int B, int T, int H, int dk,
+                void* stream) {
+  if (!kda::validate_requested()) return KDA_OK;
+  int ok = 0;
+  const hipError_t e = kda::validate_decay(dtype == KDA_BF16, g, gcum, bounded, kGmin, B, T, H * dk, kChunk,
+                                           static_cast<hipStream_t>(stream), &ok);
+  if (e != hipSuccess) return KDA_ERR_HIP;
+  return ok ? KDA_OK : KDA_ERR_RANGE;
+}
+
 int prepare_decay_impl(const void* z, const float* A, float gmin, void* g, float* gcum, int dtype, int B, int T,
                        int H, int dk, int chunk, int softplus, void* stream) {
   if (!valid_dtype(dtype)) return KDA_ERR_DTYPE;
   if (B <= 0 || T <= 0 || H <= 0 || dk <= 0 || chunk <= 0 || !size_ok(B, T, H, dk)) return KDA_ERR_SHAPE;
   if (!supported_d(dk) || chunk != kChunk) return KDA_ERR_UNSUPPORTED;
+  // the bounded gate's floor must keep 16 rows of decay inside the bf16
+  // range the prefill's rescaled tiles rely on (16 * 5 = 80 < 88.7)
+  if (z && !softplus && !(gmin >= kGmin && gmin < 0.f)) return KDA_ERR_RANGE;
   if (z) {
     if (!A || (!g && !gcum)) return KDA_ERR_NULL;
   } else {
@@ -126,9 +146,13 @@ int fwd_fused_impl(const void* q, const void* k, const void* v, const void* g, c
   const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace, 3);
   if (st != KDA_OK) return st;
   if (workspace_bytes < kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
-  hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
-                                       workspace, workspace_bytes, unbounded, nullptr, 0, nullptr, nullptr, 0,
-                                       static_cast<hipStream_t>(stream));
+  const int rs = check_range(dtype, g, gcum, !unbounded, B, T, H, dk, stream);
+  if (rs != KDA_OK) return rs;
+  hipError_t e = kda::launch_clear_status(workspace, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess)
+    e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
+                              workspace, workspace_bytes, unbounded, nullptr, 0, nullptr, nullptr, 0,
+                              static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 }  // namespace
@@ -157,6 +181,10 @@ int kda_fwd_chunked_stages(const void* q, const void* k, const void* v, const vo
   const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace, mask);
   if (st != KDA_OK) return st;
   if (workspace_bytes < kda_fwd_stages_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
+  if (mask & 1) {
+    const int rs = check_range(dtype, g, gcum, !(stages & KDA_STAGES_UNBOUNDED), B, T, H, dk, stream);
+    if (rs != KDA_OK) return rs;
+  }
   hipError_t e = kda::launch_fwd_stages(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv,
                                         workspace, mask, (stages & KDA_STAGES_UNBOUNDED) ? 1 : 0, nullptr, 0,
                                         static_cast<hipStream_t>(stream));
@@ -174,10 +202,26 @@ int kda_fwd_chunked_layer(const void* q, const void* k, const void* v, const voi
   if ((og && !aligned16(og)) || !aligned16(A)) return KDA_ERR_ALIGN;
   if (workspace_bytes < kda_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
   const int lf = 1 /* g is z */ | ((flags & KDA_LAYER_QK_L2NORM) ? 2 : 0);
-  hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, z, nullptr, beta, scale, h0, ht, o, B, T, H, dk,
-                                       dv, workspace, workspace_bytes, 0, nullptr, 0, A, og, lf,
-                                       static_cast<hipStream_t>(stream));
+  hipError_t e = kda::launch_clear_status(workspace, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess)
+    e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, z, nullptr, beta, scale, h0, ht, o, B, T, H, dk, dv,
+                              workspace, workspace_bytes, 0, nullptr, 0, A, og, lf, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+const int* kda_fwd_status_word(const void* workspace) {
+  return workspace ? static_cast<const int*>(workspace) + 8 : nullptr;
+}
+
+int kda_fwd_status(const void* workspace, void* stream) {
+  if (!workspace) return KDA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_ALIGN;
+  int word = 0;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&word, kda_fwd_status_word(workspace), sizeof(int), hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return KDA_ERR_HIP;
+  return word != 0 ? KDA_ERR_INCOMPLETE : KDA_OK;
 }
 
 long long kda_fwd_varlen_snapshots(const int* cu_seqlens, int N, int snap_every, int chunk) {
@@ -199,6 +243,9 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
   const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, 1, T, H, dk, dv, chunk, workspace, 3);
   if (st != KDA_OK) return st;
   if (!cu_seqlens) return KDA_ERR_NULL;
+  // a packed gcum restarts at multiples of 64 of the packed axis, not at
+  // each sequence's own chunks: only g is accepted here
+  if (gcum) return KDA_ERR_UNSUPPORTED;
   if (N <= 0 || cu_seqlens[0] != 0 || cu_seqlens[N] != T || snap_every < 0) return KDA_ERR_SHAPE;
   for (int i = 0; i < N; ++i)
     if (cu_seqlens[i + 1] < cu_seqlens[i]) return KDA_ERR_SHAPE;
@@ -206,7 +253,10 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
   if (snap && snap_every > 0 && !aligned16(snap)) return KDA_ERR_ALIGN;
   // the workspace sized for one sequence of T tokens serves every call below
   if (workspace_bytes < kda_fwd_workspace_bytes(1, T, H, dk, dv, chunk, dtype)) return KDA_ERR_WORKSPACE;
+  const int rs = check_range(dtype, g, nullptr, 1, 1, T, H, dk, stream);
+  if (rs != KDA_OK) return rs;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (kda::launch_clear_status(workspace, hs) != hipSuccess) return KDA_ERR_HIP;
   const size_t esz = dtype == KDA_BF16 ? 2 : 4;
   const size_t hk = (size_t)H * dk, hv = (size_t)H * dv, sd = (size_t)H * dk * dv;
   const bool snaps = snap && snap_every > 0;
@@ -227,7 +277,7 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
         return p ? static_cast<const void*>(static_cast<const char*>(p) + t0 * per_token * esz) : nullptr;
       };
       e = kda::launch_fwd_fused(dtype == KDA_BF16, at(q, hk), at(k, hk), at(v, hv), at(g, hk),
-                                gcum ? gcum + t0 * hk : nullptr, at(beta, (size_t)H), scale, h0_i, ht_i,
+                                nullptr, at(beta, (size_t)H), scale, h0_i, ht_i,
                                 o + t0 * hv, 1, len, H, dk, dv, workspace, workspace_bytes, 0,
                                 snaps ? snap + (size_t)snap_off * sd : nullptr, snaps ? snap_every : 0, nullptr,
                                 nullptr, 0, hs);
@@ -250,6 +300,8 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
   for (const void* p : {q, k, v, g, beta, (const void*)state, (const void*)o})
     if (!aligned16(p)) return KDA_ERR_ALIGN;
   if ((long long)B * H > 2147483647LL) return KDA_ERR_SHAPE;
+  const int rs = check_range(dtype, g, nullptr, 1, B, 1, H, dk, stream);
+  if (rs != KDA_OK) return rs;
   hipError_t e = kda::launch_decode_step(dtype == KDA_BF16, q, k, v, g, beta, scale, state, o, B, H, dk, dv,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -309,10 +361,15 @@ int kda_bwd_chunked(const void* q, const void* k, const void* v, const void* g, 
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
   const BwdLayout lay = bwd_layout(B, T, H, dk, dv, dtype);
   if (workspace_bytes < lay.total) return KDA_ERR_WORKSPACE;
+  st = check_range(dtype, g, nullptr, 1, B, T, H, dk, stream);
+  if (st != KDA_OK) return st;
   char* ws = static_cast<char*>(workspace);
   const int nch = (T + kChunk - 1) / kChunk;
   float* snap = nch > 1 ? reinterpret_cast<float*>(ws + lay.snap) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the forward recompute's status word is the workspace's (its forward
+  // part comes first): kda_fwd_status reads it
+  if (kda::launch_clear_status(ws + lay.fwd, s) != hipSuccess) return KDA_ERR_HIP;
   hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, nullptr, beta, scale, h0,
                                        reinterpret_cast<float*>(ws + lay.ht), reinterpret_cast<float*>(ws + lay.o), B,
                                        T, H, dk, dv, ws + lay.fwd, lay.o - lay.fwd, 0, snap, snap ? 1 : 0, nullptr,

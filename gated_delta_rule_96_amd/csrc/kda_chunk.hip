@@ -1236,9 +1236,13 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
 // Every wait is bounded (kSpinLimit); on a timeout the work-group sets the
 // error word and leaves, so the grid always drains.
 //
-// ctrl layout (ints, zeroed before the launch):
-//   [0..7]   unused                     [8] error word
+// ctrl layout (ints):
+//   [0..7]   unused                     [8] error word (status of the call)
 //   [16 ..)  ready[nheads][R], then done[nheads][NS], then cxcc[nheads][NS]
+// [16 ..) is zeroed before every launch; [0..16) once per API call
+// (launch_clear_status), so an error word set by any launch of a call (one
+// per batch of heads, or per sequence) stays set until the caller reads it,
+// and every later launch of the call gives up at its first wait.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct FusedLds {
@@ -1408,8 +1412,8 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   char* ring = reinterpret_cast<char*>(ws) + fused_ctrl_bytes<TIn, DK, DV>(batch);
   for (int head0 = 0; head0 < nbh; head0 += batch) {
     const int nh = nbh - head0 < batch ? nbh - head0 : batch;
-    const int nctrl = 16 + nh * kRingSlots + 2 * NS * nh;
-    hipLaunchKernelGGL(clear_ints_kernel, dim3((nctrl + 255) / 256), dim3(256), 0, st, ctrl, nctrl);
+    const int nflags = nh * kRingSlots + 2 * NS * nh;   // ctrl[16 ..): this launch's flags only
+    hipLaunchKernelGGL(clear_ints_kernel, dim3((nflags + 255) / 256), dim3(256), 0, st, ctrl + 16, nflags);
     // three variants: plain, unbounded decay, layer steps / snapshots
     const bool ext = lay.flags != 0 || lay.og != nullptr || (snap != nullptr && snap_every > 0);
     if (unb && ext) return hipErrorInvalidValue;
@@ -1524,4 +1528,15 @@ hipError_t launch_zero_words(void* p, size_t nwords, hipStream_t st) {
                      reinterpret_cast<int*>(p), n);
   return hipGetLastError();
 }
+}  // namespace kda
+
+namespace kda {
+
+// Status words of a prefill workspace (ints [0..16): the error word and
+// spare words) cleared once at the start of an API call.
+hipError_t launch_clear_status(void* ws, hipStream_t st) {
+  hipLaunchKernelGGL(clear_ints_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<int*>(ws), 16);
+  return hipGetLastError();
+}
+
 }  // namespace kda

@@ -13,6 +13,15 @@ hipError_t launch_prepare_decay(int is_bf16, const void* z, const float* A, floa
                                 float* gcum, int B, int T, int H, int dk, int chunk, int softplus,
                                 hipStream_t stream);
 
+// Opt-in range check of a log-decay input (KDA_VALIDATE=1 in the
+// environment: validate_requested()).  bounded != 0: every g in [gmin, 0];
+// otherwise g <= 0; finite in both cases.  With gcum != nullptr the per-row
+// decays it encodes are checked instead of g.  g / gcum are [B, T, HD]
+// (HD = H * dk).  Synchronises `stream`; *in_range = 1 if every value passes.
+bool validate_requested();
+hipError_t validate_decay(int is_bf16, const void* g, const float* gcum, int bounded, float gmin, int B, int T,
+                          int HD, int chunk, hipStream_t stream, int* in_range);
+
 // Bytes of one per-chunk record of the prefill workspace.
 size_t fwd_record_bytes(int is_bf16, int dk, int dv);
 // Workspace of the fused single-pass schedule (ring buffers + control words).
@@ -38,6 +47,11 @@ hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const vo
 
 // Zero-fills nwords 4-byte words on the stream (a kernel, not a memset node).
 hipError_t launch_zero_words(void* p, size_t nwords, hipStream_t stream);
+
+// Zeroes the status words (the first 16 ints, error word at [8]) of a
+// prefill workspace; called once per API call, before its launches.
+hipError_t launch_clear_status(void* ws, hipStream_t stream);
+
 
 // One decode token per (b, h), state updated in place.
 hipError_t launch_decode_step(int is_bf16, const void* q, const void* k, const void* v,

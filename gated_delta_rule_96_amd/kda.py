@@ -18,6 +18,7 @@ PKG = Path(__file__).resolve().parent
 LIB_PATH = PKG / "libkda.so"
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_ERR_UNSUPPORTED, KDA_ERR_RANGE, KDA_ERR_INCOMPLETE = 5, 7, 9
 KDA_STAGES_UNBOUNDED = 4
 KDA_LAYER_QK_L2NORM = 1
 CHUNK = 64
@@ -69,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.kda_bwd_workspace_bytes.restype = S
         L.kda_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kda_bwd_chunked.argtypes = [P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
+        L.kda_fwd_status.restype = I
+        L.kda_fwd_status.argtypes = [P, P]
+        L.kda_fwd_status_word.restype = P
+        L.kda_fwd_status_word.argtypes = [P]
         _lib = L
     return _lib
 
@@ -151,20 +156,32 @@ def alloc_workspace(B, T, H, dk, dv, dtype=torch.bfloat16, device="cuda", chunk=
 
 
 def workspace_error(workspace: torch.Tensor) -> int:
-    """Error word of a kda_fwd_chunked workspace (non-zero: a hand-off wait
-    timed out and the outputs are incomplete).  Synchronises the stream."""
-    return int(workspace[32:36].view(torch.int32).item())
+    """Status of the last call on a prefill (or backward) workspace through
+    kda_fwd_status: 0, or KDA_ERR_INCOMPLETE (9) when a hand-off wait of the
+    fused kernel expired and the outputs are incomplete.  Synchronises the
+    current stream."""
+    s = int(lib().kda_fwd_status(_ptr(workspace), _stream(workspace.device)))
+    if s not in (0, KDA_ERR_INCOMPLETE):
+        raise KDAError(s, "kda_fwd_status")
+    return s
+
+
+def check_workspace(workspace: torch.Tensor, where: str = "kda_fwd_status"):
+    """Raises KDAError(KDA_ERR_INCOMPLETE) if the last call on `workspace`
+    did not complete (synchronises the current stream)."""
+    _check(workspace_error(workspace), where)
 
 
 def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state=True, ht=None,
-                workspace=None, out=None, chunk=CHUNK, stages=None, unbounded=False):
+                workspace=None, out=None, chunk=CHUNK, stages=None, unbounded=False, check=False):
     """o, ht = fwd_chunked(q, k, v, g, beta, h0).  q,k,g [B,T,H,dk]; v [B,T,H,dv];
     beta [B,T,H] (bf16 or fp32); h0/ht [B,H,dk,dv] fp32; o [B,T,H,dv] fp32.
     ht may be h0 itself (in-place carry).  stages=None runs the fused
     single-pass schedule (kda_fwd_chunked); stages in {1, 2, 3} runs the
     two-kernel schedule (kda_fwd_chunked_stages) with that stage mask.
     unbounded=True: the log-decay has no lower bound (kda_fwd_chunked_unbounded,
-    or KDA_STAGES_UNBOUNDED added to the stage mask)."""
+    or KDA_STAGES_UNBOUNDED added to the stage mask).  check=True synchronises
+    and raises KDAError if the fused call did not complete (kda_fwd_status)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q)
@@ -189,6 +206,8 @@ def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state
     if stages is None:
         fn = lib().kda_fwd_chunked_unbounded if unbounded else lib().kda_fwd_chunked
         _check(fn(*args, _stream(q.device)), "kda_fwd_chunked_unbounded" if unbounded else "kda_fwd_chunked")
+        if check:
+            check_workspace(workspace, "kda_fwd_chunked")
     else:
         mask = int(stages) | (KDA_STAGES_UNBOUNDED if unbounded else 0)
         _check(lib().kda_fwd_chunked_stages(*args, mask, _stream(q.device)), "kda_fwd_chunked_stages")
@@ -196,7 +215,7 @@ def fwd_chunked(q, k, v, g, beta, h0=None, *, gcum=None, scale=None, final_state
 
 
 def fwd_chunked_layer(q, k, v, z, A, beta, h0=None, *, og=None, qk_l2norm=False, scale=None, final_state=True,
-                      ht=None, workspace=None, out=None, chunk=CHUNK):
+                      ht=None, workspace=None, out=None, chunk=CHUNK, check=False):
     """o, ht = fwd_chunked_layer(q, k, v, z, A, beta, h0): kda_fwd_chunked with
     the decay gate of z (A [H] fp32) fused into the kernel's scan, optional
     in-kernel q/k row L2 normalisation and optional sigmoid output gate og
@@ -221,6 +240,8 @@ def fwd_chunked_layer(q, k, v, z, A, beta, h0=None, *, og=None, qk_l2norm=False,
                                        float(scale), _ptr(h0), _ptr(ht if final_state else None), _ptr(o), flags,
                                        dt, B, T, H, dk, dv, chunk, _ptr(workspace), workspace.numel(),
                                        _stream(q.device)), "kda_fwd_chunked_layer")
+    if check:
+        check_workspace(workspace, "kda_fwd_chunked_layer")
     return o, (ht if final_state else None)
 
 
@@ -239,7 +260,7 @@ def varlen_snapshots(cu_seqlens, snap_every, chunk=CHUNK) -> int:
 
 
 def fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, h0=None, *, gcum=None, scale=None, snap_every=0, ht=None,
-                       workspace=None, out=None, chunk=CHUNK):
+                       workspace=None, out=None, chunk=CHUNK, check=False):
     """o, ht, snaps = fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, h0).
     N sequences packed along tokens: q,k,g [1,T,H,dk]; v [1,T,H,dv]; beta
     [1,T,H]; cu_seqlens host ints (N+1, from 0 to T); h0/ht [N,H,dk,dv] fp32.
@@ -267,6 +288,8 @@ def fwd_chunked_varlen(q, k, v, g, beta, cu_seqlens, h0=None, *, gcum=None, scal
                                         ctypes.cast(arr, ctypes.c_void_p), N, _ptr(h0), _ptr(ht), _ptr(o),
                                         _ptr(snaps), int(snap_every), dt, T, H, dk, dv, chunk, _ptr(workspace),
                                         workspace.numel(), _stream(q.device)), "kda_fwd_chunked_varlen")
+    if check:
+        check_workspace(workspace, "kda_fwd_chunked_varlen")
     if snaps is not None:
         snaps = snaps[:varlen_snapshots(cu_seqlens, snap_every, chunk)]
     return o, ht, snaps
@@ -281,12 +304,14 @@ def bwd_workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16, chunk=CHUNK) -> i
 
 
 def bwd_chunked(q, k, v, g, beta, h0, do, dht=None, *, scale=None, want_dh0=True, workspace=None, out=None,
-                chunk=CHUNK):
+                chunk=CHUNK, check=False):
     """Gradients of kda_fwd_chunked (kda_bwd_chunked): q, k, g [B,T,H,dk] and
     v [B,T,H,dv], beta [B,T,H] (bf16 or fp32), h0 [B,H,dk,dv] fp32 or None;
     do = dL/do [B,T,H,dv] fp32, dht = dL/dht [B,H,dk,dv] fp32 or None.
     Returns a dict of fp32 tensors dq, dk, dv, dg, dbeta and dh0 (None unless
-    want_dh0).  `out` may supply that dict to be filled in place."""
+    want_dh0).  `out` may supply that dict to be filled in place.  check=True
+    synchronises and raises KDAError if the forward recompute did not
+    complete."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q)
@@ -313,6 +338,8 @@ def bwd_chunked(q, k, v, g, beta, h0, do, dht=None, *, scale=None, want_dh0=True
                                  _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                                  _ptr(out["dbeta"]), _ptr(out.get("dh0")), dt, B, T, H, dk, dv, chunk,
                                  _ptr(workspace), workspace.numel(), _stream(dev)), "kda_bwd_chunked")
+    if check:
+        check_workspace(workspace, "kda_bwd_chunked (forward recompute)")
     return out
 
 

@@ -23,8 +23,9 @@
  * Conventions shared by every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller,
  *     contiguous row-major, 16-byte aligned.  Nothing is retained after the
- *     call returns.  The library never allocates device memory and keeps no
- *     mutable global state; calls are re-entrant.
+ *     call returns.  The library never allocates device memory; its only
+ *     device state is a word per GPU used by the opt-in range check (in the
+ *     code object, loaded with the library).  Calls are re-entrant.
  *   - Layouts: q, k, g, z : [B, T, H, dk];  v, o : [B, T, H, dv];
  *     beta : [B, T, H];  A : [H] (fp32);  states h0 / ht / state :
  *     [B, H, dk, dv] fp32 (key channel = row, value channel = column).
@@ -42,6 +43,25 @@
  *     enqueued on `stream` and the call returns without synchronising.
  *     Device faults surface at the caller's next synchronisation.
  *   - Return value: a kda_status code (0 = KDA_OK).
+ *   - Opt-in range check: with KDA_VALIDATE=1 in the environment, every call
+ *     that takes a log-decay g (or gcum) first checks it on the device and
+ *     returns KDA_ERR_RANGE without enqueuing anything if a value is outside
+ *     [gmin, 0] with gmin = -5 (the floor that keeps 16 rows of decay inside
+ *     the bf16 range, "Key claims" section 2.1.1), or is not finite; the
+ *     unbounded-decay calls accept any finite g <= 0.  For gcum the per-row
+ *     decays it encodes (differences of consecutive sums inside a chunk)
+ *     are checked, up to the rounding of the fp32 sums.  The check
+ *     synchronises `stream` and uses one library-owned device word per GPU
+ *     (checks running at once on one GPU are serialised).  Without it the
+ *     range is a precondition: a g below -5.5 overflows the rescaled bf16
+ *     tiles (inf/NaN outputs).
+ *   - Status of the fused prefill: its kernels hand work between
+ *     work-groups with bounded waits (about a second).  If one expires (the
+ *     GPU shared with other work that holds CUs), the call stops early and
+ *     sets the status word of its workspace; the outputs are then
+ *     incomplete.  The word is cleared at the start of every call and stays
+ *     set for the rest of it; read it with kda_fwd_status (synchronous) or
+ *     kda_fwd_status_word (its device address, for an asynchronous copy).
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -62,8 +82,11 @@ typedef enum kda_status {
   KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
   KDA_ERR_UNSUPPORTED = 5, /* dk / dv / chunk outside the supported set           */
   KDA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than kda_fwd_workspace_bytes */
-  KDA_ERR_RANGE = 7,       /* reserved: input value out of its documented range   */
-  KDA_ERR_HIP = 8          /* a HIP launch failed (hipGetLastError)               */
+  KDA_ERR_RANGE = 7,       /* a value outside its documented range (KDA_VALIDATE=1 */
+                           /* checks, and gmin of kda_prepare_decay)              */
+  KDA_ERR_HIP = 8,         /* a HIP launch failed (hipGetLastError)               */
+  KDA_ERR_INCOMPLETE = 9   /* kda_fwd_status: a hand-off wait of the fused        */
+                           /* prefill expired; the call's outputs are incomplete  */
 } kda_status;
 
 typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -84,8 +107,11 @@ const char* kda_status_str(int status);
  *               chunk of `chunk` tokens up to t (the rounded g in gate mode),
  *               accumulated in fp32.
  * At least one output (g in gate mode, or gcum) must be requested.
+ * gmin must lie in [-5, 0) (a lower floor would take 16 rows of decay out
+ * of the bf16 range the prefill's rescaled tiles rely on; the unbounded
+ * comparison has its own gate below).
  * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN,
- *         KDA_ERR_UNSUPPORTED (dk, chunk), KDA_ERR_HIP.
+ *         KDA_ERR_UNSUPPORTED (dk, chunk), KDA_ERR_RANGE (gmin), KDA_ERR_HIP.
  */
 int kda_prepare_decay(const void* z, const float* A, float gmin, void* g, float* gcum,
                       int dtype, int B, int T, int H, int dk, int chunk, void* stream);
@@ -126,11 +152,11 @@ size_t kda_fwd_stages_workspace_bytes(int B, int T, int H, int dk, int dv, int c
  * to the state pass through the workspace; the kernel needs every one of
  * its work-groups resident at once (one per CU), so it must not share the
  * GPU with other work that holds CUs for long; if a hand-off wait exceeds
- * its bound (about a second) the kernel stops early and sets the first error word
- * of the workspace (ints [8]), leaving the outputs incomplete.
- * Precondition, not checked: g in [gmin, 0] with gmin = -5.
+ * its bound (about a second) the kernel stops early and sets the status
+ * word of the workspace, leaving the outputs incomplete (kda_fwd_status).
+ * Precondition: g in [gmin, 0] with gmin = -5 (checked under KDA_VALIDATE=1).
  * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN,
- *         KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP.
+ *         KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_RANGE, KDA_ERR_HIP.
  */
 int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g,
                     const float* gcum, const void* beta, float scale, const float* h0,
@@ -145,7 +171,7 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g,
  * Gram matrices are then sums over position pairs in fp32 (each pair's
  * decay factor formed directly, never above 1); everything else is
  * unchanged.  Arguments, layouts, workspace, errors as kda_fwd_chunked;
- * precondition, not checked: g <= 0 and finite.
+ * precondition: g <= 0 and finite (checked under KDA_VALIDATE=1).
  */
 int kda_fwd_chunked_unbounded(const void* q, const void* k, const void* v, const void* g,
                               const float* gcum, const void* beta, float scale, const float* h0,
@@ -215,16 +241,34 @@ int kda_fwd_chunked_layer(const void* q, const void* k, const void* v, const voi
  * [S,H,dk,dv] fp32, sequences in order, snapshots in order within one;
  * S = kda_fwd_varlen_snapshots(cu_seqlens, N, snap_every, chunk).
  * workspace: kda_fwd_workspace_bytes(1, T, H, dk, dv, chunk, dtype) bytes.
- * One fused launch per non-empty sequence, in order on `stream`.
+ * One fused launch per non-empty sequence, in order on `stream`; the
+ * status word (kda_fwd_status) covers all of them.  gcum must be NULL (a
+ * gcum of the packed axis restarts at multiples of 64 tokens, not at each
+ * sequence's own chunks): KDA_ERR_UNSUPPORTED otherwise.
  * Errors: as kda_fwd_chunked; KDA_ERR_NULL for cu_seqlens == NULL,
  * KDA_ERR_SHAPE for inconsistent cu_seqlens or snap_every < 0,
- * KDA_ERR_ALIGN for an unaligned snap.
+ * KDA_ERR_ALIGN for an unaligned snap, KDA_ERR_UNSUPPORTED for gcum.
  */
 int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const void* g,
                            const float* gcum, const void* beta, float scale,
                            const int* cu_seqlens, int N, const float* h0, float* ht, float* o,
                            float* snap, int snap_every, int dtype, int T, int H, int dk, int dv,
                            int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Status of the last call that used `workspace` (a workspace of the fused
+ * prefill calls: kda_fwd_chunked, _unbounded, _layer, _varlen, or of
+ * kda_bwd_chunked, whose forward recompute it covers): synchronises
+ * `stream`, then returns KDA_OK, or KDA_ERR_INCOMPLETE if a hand-off wait
+ * of that call expired (its outputs are incomplete).  Errors: KDA_ERR_NULL,
+ * KDA_ERR_ALIGN (workspace not 256-byte aligned), KDA_ERR_HIP.
+ */
+int kda_fwd_status(const void* workspace, void* stream);
+
+/* Device address of the status word of `workspace` (one int; non-zero =
+ * KDA_ERR_INCOMPLETE as above), for an asynchronous read ordered after the
+ * call on its stream.  NULL for a NULL workspace. */
+const int* kda_fwd_status_word(const void* workspace);
 
 /* Number of snapshots kda_fwd_chunked_varlen writes for these sequences
  * (host computation; -1 for invalid arguments, including snap_every <= 0). */
@@ -235,8 +279,9 @@ long long kda_fwd_varlen_snapshots(const int* cu_seqlens, int N, int snap_every,
  * Details": fixed-size running state instead of a KV cache): one new token
  * per (b, h).  state [B,H,dk,dv] fp32 is read and overwritten in place with
  * S_t; o[b,h,:] = scale * S_t^T q.
+ * Precondition: g in [gmin, 0] with gmin = -5 (checked under KDA_VALIDATE=1).
  * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN,
- *         KDA_ERR_UNSUPPORTED, KDA_ERR_HIP.
+ *         KDA_ERR_UNSUPPORTED, KDA_ERR_RANGE, KDA_ERR_HIP.
  */
 int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
                     const void* beta, float scale, float* state, float* o, int dtype,
@@ -259,7 +304,9 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
  * The call recomputes the forward pass (keeping the state entering every
  * chunk) inside `workspace` of at least kda_bwd_workspace_bytes bytes
  * (256-byte aligned, owned by the caller, contents undefined afterwards);
- * it allocates nothing and returns without synchronising.
+ * it allocates nothing and returns without synchronising.  The recompute
+ * is the fused prefill: kda_fwd_status(workspace) reports whether it
+ * completed (gradients are meaningless otherwise).
  * Errors: as kda_fwd_chunked, KDA_ERR_NULL also for a NULL dout or output.
  */
 size_t kda_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);

@@ -187,3 +187,35 @@ def test_bwd_workspace_bytes():
     assert n2 - n1 >= 99 * 2 * (3 * 128 * 128 * 4)
     assert L.kda_bwd_workspace_bytes(1, 64, 2, 96, 128, 64, 1) == 0
     assert L.kda_bwd_workspace_bytes(1, 64, 2, 128, 128, 32, 1) == 0
+
+
+def test_status_codes_and_status_word():
+    L = kda.lib()
+    assert "incomplete" in kda.status_str(kda.KDA_ERR_INCOMPLETE)
+    assert "range" in kda.status_str(kda.KDA_ERR_RANGE)
+    # the status word sits at ints [8] of a (256-byte aligned) workspace
+    assert L.kda_fwd_status_word(FAKE) == FAKE + 32
+    assert L.kda_fwd_status_word(None) is None
+    # kda_fwd_status validates before it touches the device
+    assert L.kda_fwd_status(None, None) == 1
+    assert L.kda_fwd_status(FAKE + 16, None) == 4
+
+
+def test_gate_floor_outside_supported_range_is_rejected():
+    # the bounded gate's floor keeps 16 rows of decay within the bf16 range
+    # only for gmin >= -5 ("Key claims", section 2.1.1); a floor at or
+    # above 0 is no decay gate at all
+    L = kda.lib()
+    for gmin in (-5.5, -6.0, 0.0, 1.0, float("nan"), float("-inf")):
+        assert L.kda_prepare_decay(FAKE, FAKE, gmin, FAKE, None, 1, 1, 64, 1, 128, 64, None) == kda.KDA_ERR_RANGE
+    # the unbounded gate has no floor argument; scan mode ignores gmin
+    assert L.kda_prepare_decay(None, None, -9.0, FAKE, FAKE, 1, 0, 64, 1, 128, 64, None) == 2
+
+
+def test_varlen_rejects_packed_gcum():
+    # a gcum of the packed token axis restarts at multiples of 64 tokens, not
+    # at each sequence's own chunks
+    L = kda.lib()
+    cu = (ctypes.c_int * 3)(0, 30, 100)
+    assert L.kda_fwd_chunked_varlen(FAKE, FAKE, FAKE, None, FAKE, FAKE, 0.1, cu, 2, None, None, FAKE, None, 0, 1,
+                                    100, 2, 128, 128, 64, FAKE, 1 << 40, None) == kda.KDA_ERR_UNSUPPORTED
