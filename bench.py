@@ -11,9 +11,21 @@ the timed region starts.
 Printed: ONE JSON line with the prefill tokens/s (value), the roofline of
 the prefill call (HBM-bound: algorithmic bytes / measured time), the MFMA
 fraction on the algorithmic flop count, per-kernel times (HIP events on the
-launch stream), the batched decode step (B=256, H=32, 1000 steps) against
-the HBM roofline, a parity check of the timed output against the CPU oracle
-on a sample, and the CPU oracle's own throughput (cpu_baseline).
+launch stream), the B=4 H=16 T=8192 prefill and the million-token prefill
+(16 segments of 65536 carrying the state) with the linear-cost check, the
+batched decode step (B=256, H=32, 1000 steps) against the HBM roofline, a
+parity check of the timed output against the CPU oracle on a sample, and the
+CPU oracle's own throughput (cpu_baseline).
+
+Profiling helpers (for rocprofv3 runs; they print no JSON line):
+  bench.py --probe fused|stages|copy [--calls N]
+      a few calls of one prefill schedule on the benchmark workload, or a
+      plain 1 GiB device copy that calibrates the memory counters;
+  bench.py --summarize RESULTS.db|kernel_stats.csv
+      the kernel trace as a short table;
+  bench.py --summarize-pmc KERNEL FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv COPY_BYTES
+      FETCH_SIZE / WRITE_SIZE of one kernel scaled by what they read for
+      the copy of COPY_BYTES, as HBM bytes per launch.
 """
 from __future__ import annotations
 
@@ -36,30 +48,45 @@ METRIC = "KDA chunked prefill tokens/s + % bf16 MFMA peak (T=64K); decode % HBM 
 
 # prefill workload
 B, H, T, DK, DV, CHUNK = 1, 32, 65536, 128, 128, 64
+# the other prefill workloads: B=4 H=16 T=8192, and 16 segments of 65536 (1M tokens)
+C1 = (4, 16, 8192)
+C3_SEGMENTS = 16
 # decode workload
 DB, DH, DSTEPS, DPOOL = 256, 32, 1000, 8
 
 
-def prefill_alg_counts(B, T, H, dk, dv, C=64):
+def prefill_alg_counts(B, T, H, dk, dv, C=64, out_bytes=2):
     """Algorithmic flop and HBM bytes of one prefill call (no dense upper-triangle
     work, no intermediates): per token-head 6 dk dv + 1.25 C (3 dk + 2 dv) + C^2/3
-    flop; bytes = bf16 q, k, g, v, beta read, fp32 o written, fp32 h0 read and ht
-    written."""
+    flop; bytes = bf16 q, k, g, v, beta read and o written at `out_bytes` per
+    element (2: the 1282 B per token-head of a bf16 output at dk = dv = 128;
+    4: the fp32 output this library writes, 1538 B), plus fp32 h0 read and
+    ht written per (b, h)."""
     th = B * T * H
     flop = th * (6 * dk * dv + 1.25 * C * (3 * dk + 2 * dv) + C * C / 3.0)
-    bytes_ = th * (2 * (3 * dk + dv) + 2 + 4 * dv) + B * H * 2 * 4 * dk * dv
+    bytes_ = th * (2 * (3 * dk + dv) + 2 + out_bytes * dv) + B * H * 2 * 4 * dk * dv
     return flop, bytes_
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kda_fused_fwd_B1H32T65536_hbm_traffic.txt")
+KERNEL_SOURCES = ("kda_chunk.hip", "kda_device.h")
+
+
+def source_sha256() -> str:
+    """sha256 over the fused prefill kernel's sources (the code the counters describe)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_96_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per fused prefill launch from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
     summary is missing or was taken on other kernel sources."""
-    from gated_delta_rule_96_amd import profsum
-
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     vals = {}
@@ -68,12 +95,101 @@ def measured_traffic():
             if ":" in line:
                 key, val = line.split(":", 1)
                 vals[key.strip()] = val.strip()
-    if vals.get("source_sha256") != profsum.source_sha256():
+    if vals.get("source_sha256") != source_sha256():
         return None
     try:
         return int(float(vals["traffic_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+# ---------------------------------------------------------------- profiling helpers
+COPY_BYTES = 1 << 30
+
+
+def probe(what: str, calls: int):
+    """A few calls of one prefill schedule on the benchmark workload (or a
+    plain device copy of COPY_BYTES, which reads and writes exactly that many
+    bytes and so calibrates FETCH_SIZE / WRITE_SIZE), for rocprofv3 runs."""
+    import torch
+
+    from gated_delta_rule_96_amd import kda, synth
+
+    dev = torch.device("cuda:0")
+    if what == "copy":
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(calls):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[probe] copy of {COPY_BYTES} bytes x {calls}", file=sys.stderr, flush=True)
+        return
+    d = synth.make_inputs(B, T, H, DK, DV, seed=2)
+    bf = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+    q, k, v, beta, z = (bf(d[n]) for n in ("q", "k", "v", "beta", "z"))
+    A = torch.from_numpy(d["A"].copy()).to(dev)
+    h0 = torch.from_numpy(d["h0"]).to(dev)
+    g, _ = kda.prepare_decay(z, A, want_gcum=False)
+    stages = what == "stages"
+    ws = kda.alloc_workspace(B, T, H, DK, DV, torch.bfloat16, dev, stages=stages)
+    o = torch.empty((B, T, H, DV), dtype=torch.float32, device=dev)
+    ht = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    for _ in range(calls):
+        kda.fwd_chunked(q, k, v, g, beta, h0, ht=ht, workspace=ws, out=o, stages=3 if stages else None)
+    torch.cuda.synchronize()
+    print(f"[probe] {what} x {calls} done", file=sys.stderr, flush=True)
+
+
+def summarize_trace(path: str):
+    """Kernel trace (rocpd SQLite database or kernel_stats CSV) as a table:
+    kernel, calls, total and average duration (us), share of GPU time."""
+    import csv
+    import sqlite3
+
+    if path.endswith(".db"):
+        con = sqlite3.connect(path)
+        cur = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels")
+        rows = [(r[0], int(r[1]), float(r[2]), float(r[3]), float(r[4])) for r in cur]   # microseconds
+    else:
+        with open(path) as f:
+            rows = [(r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3, float(r["AverageNs"]) / 1e3,
+                     float(r["Percentage"])) for r in csv.DictReader(f)]
+    print(f"{'kernel':<60} {'calls':>6} {'total_us':>12} {'avg_us':>10} {'pct':>6}")
+    for name, calls, tot, avg, pct in rows:
+        short = name if len(name) <= 60 else name[:57] + "..."
+        print(f"{short:<60} {calls:>6} {tot:>12.1f} {avg:>10.2f} {pct:>6.2f}")
+
+
+def summarize_pmc(kernel_sub, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernels whose name
+    contains kernel_sub, each scaled by copy_bytes / (the same counter for the
+    copy), as HBM bytes per launch; records the kernel sources' sha256."""
+    import csv
+
+    def per_dispatch(path, counter, sub):
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and sub in r["Kernel_Name"]:
+                    per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not per:
+            raise SystemExit(f"no {counter} rows for kernels matching {sub!r} in {path}")
+        return sum(per.values()) / len(per), len(per)
+
+    copy_bytes = float(copy_bytes)
+    cf, ncf = per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    cw, ncw = per_dispatch(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    kf, nkf = per_dispatch(fetch_csv, "FETCH_SIZE", kernel_sub)
+    kw, nkw = per_dispatch(write_csv, "WRITE_SIZE", kernel_sub)
+    sf, sw = copy_bytes / cf, copy_bytes / cw
+    print(f"kernel: {kernel_sub}")
+    print(f"copy calibration: {copy_bytes:.0f} bytes each way; FETCH_SIZE {cf:.1f} KiB/dispatch "
+          f"({ncf} dispatches) -> scale {sf:.4f} bytes per unit; WRITE_SIZE {cw:.1f} KiB/dispatch "
+          f"({ncw}) -> scale {sw:.4f}")
+    print(f"kernel FETCH_SIZE {kf:.1f} KiB/dispatch ({nkf} dispatches) -> {kf * sf:.0f} bytes read")
+    print(f"kernel WRITE_SIZE {kw:.1f} KiB/dispatch ({nkw} dispatches) -> {kw * sw:.0f} bytes written")
+    print(f"traffic_bytes_per_launch: {kf * sf + kw * sw:.0f}")
+    print(f"source_sha256: {source_sha256()}")
 
 
 def bwd_alg_counts(B, T, H, dk, dv, C=64):
@@ -93,6 +209,166 @@ def decode_alg_bytes(B, H, dk, dv):
     return B * H * (2 * 4 * dk * dv + 2 * (3 * dk + dv) + 2 + 4 * dv)
 
 
+def extra_configs(args, torch, kda, synth, dev, stream, log, ms_c2):
+    """The other two prefill workloads, timed like the headline one:
+    B=4 H=16 T=8192 (inputs from synth, oracle parity on every head) and the
+    million-token prefill B=1 H=32 as 16 segments of 65536 carrying the fp32
+    state in place (inputs drawn on the device with the same distributions;
+    segment 0's four sampled heads from synth, checked against the oracle,
+    whose time on them is extrapolated to the whole run).  Then the
+    linear-cost check: throughput per token-head of the three prefills."""
+    BF = torch.bfloat16
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(BF)
+
+    def timed(fn, n):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    out = {}
+    # ---- B=4 H=16 T=8192
+    Bc, Hc, Tc = C1
+    log(f"prefill B={Bc} H={Hc} T={Tc}")
+    d = synth.make_inputs(Bc, Tc, Hc, DK, DV, seed=21)
+    host = {n: bf(d[n]) for n in ("q", "k", "v", "beta", "z")}
+    q, k, v, beta, z = (host[n].to(dev) for n in ("q", "k", "v", "beta", "z"))
+    A = torch.from_numpy(d["A"].copy()).to(dev)
+    h0 = torch.from_numpy(d["h0"]).to(dev)
+    g, _ = kda.prepare_decay(z, A, want_gcum=False)
+    ws = kda.alloc_workspace(Bc, Tc, Hc, DK, DV, BF, dev)
+    o = torch.empty((Bc, Tc, Hc, DV), dtype=torch.float32, device=dev)
+    ht = torch.empty((Bc, Hc, DK, DV), dtype=torch.float32, device=dev)
+    ms1 = timed(lambda: kda.fwd_chunked(q, k, v, g, beta, h0, ht=ht, workspace=ws, out=o), max(5, args.steps))
+    kda.check_workspace(ws)
+    c1 = {"workload": f"KDA chunked prefill B={Bc} H={Hc} T={Tc} dk=dv={DK}, bf16 inputs, fp32 state and output",
+          "ms_per_call": round(ms1, 4), "tokens_per_s": round(Bc * Tc / (ms1 * 1e-3), 1),
+          "token_heads_per_s": round(Bc * Tc * Hc / (ms1 * 1e-3), 1)}
+    if not args.no_cpu_baseline:
+        from oracle import gate as ogate
+        from oracle import seq
+
+        f = lambda t: t.float().numpy()
+        g_ref = f(bf(ogate.gate(f(host["z"]), d["A"]).astype(np.float32)))
+        t0 = time.perf_counter()
+        o_ref, h_ref = seq.kda_seq(f(host["q"]), f(host["k"]), f(host["v"]), g_ref, f(host["beta"]), d["h0"],
+                                   nthreads=seq.threads_default())
+        c1_cpu = time.perf_counter() - t0
+        rms = lambda x: math.sqrt(float(np.mean(x * x)))
+        c1["parity"] = {"sample": "every output and final state, all heads, vs fp64 oracle (its own gate of the "
+                                  "same z, rounded to bf16)",
+                        "max_err_over_rms_o": float(np.max(np.abs(o.cpu().double().numpy() - o_ref)) / rms(o_ref)),
+                        "max_err_over_rms_ht": float(np.max(np.abs(ht.cpu().double().numpy() - h_ref)) / rms(h_ref)),
+                        "tolerance": 2e-2}
+        c1["cpu_oracle_tokens_per_s"] = round(Bc * Tc / c1_cpu, 1)
+    out["B4_H16_T8192"] = c1
+    log(f"  {ms1:.3f} ms per call" + (f"; parity o {c1['parity']['max_err_over_rms_o']:.2e}" if "parity" in c1 else ""))
+    del q, k, v, beta, z, g, o, ht, ws, host, d
+
+    # ---- 1M tokens: 16 segments of 65536, state carried in place
+    nseg, heads = C3_SEGMENTS, [0, 9, 18, 27]
+    log(f"million-token prefill: {nseg} segments of {T}, B={B} H={H}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(23)
+    A = torch.from_numpy(synth.head_A(23, H).copy()).to(dev)
+    unit = lambda x: x / x.norm(dim=-1, keepdim=True)
+    segs = []
+    for s in range(nseg):
+        shp = (B, T, H, DK)
+        x = {"q": unit(torch.randn(shp, generator=gen, device=dev)), "k": unit(torch.randn(shp, generator=gen,
+                                                                                           device=dev)),
+             "z": torch.randn(shp, generator=gen, device=dev), "v": torch.randn(shp, generator=gen, device=dev),
+             "beta": torch.sigmoid(torch.randn((B, T, H), generator=gen, device=dev))}
+        if s == 0:
+            ds = synth.make_inputs(B, T, H, DK, DV, seed=23, part=0, with_h0=False, heads=heads)
+            for n in x:
+                x[n][:, :, heads] = torch.from_numpy(ds[n]).to(dev)
+        x = {n: t_.to(BF) for n, t_ in x.items()}
+        x["g"] = kda.prepare_decay(x["z"], A, want_gcum=False)[0]
+        del x["z"]
+        segs.append(x)
+    h0_host = synth.initial_state(23, B, H, DK, DV)
+    h0 = torch.from_numpy(h0_host).to(dev)
+    state = torch.empty_like(h0)
+    ws = kda.alloc_workspace(B, T, H, DK, DV, BF, dev)
+    o = torch.empty((B, T, H, DV), dtype=torch.float32, device=dev)
+    o0 = torch.empty_like(o)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)]
+
+    def one_pass(record):
+        state.copy_(h0)
+        for s, x in enumerate(segs):
+            if record:
+                evs[s].record(stream)
+            kda.fwd_chunked(x["q"], x["k"], x["v"], x["g"], x["beta"], state, ht=state, workspace=ws,
+                            out=o0 if s == 0 else o)
+        if record:
+            evs[nseg].record(stream)
+
+    one_pass(False)
+    torch.cuda.synchronize()
+    reps = max(2, args.steps // 8)
+    tot, per_seg = 0.0, np.zeros(nseg)
+    for _ in range(reps):
+        one_pass(True)
+        torch.cuda.synchronize()
+        seg_ms = np.array([evs[s].elapsed_time(evs[s + 1]) for s in range(nseg)])
+        per_seg += seg_ms
+        tot += seg_ms.sum()
+    kda.check_workspace(ws)
+    ms3 = tot / reps
+    per_seg /= reps
+    c3 = {"workload": f"KDA million-token prefill B={B} H={H} T={nseg * T} as {nseg} segments of {T} carrying the "
+                      f"fp32 state in place, bf16 inputs (drawn on the device, same distributions)",
+          "ms_per_pass": round(ms3, 4), "tokens_per_s": round(B * nseg * T / (ms3 * 1e-3), 1),
+          "token_heads_per_s": round(B * nseg * T * H / (ms3 * 1e-3), 1),
+          "segment_ms": [round(float(x), 4) for x in per_seg]}
+    if not args.no_cpu_baseline:
+        from oracle import gate as ogate
+        from oracle import seq
+
+        f = lambda t_: t_.float().numpy()
+        sel = lambda n: f(bf(ds[n]))
+        g_ref = f(bf(ogate.gate(sel("z"), synth.head_A(23, H)[heads]).astype(np.float32)))
+        t0 = time.perf_counter()
+        o_ref, _ = seq.kda_seq(sel("q"), sel("k"), sel("v"), g_ref, sel("beta"), h0_host[:, heads],
+                               nthreads=seq.threads_default())
+        cpu_s = time.perf_counter() - t0
+        o_gpu = o0[:, :, heads].cpu().double().numpy()
+        rms = math.sqrt(float(np.mean(o_ref * o_ref)))
+        c3["parity"] = {"sample": f"segment 0, heads {heads}, every output, vs fp64 oracle",
+                        "max_err_over_rms": float(np.max(np.abs(o_gpu - o_ref)) / rms), "tolerance": 2e-2}
+        rate = len(heads) * T / cpu_s
+        c3["cpu_oracle"] = {"sample": f"{len(heads)} heads x {T} tokens (segment 0), {cpu_s:.2f} s on "
+                                      f"{min(len(heads), seq.threads_default())} threads (one per head)",
+                            "token_heads_per_s": round(rate, 1),
+                            "extrapolated_s_for_whole_run": round(B * nseg * T * H / rate, 1),
+                            "extrapolation": "labelled estimate: the measured per-token-head rate times the run's "
+                                             f"{B * nseg * T * H} token-heads"}
+    out["B1_H32_T1048576_16_segments"] = c3
+    log(f"  {ms3:.3f} ms per pass ({ms3 / nseg:.3f} ms per segment)"
+        + (f"; parity {c3['parity']['max_err_over_rms']:.2e}" if "parity" in c3 else ""))
+    del segs, state, o, o0, ws
+
+    # ---- linear cost (page "How a Frontier Model Gets Built...", Technical
+    # Details: cost proportional to n): throughput per token-head should not
+    # depend on the length or the batch shape
+    th2 = B * T * H / (ms_c2 * 1e-3)
+    rates = {"B4_H16_T8192": c1["token_heads_per_s"], "B1_H32_T65536": round(th2, 1),
+             "B1_H32_T1048576_16_segments": c3["token_heads_per_s"]}
+    ratio = {n: round(r / th2, 4) for n, r in rates.items()}
+    out["linear_cost_check"] = {"token_heads_per_s": rates, "ratio_to_T65536": ratio,
+                                "within_15_percent": all(0.85 <= x <= 1.15 for x in ratio.values()),
+                                "note": "token-heads/s (the configurations differ in H, so tokens/s alone would "
+                                        "compare different work per token)"}
+    log(f"  linear cost: ratios to T=65536 {ratio}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,7 +381,22 @@ def main():
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the B=4 H=16 T=8192 and million-token prefill lines")
+    ap.add_argument("--probe", choices=("fused", "stages", "copy"))
+    ap.add_argument("--calls", type=int, default=3)
+    ap.add_argument("--summarize")
+    ap.add_argument("--summarize-pmc", nargs=6)
     args = ap.parse_args()
+    if args.summarize:
+        summarize_trace(args.summarize)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.probe:
+        probe(args.probe, args.calls)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards by "
               "(batch, head) with no exchange, see DESIGN.md).", file=sys.stderr)
@@ -177,6 +468,29 @@ def main():
     log(f"two-kernel schedule: intra-chunk {ms_intra:.3f} ms + state pass {ms_state:.3f} ms; same output {same}")
 
     flop, abytes = prefill_alg_counts(B, T, H, DK, DV, CHUNK)
+    _, abytes32 = prefill_alg_counts(B, T, H, DK, DV, CHUNK, out_bytes=4)
+
+    # ---------------- decay gate (z -> g) at the same shape, on its own
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g_tmp = torch.empty_like(g)
+
+    def gate_call():
+        kda.lib().kda_prepare_decay(z.data_ptr(), A.data_ptr(), -5.0, g_tmp.data_ptr(), None, kda.KDA_BF16, B, T, H,
+                                    DK, CHUNK, stream.cuda_stream)
+
+    gate_call()
+    e0.record(stream)
+    for _ in range(n_k):
+        gate_call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_gate = e0.elapsed_time(e1) / n_k
+    gate_bytes = 2 * 2 * B * T * H * DK + 4 * H
+    assert torch.equal(g_tmp, g)
+    del g_tmp
+    log(f"decay gate z -> g: {ms_gate * 1e3:.1f} us ({gate_bytes / (ms_gate * 1e-3) / 1e9:.0f} GB/s)")
+
+    extra = None if args.no_extra_configs else extra_configs(args, torch, kda, synth, dev, stream, log, ms_step)
 
     # ---------------- unbounded-decay ablation: the same workload through the
     # kernel for a log-decay with no lower bound (diagonal tiles by position
@@ -425,6 +739,7 @@ def main():
 
     tok_s = B * T / (ms_step * 1e-3)
     gbs = abytes / (ms_step * 1e-3) / 1e9
+    gbs32 = abytes32 / (ms_step * 1e-3) / 1e9
     tflops = flop / (ms_step * 1e-3) / 1e12
     bind_ms = max(flop / (BF16_PEAK_TFLOPS * 1e12), abytes / (HBM_PEAK_GBS * 1e9)) * 1e3
 
@@ -508,15 +823,23 @@ def main():
                    "B": B, "H": H, "T": T, "dk": DK, "dv": DV, "chunk": CHUNK},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "fused_fwd_kernel (one launch per call, + a small flag-clearing kernel)",
-                     "alg_bytes_per_call": int(abytes)},
+                     "kernel": "fused_fwd_kernel (one launch per call, after two 64-thread flag-clearing kernels; "
+                               "HIP events bracket the whole call)",
+                     "alg_bytes_per_call": int(abytes),
+                     "alg_bytes_basis": "1282 B per token-head (bf16 q, k, g, v read, o counted at 2 B, beta) "
+                                        "+ fp32 h0 read and ht written per head",
+                     "frac_with_fp32_output": round(gbs32 / HBM_PEAK_GBS, 4),
+                     "alg_bytes_per_call_fp32_output": int(abytes32)},
         "mfma": {"achieved_tflops": round(tflops, 2), "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "alg_flop_per_call": int(flop)},
         "binding_roofline_frac": round(bind_ms / ms_step, 4),
         "kernels_ms": {"fused_fwd_kernel (per call)": round(ms_step, 4),
+                       "prepare_decay_kernel (gate z -> g, same shape)": round(ms_gate, 4),
+                       "prepare_decay_gbs": round(gate_bytes / (ms_gate * 1e-3) / 1e9, 1),
                        "two_kernel_schedule": {"intra_chunk_kernel": round(ms_intra, 4),
                                                "state_pass_kernel": round(ms_state, 4),
                                                "bitwise_equal_output": same}},
+        "other_prefill_configs": extra,
         "decode": decode,
         "unbounded_decay_ablation": ablation,
         "varlen_snapshots": varlen,

@@ -12,8 +12,14 @@ bf16 products in bf16 mode).  Gradients are heavy-tailed (max |ref| reaches
 150x rms(ref) where dht enters the last chunk, and dg sums contributions tens
 of times larger than itself), and fp32 arithmetic leaves each element an error
 proportional to its own size; a bound on max error over rms alone would ask
-the largest elements for precision below fp32's.  max error over rms is
-printed as well.
+the largest elements for precision below fp32's.
+
+The forward's rule, max |x - ref| <= tau_mr * rms(ref), is asserted as well:
+tau_mr = tau for every gradient, except dg with fp32 inputs, whose bar is
+10 tau.  dg is the reverse cumulative sum over a chunk of row and column
+terms tens of times larger than dg itself, so the fp32 rounding of those
+terms (relative 2^-24 each, summed over up to 64 rows) lands on dg at
+several 1e-5 of rms(dg) where |dg| peaks (measured up to 2.4e-4).
 """
 import numpy as np
 import pytest
@@ -22,6 +28,10 @@ import torch
 from gated_delta_rule_96_amd import kda, synth
 from oracle import seq
 from kda_testutil import TOL, err_ratio, f32, prefill_case, say, to_dev
+
+
+def max_rms_bar(name, dtype) -> float:
+    return TOL[dtype] * (10.0 if (name == "dg" and dtype == torch.float32) else 1.0)
 
 
 def grad_err(x, ref) -> float:
@@ -60,6 +70,7 @@ def test_bwd_matches_oracle(dtype, B, T, H, dk, dv):
     for n in NAMES:
         assert np.isfinite(got[n]).all(), n
         assert errs[n] <= TOL[dtype], (n, errs[n])
+        assert err_ratio(got[n], ref[n]) <= max_rms_bar(n, dtype), (n, err_ratio(got[n], ref[n]))
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -69,6 +80,7 @@ def test_bwd_zero_state_and_no_final_gradient(dtype):
     got, ref = _run(1, 150, 2, 128, 128, 62, dtype, with_h0=False, with_dht=False)
     for n in NAMES:
         assert grad_err(got[n], ref[n]) <= TOL[dtype], n
+        assert err_ratio(got[n], ref[n]) <= max_rms_bar(n, dtype), n
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -108,3 +120,4 @@ def test_bwd_full_size_sampled_heads():
         e = grad_err(got, ref[n])
         say(f"  {n} element-wise {e:.2e} max/rms {err_ratio(got, ref[n]):.2e}")
         assert e <= TOL[torch.bfloat16], n
+        assert err_ratio(got, ref[n]) <= max_rms_bar(n, torch.bfloat16), n
