@@ -42,9 +42,10 @@
 // With fp32 inputs every operand is fp32 (v_mfma_f32_16x16x4_f32).
 //
 // Workspace record per (b, h, chunk), every matrix stored as 16x16 tiles in
-// MFMA lane order (tile = 64 lanes x 4 consecutive values), so the state
-// pass reads each operand with one contiguous vector load per lane:
-//   W  : tile (ct, rt) lane l = W[16rt + l%16][16ct + 4(l/16) + i]       (Op)
+// MFMA lane order (tile = 64 lanes x 4 consecutive values; the two tiles of
+// an operand slab interleaved lane by lane, tile_elem), so the state pass
+// reads each operand slab with one contiguous 16-byte load per lane:
+//   W  : tile (ct, rt) lane l = -W[16rt + l%16][16ct + 4(l/16) + i]      (Op)
 //   Q  : tile (ct, rt) lane l = Qbar[16rt + l%16][16ct + 4(l/16) + i]    (Op)
 //        with Qbar = scale e^Gamma * Q
 //   K  : tile (st, ct) lane l = Khat[16st + 4(l/16) + i][16ct + l%16]    (Op)
@@ -92,14 +93,21 @@ struct Rec {
 
 // Record tile order.  The state pass reads operand slabs made of two tiles
 // that are consecutive along the reduction index (reduction tiles 2s and
-// 2s + 1); those two tiles are stored next to each other, so one paired LDS
-// read puts a lane's slab straight into consecutive registers.
+// 2s + 1); those two tiles get consecutive indices (2j, 2j + 1), whose
+// values tile_elem interleaves per lane.
 //   W, Q, M tile (ct, rt), reduction tile ct, 4 row tiles rt
 __host__ __device__ constexpr int tile_cr(int ct, int rt) { return (ct >> 1) * 8 + rt * 2 + (ct & 1); }
 //   K tile (st, ct), reduction tile st, NCT column tiles ct
 template <int NCT> __host__ __device__ constexpr int tile_k(int st, int ct) {
   return (st >> 1) * (2 * NCT) + ct * 2 + (st & 1);
 }
+
+// Element offset of lane `lane`'s 4 values of record tile t (tiles of 256
+// elements, 64 lanes x 4 consecutive values).  The two tiles of an operand
+// slab, 2j and 2j + 1, are interleaved lane by lane: a lane's 8 values of
+// slab j are contiguous (16 bytes in fp16), so the state pass reads a slab
+// with one 16-byte load.
+__host__ __device__ constexpr int tile_elem(int t, int lane) { return (t >> 1) * 512 + lane * 8 + (t & 1) * 4; }
 
 typedef float raw16 __attribute__((ext_vector_type(4)));   // 16 raw bytes
 
@@ -556,7 +564,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       // diagonal tile from the position pairs of phase 0: scale M to the record
       // (lane holds M[16a + l16][16a + g4 + i]); A is already in place
       const float* md = sMd + t0i * 256 + l16 * 16 + g4;
-      store4<Op>(rM + tile_cr(t0i, t0i) * 256 + 4 * lane, narrow4<Op>(f32x4{md[0], md[1], md[2], md[3]}));
+      store4<Op>(rM + tile_elem(tile_cr(t0i, t0i), lane), narrow4<Op>(f32x4{md[0], md[1], md[2], md[3]}));
     } else if (ntile > 0) {
       // both tiles of a wave share the row block a, hence the row operand
       const int a = nib(kTileA, t0i);
@@ -607,14 +615,14 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
           mrow[i] = sc <= r ? accM[i] : 0.f;
         }
         *reinterpret_cast<f32x4*>(sA + r * L::LA + 16 * bb + g4) = arow;
-        store4<Op>(rM + tile_cr(bb, a) * 256 + 4 * lane, narrow4<Op>(mrow * scale));
+        store4<Op>(rM + tile_elem(tile_cr(bb, a), lane), narrow4<Op>(mrow * scale));
       }
     }
   }
   if (w >= 2) {   // the six tiles above the diagonal of the record's M are zero
     // (the mirror of lower tile (a, b): row block b, column block a)
     const int zt = w - 2, kt = nib(kTileA, 4 + zt), rt = nib(kTileB, 4 + zt);
-    store4<Op>(rM + tile_cr(kt, rt) * 256 + 4 * lane, narrow4<Op>(zero4()));
+    store4<Op>(rM + tile_elem(tile_cr(kt, rt), lane), narrow4<Op>(zero4()));
   }
   // V's range (for its fp16 staging): wave maxima of the chunk's v, combined
   // after the barrier
@@ -653,7 +661,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
         const int ct = t >> 2, rt = t & 3;
         const int row = 16 * rt + l16, col = 16 * ct + g4;
         const f32x4 f = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + col);
-        store4<Op>(rQ + tile_cr(ct, rt) * 256 + 4 * lane,
+        store4<Op>(rQ + tile_elem(tile_cr(ct, rt), lane),
                    narrow4<Op>(*reinterpret_cast<const f32x4*>(sQP + row * L::LG + col) * (f * scale)));
       } else {
         // Khat tile (st, ct): lane holds Khat[16st + g4 + i][16ct + l16]
@@ -663,7 +671,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
         f32x4 val;
 #pragma unroll
         for (int i = 0; i < 4; ++i) val[i] = sKE[(row0 + i) * L::LG + col] * e;
-        store4<Op>(rK + tile_k<DK / 16>(st, ct) * 256 + 4 * lane, narrow4<Op>(val));
+        store4<Op>(rK + tile_elem(tile_k<DK / 16>(st, ct), lane), narrow4<Op>(val));
       }
     }
   }
@@ -730,7 +738,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     int ct, rt;
     wave_tile(w, j, NQW, ct, rt);
     const f32x4 acc = tri_mma(sKbt + (16 * ct + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
-    store4<Op>(rW + tile_cr(ct, rt) * 256 + 4 * lane, narrow4<Op>(acc));
+    store4<Op>(rW + tile_elem(tile_cr(ct, rt), lane), narrow4<Op>(-acc));   // the record holds -W
   }
   constexpr int NUT = (DV / 16) * 4;
   constexpr int NUW = NUT / kNW;
@@ -750,7 +758,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   for (int j = 0; j < NUW; ++j) {
     int jt, st;
     wave_tile(w, j, NUW, jt, st);
-    store4<Op>(rU + (jt * 4 + st) * 256 + 4 * lane, narrow4<Op>(ut[j] * su));
+    store4<Op>(rU + tile_elem(jt * 4 + st, lane), narrow4<Op>(ut[j] * su));
   }
   if (tid == 0) *rUinv = suinv;
   return true;
@@ -776,12 +784,13 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __rest
 
 // ---------------------------------------------------------------------------
 // State pass over one head's chunks.  Waves 0..3 (one per SIMD) own the
-// value columns: wave w keeps the dk x (dv/4) slice S[:, w*dv/4 ...] in fp32
+// value columns: wave w keeps the dk x 16 slice of S it owns in fp32
 // accumulators for the whole sequence; waves 4..7 stage the records: each
 // chunk's record is copied into LDS once, and the next chunk's copy is
-// prefetched into their registers while the owners compute the current one.  With the whole record in LDS every operand tile read from LDS
-// feeds dv/64 MFMAs.  When the record does not fit (fp32 inputs with
-// dk = dv = 128), Ut and Ot stay in global memory and are read where used.
+// prefetched into their registers while the owners compute the current one.
+// Operand slabs are lane-interleaved in the record (tile_elem), so every
+// slab is one 16-byte LDS read.  When two records do not fit in LDS (fp32
+// inputs), one buffer is staged between two barriers.
 //
 // kRing = false: records of every chunk are stored one after another at
 //   recbase (two-stage schedule).
@@ -842,31 +851,55 @@ __device__ __forceinline__ int spin_until_geq(const int* p, int target, int* err
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 constexpr size_t kLdsMax = 160 * 1024;
-constexpr int kOwners = 4;   // waves that own value columns
+constexpr int kOwners = 4;   // waves that own value columns, 16 each
 
 // The state pass of one head runs on NS work-groups (value-column blocks
-// of dv / NS), each staging the record's shared part (W, Qbar, Khat, M,
-// dec, uinv) and its own Ut columns.  LDS: NBUF such buffers (two when they
-// fit, so that the next chunk is staged while the current one is computed)
-// + abort word.
+// of dv / NS = 64 columns), each staging the record's shared part (W, Qbar,
+// Khat, M, dec, uinv) and its own Ut columns.  LDS: NBUF such buffers (two
+// when they fit, so that the next chunk is staged while the current one is
+// computed) + abort word.
 template <typename TIn, int DK, int DV>
 struct ConsumerLds {
   using R = Rec<TIn, DK, DV>;
   using Op = typename Policy<TIn>::Op;
-  static constexpr int NS = DV >= 128 ? 2 : 1;
+  static constexpr int NS = DV / (16 * kOwners);
   static constexpr size_t SH = R::U_OFF_BYTES;
   static constexpr size_t UPART = (size_t)kC * (DV / NS) * sizeof(Op);
   static constexpr size_t USED = SH + UPART;
-  // output-gate values of the chunk's rows and this work-group's columns
-  // (input type, row-major [C][dv / NS]), staged after the record
-  static constexpr size_t OGB = (size_t)kC * (DV / NS) * sizeof(TIn);
-  static constexpr size_t OG_OFF = (USED + 15) / 16 * 16;
-  static constexpr size_t BUF = (OG_OFF + OGB + 255) / 256 * 256;
+  static constexpr size_t BUF = (USED + 255) / 256 * 256;
   static constexpr int NBUF = 2 * BUF + 16 <= kLdsMax ? 2 : 1;
   static constexpr size_t BYTES = NBUF * BUF + 16;
+  static_assert(NS * 16 * kOwners == DV, "dv must be 64 or 128");
   static_assert(BUF + 16 <= kLdsMax, "record does not fit in LDS");
   static_assert(SH % 16 == 0 && UPART % 16 == 0, "16-byte staging");
 };
+
+// The state pass's fp16 domain: Sh = sigma S and Uh = sigma U with sigma a
+// power of two.  kFp16Safe bounds what converts to fp16 without overflow.
+constexpr float kFp16Safe = 65000.f;
+// Exponent k with m * 2^k in [2^12, 2^13) for finite m > 0; 0 otherwise.
+__device__ __forceinline__ int fp16_domain_exp(float m) {
+  const int ex = (int)((__float_as_uint(m) >> 23) & 0xffu);
+  if (!(m > 0.f) || ex == 0xff) return 0;
+  const int k = 12 - (ex - 127);
+  return k < -100 ? -100 : (k > 100 ? 100 : k);
+}
+// Exponent step moving a domain maximum m into [2^12, 2^13), limited so that
+// sigma = 2^se stays within 2^-120 .. 2^120 (a state that has decayed to
+// nothing keeps its last sigma).
+__device__ __forceinline__ int domain_rescale_exp(float m, int se) {
+  const int k = fp16_domain_exp(m);
+  return (se + k > 120 || se + k < -120) ? 0 : k;
+}
+
+// One lane's slab of 8 reduction indices, stored contiguously (tile_elem).
+template <typename T> __device__ __forceinline__ Slab<T> load_slab8(const T* p);
+template <> __device__ __forceinline__ Slab<f16> load_slab8<f16>(const f16* p) {
+  return Slab<f16>{*reinterpret_cast<const f16x8*>(p)};
+}
+template <> __device__ __forceinline__ Slab<float> load_slab8<float>(const float* p) {
+  return Slab<float>{load4(p), load4(p + 4)};
+}
 
 // Prefix-state snapshots: with p != nullptr and every > 0, the state after
 // chunk c (c + 1 a multiple of `every`, and not the sequence's end, which
@@ -891,19 +924,17 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   using CL = ConsumerLds<TIn, DK, DV>;
   constexpr int NBUF = CL::NBUF;
   constexpr int NCT = DK / 16;
-  constexpr int NJ = DV / CL::NS / 16 / kOwners;   // column tiles per owner wave
   constexpr int NV16 = CL::USED / 16;
   constexpr int NSH16 = CL::SH / 16;
   constexpr int kHelpers = kThreads - 64 * kOwners;   // threads of the staging waves
   constexpr int PPT = (NV16 + kHelpers - 1) / kHelpers;
-  static_assert(NJ >= 1 && NJ * kOwners * 16 * CL::NS == DV, "dv must be a multiple of 64");
   int* sAbort = reinterpret_cast<int*>(smem + NBUF * CL::BUF);
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = 4 * (lane >> 4);
   const bool owner = w < kOwners;   // wave-uniform
-  const int jl0 = (owner ? w : 0) * NJ;           // first local column tile
-  const int jt0 = vb * NJ * kOwners + jl0;        // first column tile of the head
+  const int jl0 = owner ? w : 0;                   // local column tile
+  const int jt0 = vb * kOwners + jl0;              // column tile of the head
   const size_t bh = (size_t)b * H + h;
   auto rec_of = [&](int c) { return recbase + (size_t)(kRing ? c % ring.R : c) * R::BYTES; };
   auto buf_of = [&](int c) { return smem + (size_t)(NBUF == 2 ? (c & 1) : 0) * CL::BUF; };
@@ -930,10 +961,6 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   if (!owner) {
     const int htid = tid - 64 * kOwners;
     raw16 pre[PPT];
-    // output gate rows of a chunk: 16-byte pieces, row-major over the columns
-    constexpr int OGV = DV / CL::NS * (int)sizeof(TIn) / 16;   // pieces per row
-    constexpr int OGN = (kC * OGV + kHelpers - 1) / kHelpers;
-    raw16 preg[OGN];
     bool ok = true;
     // true once chunk c is published and may be read
     auto ready_wait = [&](int c) -> bool {
@@ -953,18 +980,6 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         const int n = htid + kHelpers * i;
         if (n < NV16) pre[i] = rec[n < NSH16 ? n : n + uoff16];
       }
-      if (kExt && lay.og) {
-        const TIn* ogc = reinterpret_cast<const TIn*>(lay.og) + (((size_t)b * T_len + c * kC) * H + h) * DV +
-                         (size_t)vb * (DV / CL::NS);
-#pragma unroll
-        for (int i = 0; i < OGN; ++i) {
-          const int n = htid + kHelpers * i, r = n / OGV, pc = n % OGV;
-          if (n < kC * OGV)
-            preg[i] = c * kC + r < T_len ? *reinterpret_cast<const raw16*>(ogc + (size_t)r * H * DV +
-                                                                           pc * (16 / sizeof(TIn)))
-                                         : raw16{0.f, 0.f, 0.f, 0.f};
-        }
-      }
     };
     auto stage = [&](int c) {
       char* buf = buf_of(c);
@@ -972,13 +987,6 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       for (int i = 0; i < PPT; ++i) {
         const int n = htid + kHelpers * i;
         if (n < NV16) reinterpret_cast<raw16*>(buf)[n] = pre[i];
-      }
-      if (kExt && lay.og) {
-#pragma unroll
-        for (int i = 0; i < OGN; ++i) {
-          const int n = htid + kHelpers * i;
-          if (n < kC * OGV) reinterpret_cast<raw16*>(buf + CL::OG_OFF)[n] = preg[i];
-        }
       }
       // every load of chunk c has returned its data before its slot is
       // handed back (after the next X)
@@ -1009,17 +1017,40 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     return;
   }
 
-  f32x4 S[NCT][NJ];
+  // S from h0 (one wave-uniform branch around unconditional loads), used
+  // before the loop, so that no wait inside the loop is tied to its loads
+  f32x4 S[NCT];
   const size_t sbase = bh * DK * DV;
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+  for (int ct = 0; ct < NCT; ++ct) S[ct] = zero4();
+  if (h0) {
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[ct][jj][i] = h0 ? h0[sbase + (size_t)(16 * ct + g4 + i) * DV + 16 * (jt0 + jj) + l16] : 0.f;
+      for (int i = 0; i < 4; ++i) S[ct][i] = h0[sbase + (size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16];
+  }
+  float m0 = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) m0 = fmaxf(m0, absmax4(S[ct]));
+  m0 = wave_max_dpp(m0);
+
+  // O of chunk c, as 16-byte non-temporal vectors (written once, not re-read)
+  auto store_out = [&](int c, const f32x4 (&Ov)[4]) {
+    const int t0 = c * kC;
+    float* orow = o + (((size_t)b * T_len + t0 + l16) * H + h) * DV + 16 * jt0 + g4;
+    const size_t ors = (size_t)16 * H * DV;   // 16 rows
+    const bool full = t0 + kC <= T_len;       // uniform; only the last chunk is partial
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      if (full || t0 + 16 * rt + l16 < T_len) __builtin_nontemporal_store(Ov[rt], reinterpret_cast<f32x4*>(orow + rt * ors));
+  };
 
   const bool mixed = P::kMixed;
+  // sigma = 2^sig_e: the owner holds Sh = sigma S.  Sigma is chosen at every
+  // chunk from the state alone (its maximum moved into [2^12, 2^13)), so a
+  // run split into several calls at chunk boundaries does the same
+  // arithmetic as one call.
+  int sig_e = 0;
   for (int c = 0; c < nchunks; ++c) {
     __syncthreads();   // X_c
     if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
@@ -1031,171 +1062,152 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     const float* sDec = reinterpret_cast<const float*>(buf + R::DEC_OFF_BYTES);
     const float uinv = *reinterpret_cast<const float*>(buf + R::UINV_OFF_BYTES);
     const Op* sU = reinterpret_cast<const Op*>(buf + CL::SH);   // local column tiles, 4 jl + st
+    const int t0 = c * kC;
+    // output gate values of this owner's outputs, loaded early
+    f32x4 gz[4];
+    if (kExt && lay.og) {
+      const TIn* og = reinterpret_cast<const TIn*>(lay.og);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int row = t0 + 16 * rt + l16;
+        gz[rt] = row < T_len ? widen4(load4(og + (((size_t)b * T_len + row) * H + h) * DV + 16 * jt0 + g4)) : zero4();
+      }
+    }
 
-    // S as an operand, range-scaled by a power of two
-    float smax = 0.f;
+    // The products run in the sigma domain (bf16 mode): Sh = sigma S and
+    // Uh = sigma U are fp16 operands as they are (fp16 has the same
+    // relative precision at every normal magnitude; sigma keeps the
+    // largest values in range), and the record holds -W, so the MFMAs
+    // accumulating onto sigma Ut give Uh directly.
+    if (mixed) {
+      const int k = domain_rescale_exp(m0, sig_e);
+      if (k != 0) {
+        const float f = ldexpf(1.f, k);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct) S[ct] = S[ct] * f;
+        sig_e += k;
+      }
+    }
+    const float sig = ldexpf(1.f, sig_e), isig = ldexpf(1.f, -sig_e);
+    V4<Op> Sb[NCT];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) smax = fmaxf(smax, absmax4(S[ct][jj]));
-    float ss = 1.f, iss = 1.f;
-    if (mixed) fp16_range_scale2(wave_max_dpp(smax), ss, iss);
-    V4<Op> Sb[NCT][NJ];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) Sb[ct][jj] = narrow4<Op>(S[ct][jj] * ss);
-
-    // U = Ut - W S and the Qbar S part of O, row block by row block: the two
-    // products need only S, so their LDS reads and MFMAs interleave (each
-    // block's operands are read before its products, one LDS latency per
-    // block).  O^T = S^T Qbar^T + U^T (scale M)^T: lane l holds row
-    // 16rt + l%16, columns 16jt + 4(l/16) .. +3.
-    f32x4 U[4][NJ], accQ[4][NJ];
-    float umax = 0.f;
+    for (int ct = 0; ct < NCT; ++ct) Sb[ct] = narrow4<Op>(S[ct]);
+    // Uh = sigma Ut - W Sh and the Qbar Sh part of O, row block by row
+    // block (both need only Sh); O^T = Sh^T Qbar^T + Uh^T (scale M)^T:
+    // lane l holds row 16rt + l%16, columns 16jt + 4(l/16) .. +3.
+    const float cu = sig * uinv;
+    f32x4 Uh[4], accO[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      f32x4 Pv[NJ];
+      Uh[st] = widen4(load4(sU + tile_elem(jl0 * 4 + st, lane))) * cu;
+      accO[st] = zero4();
+    }
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        Pv[jj] = zero4();
-        accQ[st][jj] = zero4();
-      }
+    for (int st = 0; st < 4; ++st) {
       Slab<Op> Wa[DK / 32], Qa[DK / 32];
 #pragma unroll
       for (int sl = 0; sl < DK / 32; ++sl) {
-        Wa[sl] = slab_of<Op>(load4(sW + tile_cr(2 * sl, st) * 256 + 4 * lane),
-                             load4(sW + tile_cr(2 * sl + 1, st) * 256 + 4 * lane));
-        Qa[sl] = slab_of<Op>(load4(sQ + tile_cr(2 * sl, st) * 256 + 4 * lane),
-                             load4(sQ + tile_cr(2 * sl + 1, st) * 256 + 4 * lane));
+        Wa[sl] = load_slab8<Op>(sW + tile_elem(tile_cr(2 * sl, st), lane));
+        Qa[sl] = load_slab8<Op>(sQ + tile_elem(tile_cr(2 * sl, st), lane));
       }
 #pragma unroll
       for (int sl = 0; sl < DK / 32; ++sl) {
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const Slab<Op> sb = slab_of<Op>(Sb[2 * sl][jj], Sb[2 * sl + 1][jj]);
-          Pv[jj] = mma(Wa[sl], sb, Pv[jj]);
-          accQ[st][jj] = mma(sb, Qa[sl], accQ[st][jj]);
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        U[st][jj] = widen4(load4(sU + ((jl0 + jj) * 4 + st) * 256 + 4 * lane)) * uinv - Pv[jj] * iss;
-        umax = fmaxf(umax, absmax4(U[st][jj]));
+        const Slab<Op> sb = slab_of<Op>(Sb[2 * sl], Sb[2 * sl + 1]);
+        Uh[st] = mma(Wa[sl], sb, Uh[st]);
+        accO[st] = mma(sb, Qa[sl], accO[st]);
       }
     }
-    float us = 1.f, ius = 1.f;
-    if (mixed) fp16_range_scale2(wave_max_dpp(umax), us, ius);
-    V4<Op> Ub[4][NJ];
+    // Uh must fit fp16.  It does unless U is more than 8x larger than S
+    // (or the input holds inf/NaN): then Uh is scaled into range by a power
+    // of two r (wave-uniform branch).
+    float umax = 0.f;
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int st = 0; st < 4; ++st) umax = fmaxf(umax, absmax4(Uh[st]));
+    int re = 0;
+    if (mixed) {
+      umax = wave_max_dpp(umax);
+      if (!(umax <= kFp16Safe)) re = fp16_domain_exp(umax);
+    }
+    const float r = ldexpf(1.f, re), ir = ldexpf(1.f, -re);
+    // Sh <- e^{Gamma_C} Sh + Khat^T Uh: MFMAs accumulating onto the decayed
+    // state; and the (scale M) Uh part of O onto the Qbar Sh part.  With
+    // Uh scaled by r, both are unscaled in fp32 afterwards.
+    f32x4 accS[NCT];
+    auto u_products = [&](auto kScaled) {
+      constexpr bool scl = decltype(kScaled)::value;
+      V4<Op> Ub[4];
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) Ub[st][jj] = narrow4<Op>(U[st][jj] * us);
-
-    // S <- e^{Gamma_C} S + Khat^T U, ahead of the output: only S feeds the
-    // next chunk, so its products overlap the output work below
+      for (int st = 0; st < 4; ++st) Ub[st] = narrow4<Op>(scl ? Uh[st] * r : Uh[st]);
 #pragma unroll
-    for (int cp = 0; cp < NCT; cp += 2) {   // two column tiles of S per LDS batch
-      Slab<Op> Ka[2][2];
+      for (int ct = 0; ct < NCT; ++ct) {
+        const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
+        accS[ct] = scl ? S[ct] * d * r : S[ct] * d;
+      }
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+      for (int cp = 0; cp < NCT; cp += 2) {   // two column tiles of S per LDS batch
+        Slab<Op> Ka[2][2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) Ka[cc][sl] = load_slab8<Op>(sK + tile_elem(tile_k<NCT>(2 * sl, cp + cc), lane));
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl)
+            accS[cp + cc] = mma(Ka[cc][sl], slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), accS[cp + cc]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int nms = rt < 2 ? 1 : 2;   // slabs of M's row block rt that are not all zero
+        f32x4 am = scl ? zero4() : accO[rt];
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl)
-          Ka[cc][sl] = slab_of<Op>(load4(sK + tile_k<NCT>(2 * sl, cp + cc) * 256 + 4 * lane),
-                                   load4(sK + tile_k<NCT>(2 * sl + 1, cp + cc) * 256 + 4 * lane));
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ct = cp + cc;
-        const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
-        f32x4 acc[NJ];
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) acc[jj] = zero4();
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-#pragma unroll
-          for (int jj = 0; jj < NJ; ++jj) acc[jj] = mma(Ka[cc][sl], slab_of<Op>(Ub[2 * sl][jj], Ub[2 * sl + 1][jj]), acc[jj]);
-        }
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) S[ct][jj] = S[ct][jj] * d + acc[jj] * ius;
+          if (sl < nms)
+            am = mma(slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), load_slab8<Op>(sM + tile_elem(tile_cr(2 * sl, rt), lane)),
+                     am);
+        accO[rt] = scl ? accO[rt] + am * ir : am;
       }
-    }
-    // O = Qbar S + (scale M) U, stored as 16-byte non-temporal vectors
-    // (written once, not re-read)
-    const int t0 = c * kC;
-    const bool full = t0 + kC <= T_len;   // uniform; only the last chunk is partial
-    float* orow = o + (((size_t)b * T_len + t0 + l16) * H + h) * DV + 16 * jt0 + g4;
-    const size_t ors = (size_t)16 * H * DV;   // 16 rows
-    f32x4 Ov[4][NJ];
+      if (scl) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 accM[NJ];
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) accM[jj] = zero4();
-      Slab<Op> Ma[2];
-      const int nms = rt < 2 ? 1 : 2;   // slabs of M's row block rt that are not all zero
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
-        if (sl < nms)
-          Ma[sl] = slab_of<Op>(load4(sM + tile_cr(2 * sl, rt) * 256 + 4 * lane),
-                               load4(sM + tile_cr(2 * sl + 1, rt) * 256 + 4 * lane));
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        if (sl < nms) {
-#pragma unroll
-          for (int jj = 0; jj < NJ; ++jj)
-            accM[jj] = mma(slab_of<Op>(Ub[2 * sl][jj], Ub[2 * sl + 1][jj]), Ma[sl], accM[jj]);
-        }
+        for (int ct = 0; ct < NCT; ++ct) accS[ct] = accS[ct] * ir;
       }
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) Ov[rt][jj] = accQ[rt][jj] * iss + accM[jj] * ius;
-    }
-    if (kExt && lay.og) {   // output gate: o <- Sigmoid(og) o, og staged with the record
-      const TIn* sOg = reinterpret_cast<const TIn*>(buf + CL::OG_OFF);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const f32x4 gz = widen4(load4(sOg + (16 * rt + l16) * (DV / CL::NS) + 16 * (jl0 + jj) + g4));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Ov[rt][jj][i] *= sigmoid_fast(gz[i]);
-        }
-    }
-    if (full) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
-          __builtin_nontemporal_store(Ov[rt][jj], reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj));
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
-          if (t0 + 16 * rt + l16 < T_len)
-            __builtin_nontemporal_store(Ov[rt][jj], reinterpret_cast<f32x4*>(orow + rt * ors + 16 * jj));
-    }
+    };
+    if (__builtin_amdgcn_readfirstlane(re)) u_products(std::true_type{});
+    else u_products(std::false_type{});
 
+    float smax = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      S[ct] = accS[ct];
+      smax = fmaxf(smax, absmax4(S[ct]));
+    }
+    m0 = mixed ? wave_max_dpp(smax) : 0.f;   // the next chunk's sigma comes from it
+    f32x4 Ov[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) Ov[rt] = accO[rt] * isig;
+    if (kExt && lay.og) {   // output gate: o <- Sigmoid(og) o
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ov[rt][i] *= sigmoid_fast(gz[rt][i]);
+    }
+    store_out(c, Ov);
     if (kExt && snap.p && snap.every > 0 && (c + 1) % snap.every == 0 && (c + 1) * kC < T_len) {
       float* sp = snap.p + ((size_t)((c + 1) / snap.every - 1) * snap.nbh + bh) * DK * DV;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sp[(size_t)(16 * ct + g4 + i) * DV + 16 * (jt0 + jj) + l16] = S[ct][jj][i];
+        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
     }
     if (NBUF == 1) __syncthreads();   // Y_c
   }
 
   if (ht) {
+    const float isig = ldexpf(1.f, -sig_e);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ht[sbase + (size_t)(16 * ct + g4 + i) * DV + 16 * (jt0 + jj) + l16] = S[ct][jj][i];
+      for (int i = 0; i < 4; ++i) ht[sbase + (size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
   }
 }
 
@@ -1209,8 +1221,8 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
   __shared__ __align__(16) char smem[CL::BYTES];
   const int bh = blockIdx.x / CL::NS, vb = blockIdx.x % CL::NS;
   consume_chain<TIn, DK, DV, false, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
-                                    Ring{nullptr, nullptr, nullptr, nullptr, 1}, vb, h0, ht, o, bh / H, bh % H,
-                                    T_len, H, nchunks, snap);
+                                           Ring{nullptr, nullptr, nullptr, nullptr, 1}, vb, h0, ht, o, bh / H,
+                                           bh % H, T_len, H, nchunks, snap);
 }
 
 // ---------------------------------------------------------------------------
@@ -1273,8 +1285,8 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   if (li < nloc * NS) {   // consumer vb of head jh
     const int jh = xcd + 8 * (li / NS), vb = li % NS, bh = head0 + jh;
     consume_chain<TIn, DK, DV, true, kExt>(smem, ring + (size_t)jh * R * Rc::BYTES,
-                                     Ring{ready + jh * R, done + jh * NS + vb, err, cxcc + jh * NS + vb, R}, vb, h0,
-                                     ht, o, bh / H, bh % H, T_len, H, nchunks, snap, lay);
+                                           Ring{ready + jh * R, done + jh * NS + vb, err, cxcc + jh * NS + vb, R}, vb,
+                                           h0, ht, o, bh / H, bh % H, T_len, H, nchunks, snap, lay);
     return;
   }
 
