@@ -20,7 +20,7 @@ OUT = PKG / "libkda.so"
 BUILD = PKG / "_build"
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["kda_api.cpp", "kda_decay.hip", "kda_chunk.hip", "kda_decode.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_decay.hip", "kda_chunk.hip", "kda_decode.hip", "kda_bwd.hip", "kda_noalloc.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -137,6 +137,10 @@ int check_fwd(const void* q, const void* k, const void* v, const void* g, const 
   return KDA_OK;
 }
 
+// The scratch of the allocation-free prefill stands in for the workspace
+// in the shared checks (never dereferenced on the host).
+const void* const kNoAllocWs = reinterpret_cast<const void*>(static_cast<uintptr_t>(256));
+
 }  // namespace
 
 namespace {
@@ -162,6 +166,26 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g, 
                     int H, int dk, int dv, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_fused_impl(q, k, v, g, gcum, beta, scale, h0, ht, o, dtype, B, T, H, dk, dv, chunk, workspace,
                         workspace_bytes, 0, stream);
+}
+
+int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const void* g, const float* gcum,
+                            const void* beta, float scale, const float* h0, float* ht, float* o, int dtype, int B,
+                            int T, int H, int dk, int dv, int chunk, void* stream) {
+  const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, kNoAllocWs, 3);
+  if (st != KDA_OK) return st;
+  // the scratch holds at least one head's ring for every supported size
+  // (more heads run as further launches); checked for completeness
+  if (kda_fwd_workspace_bytes(1, 1, 1, dk, dv, chunk, dtype) > kda::kNoAllocScratchBytes) return KDA_ERR_WORKSPACE;
+  const int rs = check_range(dtype, g, gcum, 1, B, T, H, dk, stream);
+  if (rs != KDA_OK) return rs;
+  void* scr = nullptr;
+  hipError_t e = kda::noalloc_scratch(&scr);
+  if (e == hipSuccess) e = kda::launch_clear_status(scr, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess)
+    e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T, H, dk, dv, scr,
+                              kda::kNoAllocScratchBytes, 0, nullptr, 0, nullptr, nullptr, 0,
+                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_fwd_chunked_unbounded(const void* q, const void* k, const void* v, const void* g, const float* gcum,
@@ -214,7 +238,11 @@ const int* kda_fwd_status_word(const void* workspace) {
 }
 
 int kda_fwd_status(const void* workspace, void* stream) {
-  if (!workspace) return KDA_ERR_NULL;
+  if (!workspace) {   // the allocation-free prefill's scratch on the current device
+    void* scr = nullptr;
+    if (kda::noalloc_scratch(&scr) != hipSuccess) return KDA_ERR_HIP;
+    workspace = scr;
+  }
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KDA_ERR_ALIGN;
   int word = 0;
   const hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -52,6 +52,15 @@ hipError_t launch_zero_words(void* p, size_t nwords, hipStream_t stream);
 // prefill workspace; called once per API call, before its launches.
 hipError_t launch_clear_status(void* ws, hipStream_t stream);
 
+// Library-owned scratch of the allocation-free prefill (a file-scope device
+// array, one per GPU): its device address on the current device, fetched
+// with hipGetSymbolAddress on the first call there.  40 MiB hold the ring of
+// 34 heads with fp32 inputs at dk = dv = 128 (the largest record, 1.16 MB per
+// head) and 70 heads with bf16 inputs; larger batches of heads run as
+// further launches of the same kernel.
+constexpr size_t kNoAllocScratchBytes = (size_t)40 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 
 // One decode token per (b, h), state updated in place.
 hipError_t launch_decode_step(int is_bf16, const void* q, const void* k, const void* v,

@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked_varlen.argtypes = [P, P, P, P, P, P, F, P, I, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
         L.kda_fwd_varlen_snapshots.restype = ctypes.c_longlong
         L.kda_fwd_varlen_snapshots.argtypes = [P, I, I, I]
+        L.kda_fwd_chunked_noalloc.restype = I
+        L.kda_fwd_chunked_noalloc.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P]
         L.kda_fwd_chunked_unbounded.restype = I
         L.kda_fwd_chunked_unbounded.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, P]
         L.kda_fwd_chunked_stages.restype = I

@@ -24,8 +24,9 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller,
  *     contiguous row-major, 16-byte aligned.  Nothing is retained after the
  *     call returns.  The library never allocates device memory; its only
- *     device state is a word per GPU used by the opt-in range check (in the
- *     code object, loaded with the library).  Calls are re-entrant.
+ *     device state is in its code object (one copy per GPU): a word used by
+ *     the opt-in range check and the scratch of kda_fwd_chunked_noalloc.
+ *     Calls are re-entrant.
  *   - Layouts: q, k, g, z : [B, T, H, dk];  v, o : [B, T, H, dv];
  *     beta : [B, T, H];  A : [H] (fp32);  states h0 / ht / state :
  *     [B, H, dk, dv] fp32 (key channel = row, value channel = column).
@@ -164,6 +165,28 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g,
                     int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_fwd_chunked without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same computation, kernels and results
+ * as kda_fwd_chunked (bit for bit); the ring buffers and control words live
+ * in a library-owned device array of 40 MiB per GPU (a file-scope array in
+ * the code object, held until the process ends; no allocation by this call
+ * or by the library).  The array holds the rings of 34 heads (fp32 inputs,
+ * dk = dv = 128) to 70 heads (bf16 inputs): larger batches of heads run as
+ * further launches, so no supported size is refused for lack of scratch.
+ * Every call on one GPU uses that GPU's array: calls that overlap on one
+ * GPU (unordered streams) race and must not be issued.  Status:
+ * kda_fwd_status(NULL, stream) reads this array's status word (current
+ * device).
+ * Errors: as kda_fwd_chunked without KDA_ERR_WORKSPACE for a missing
+ * workspace.
+ */
+int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const void* g,
+                            const float* gcum, const void* beta, float scale, const float* h0,
+                            float* ht, float* o, int dtype, int B, int T, int H, int dk, int dv,
+                            int chunk, void* stream);
+
+/*
  * kda_fwd_chunked for a log-decay with no lower bound (g <= 0, e.g. from
  * kda_prepare_decay_softplus): the comparison point of "Key claims",
  * section 2.1.1 / Fig. 3, where an unbounded decay rules out the rescaled
@@ -260,7 +283,8 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
  * prefill calls: kda_fwd_chunked, _unbounded, _layer, _varlen, or of
  * kda_bwd_chunked, whose forward recompute it covers): synchronises
  * `stream`, then returns KDA_OK, or KDA_ERR_INCOMPLETE if a hand-off wait
- * of that call expired (its outputs are incomplete).  Errors: KDA_ERR_NULL,
+ * of that call expired (its outputs are incomplete).  workspace NULL: the
+ * scratch of kda_fwd_chunked_noalloc on the current device.  Errors:
  * KDA_ERR_ALIGN (workspace not 256-byte aligned), KDA_ERR_HIP.
  */
 int kda_fwd_status(const void* workspace, void* stream);

@@ -197,7 +197,6 @@ def test_status_codes_and_status_word():
     assert L.kda_fwd_status_word(FAKE) == FAKE + 32
     assert L.kda_fwd_status_word(None) is None
     # kda_fwd_status validates before it touches the device
-    assert L.kda_fwd_status(None, None) == 1
     assert L.kda_fwd_status(FAKE + 16, None) == 4
 
 
@@ -219,3 +218,21 @@ def test_varlen_rejects_packed_gcum():
     cu = (ctypes.c_int * 3)(0, 30, 100)
     assert L.kda_fwd_chunked_varlen(FAKE, FAKE, FAKE, None, FAKE, FAKE, 0.1, cu, 2, None, None, FAKE, None, 0, 1,
                                     100, 2, 128, 128, 64, FAKE, 1 << 40, None) == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_noalloc_entry_validates_like_kda_fwd_chunked():
+    L = kda.lib()
+    a = [FAKE, FAKE, FAKE, FAKE, None, FAKE, 0.1, None, None, FAKE, 1, 1, 64, 1, 128, 128, 64, None]
+    for i in (0, 5, 9):
+        bad = list(a); bad[i] = None
+        assert L.kda_fwd_chunked_noalloc(*bad) == 1
+    bad = list(a); bad[3] = None                     # neither g nor gcum
+    assert L.kda_fwd_chunked_noalloc(*bad) == 1
+    bad = list(a); bad[11] = 0
+    assert L.kda_fwd_chunked_noalloc(*bad) == 2
+    bad = list(a); bad[10] = 4
+    assert L.kda_fwd_chunked_noalloc(*bad) == 3
+    bad = list(a); bad[7] = FAKE + 8
+    assert L.kda_fwd_chunked_noalloc(*bad) == 4
+    bad = list(a); bad[15] = 96
+    assert L.kda_fwd_chunked_noalloc(*bad) == 5
