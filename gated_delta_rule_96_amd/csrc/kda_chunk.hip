@@ -224,7 +224,7 @@ struct InRegs {
   static constexpr int NV = kC * DV / VE / kThreads;
   static_assert(NK * kThreads * VE == kC * DK && NV * kThreads * VE == kC * DV, "shape");
   raw16 k[NK], q[NK], g[NK], v[NV];
-  float beta;
+  TIn beta;   // raw: converted when staged, so that no wait follows its load
 };
 
 // Parts of the inputs (bit mask of load_inputs): the next chunk's loads
@@ -266,7 +266,7 @@ __device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* 
       in.v[i] = r < Lrows ? __builtin_nontemporal_load(reinterpret_cast<const raw16*>(v + base_v + r * tokv + c)) : zero16;
   }
   if (kParts & kLoadBeta)
-    in.beta = (tid < kC && tid < Lrows) ? to_f32(beta[((size_t)b * T_len + t0 + tid) * H + h]) : 0.f;
+    in.beta = (tid < kC && tid < Lrows) ? beta[((size_t)b * T_len + t0 + tid) * H + h] : (TIn)0.f;
 }
 
 // 2^x for x given in fp64, rounded to fp32 with about one ulp of error
@@ -367,19 +367,22 @@ constexpr unsigned long long kWaveTile1 = 0xff87ffffull;
 
 // Builds the record of chunk `ch` of head (b, h) at `rec`.  Called by a
 // whole work-group of kThreads threads; `smem` holds IntraLds::BYTES.
-// `in` holds the chunk's inputs (load_inputs); right after they are staged
-// in LDS, `after_stage()` runs with every thread; if it returns false
-// nothing is written.  From then on `in` is free (v is read from it once
+// `in` holds the chunk's inputs (load_inputs).  `slot(step)` (step an
+// std::integral_constant) is called by every thread: kSlotPeek once the
+// inputs are staged, kSlotCheck before the barrier that ends phase 0 and
+// kSlotOk after it; if that returns false nothing is written.  From then on `in` is free (v is read from it once
 // more, before the last call): `prefetch(parts)` is called by every thread
 // at four points of the later phases, with kLoadK | kLoadBeta, kLoadQ,
 // kLoadG, kLoadV in turn (as std::integral_constant), e.g. to load the next
 // chunk's inputs into `in` in portions while this one is computed.
 // kExt: the layer steps (Layer) may be requested; without it their code is
 // compiled out of the plain kernels.
-template <typename TIn, int DK, int DV, bool kUnb, bool kExt, typename AfterStage, typename Prefetch>
+constexpr int kSlotPeek = 0, kSlotCheck = 1, kSlotOk = 2;
+
+template <typename TIn, int DK, int DV, bool kUnb, bool kExt, typename Slot, typename Prefetch>
 __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& in, const float* __restrict__ gcum,
                                               float scale, int b, int h, int T_len, int H, int ch,
-                                              char* __restrict__ rec, AfterStage after_stage, Prefetch prefetch,
+                                              char* __restrict__ rec, Slot slot, Prefetch prefetch,
                                               Layer lay = Layer{nullptr, nullptr, 0}) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
@@ -445,8 +448,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
         *reinterpret_cast<f32x4*>(sG + r * L::LG + c + x) = f32x4{gv[x], gv[x + 1], gv[x + 2], gv[x + 3]};
     }
   }
-  if (tid < kC) sBeta[tid] = in.beta;
+  if (tid < kC) sBeta[tid] = to_f32(in.beta);
   __syncthreads();
+  slot(std::integral_constant<int, kSlotPeek>{});
 
   // Block scans: thread (block a, channel c) forms G for its 16 rows (local
   // sums in row order, or differences of the given cumulative sums), the two
@@ -552,8 +556,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       for (int j = 0; j < 4; ++j) sBlk[(kBlkM + j) * DK + c] = exp2_split(-(double)sTot[j * DK + c] * l2e);
     }
   }
+  slot(std::integral_constant<int, kSlotCheck>{});
   __syncthreads();
-  if (!after_stage()) return false;
+  if (!slot(std::integral_constant<int, kSlotOk>{})) return false;
   prefetch(std::integral_constant<int, kLoadK | kLoadBeta>{});
 
   // ---- phase 1: Gram tiles (A -> LDS, scale M -> record)
@@ -778,7 +783,7 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __rest
   InRegs<TIn, DK, DV> in;
   load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, ch);
   produce_chunk<TIn, DK, DV, kUnb, false>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, ch,
-                                   ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [] { return true; },
+                                   ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [](auto) { return true; },
                                    [](auto) {});
 }
 
@@ -849,6 +854,11 @@ __device__ __forceinline__ int spin_until_geq(const int* p, int target, int* err
 // Waits until every vector memory access this wave issued has completed
 // (stores acknowledged by the L2, loads returned); also a compiler barrier.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Buffer resource word 3 for raw dword access on gfx950, and the cache
+// policy bit sc0 of a buffer load (served by this XCD's L2, not the CU's L1).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kCachePolicySc0 = 1;
 
 constexpr size_t kLdsMax = 160 * 1024;
 constexpr int kOwners = 4;   // waves that own value columns, 16 each
@@ -1129,15 +1139,17 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       if (!(umax <= kFp16Safe)) re = fp16_domain_exp(umax);
     }
     const float r = ldexpf(1.f, re), ir = ldexpf(1.f, -re);
-    // Sh <- e^{Gamma_C} Sh + Khat^T Uh: MFMAs accumulating onto the decayed
-    // state; and the (scale M) Uh part of O onto the Qbar Sh part.  With
-    // Uh scaled by r, both are unscaled in fp32 afterwards.
-    f32x4 accS[NCT];
-    auto u_products = [&](auto kScaled) {
+    // The rest of the chunk, one straight-line block per case (so that the
+    // output work and stores can be scheduled into the gaps of the state
+    // update's products).  Sh <- e^{Gamma_C} Sh + Khat^T Uh: MFMAs
+    // accumulating onto the decayed state; the (scale M) Uh part of O onto
+    // the Qbar Sh part.  With Uh scaled by r, both are unscaled in fp32.
+    auto tail = [&](auto kScaled) {
       constexpr bool scl = decltype(kScaled)::value;
       V4<Op> Ub[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) Ub[st] = narrow4<Op>(scl ? Uh[st] * r : Uh[st]);
+      f32x4 accS[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
@@ -1156,6 +1168,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
           for (int sl = 0; sl < 2; ++sl)
             accS[cp + cc] = mma(Ka[cc][sl], slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), accS[cp + cc]);
       }
+      f32x4 Ov[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int nms = rt < 2 ? 1 : 2;   // slabs of M's row block rt that are not all zero
@@ -1165,33 +1178,25 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
           if (sl < nms)
             am = mma(slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), load_slab8<Op>(sM + tile_elem(tile_cr(2 * sl, rt), lane)),
                      am);
-        accO[rt] = scl ? accO[rt] + am * ir : am;
+        Ov[rt] = (scl ? accO[rt] + am * ir : am) * isig;
       }
-      if (scl) {
+      if (kExt && lay.og) {   // output gate: o <- Sigmoid(og) o
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) accS[ct] = accS[ct] * ir;
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Ov[rt][i] *= sigmoid_fast(gz[rt][i]);
       }
+      store_out(c, Ov);
+      float smax = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        S[ct] = scl ? accS[ct] * ir : accS[ct];
+        smax = fmaxf(smax, absmax4(S[ct]));
+      }
+      m0 = mixed ? wave_max_dpp(smax) : 0.f;   // the next chunk's sigma comes from it
     };
-    if (__builtin_amdgcn_readfirstlane(re)) u_products(std::true_type{});
-    else u_products(std::false_type{});
-
-    float smax = 0.f;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      S[ct] = accS[ct];
-      smax = fmaxf(smax, absmax4(S[ct]));
-    }
-    m0 = mixed ? wave_max_dpp(smax) : 0.f;   // the next chunk's sigma comes from it
-    f32x4 Ov[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) Ov[rt] = accO[rt] * isig;
-    if (kExt && lay.og) {   // output gate: o <- Sigmoid(og) o
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Ov[rt][i] *= sigmoid_fast(gz[rt][i]);
-    }
-    store_out(c, Ov);
+    if (__builtin_amdgcn_readfirstlane(re)) tail(std::true_type{});
+    else tail(std::false_type{});
     if (kExt && snap.p && snap.every > 0 && (c + 1) % snap.every == 0 && (c + 1) * kC < T_len) {
       float* sp = snap.p + ((size_t)((c + 1) / snap.every - 1) * snap.nbh + bh) * DK * DV;
 #pragma unroll
@@ -1333,20 +1338,32 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   for (;;) {
     const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
     const int nxt = it + P;
-    // Runs once this chunk's inputs are in LDS: wait until the ring slot of
-    // chunk c is free (it held chunk c - R, which the head's consumers must
-    // have read).
-    auto after_stage = [&]() -> bool {
+    // The ring slot of chunk c is free once the head's consumers have read
+    // chunk c - R.  Wave 0 reads their progress words from this XCD's L2
+    // once the inputs are staged (after the input registers are consumed:
+    // vector loads complete in order), checks them at the end of the block
+    // scans, polling only if the slot is still taken, and leaves its verdict
+    // in LDS for the other waves to read after the next barrier.
+    int seen[NS] = {};
+    auto slot = [&](auto step) -> bool {
+      constexpr int s = decltype(step)::value;
       if (c < R) return true;
-      if (w == 0) {
+      if (s == kSlotPeek && w == 0) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(done + jh * NS, (short)0, NS * 4, kBufferRsrcWord3);
+#pragma unroll
+        for (int vb = 0; vb < NS; ++vb) seen[vb] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * vb, 0, kCachePolicySc0);
+      } else if (s == kSlotCheck && w == 0) {
         bool ok = true;
-        for (int vb = 0; vb < NS && ok; ++vb) ok = spin_until_geq(done + jh * NS + vb, c - R + 1, err) >= 0;
+#pragma unroll
+        for (int vb = 0; vb < NS; ++vb)
+          if (ok && __builtin_amdgcn_readfirstlane(seen[vb]) < c - R + 1)
+            ok = spin_until_geq(done + jh * NS + vb, c - R + 1, err) >= 0;
         if (lane == 0) *sWord = ok ? 1 : 0;
+      } else if (s == kSlotOk) {
+        return __builtin_amdgcn_readfirstlane(*sWord) != 0;
       }
-      __syncthreads();
-      const int ok = __builtin_amdgcn_readfirstlane(*sWord);
-      __syncthreads();
-      return ok != 0;
+      return true;
     };
     // the next item's inputs, loaded in portions during this item's phases
     auto prefetch = [&](auto parts) {
@@ -1357,7 +1374,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
       }
     };
     if (!produce_chunk<TIn, DK, DV, kUnb, kExt>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
-                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, after_stage, prefetch, lay))
+                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, slot, prefetch, lay))
       return;
     // Published as soon as its stores are in the L2.  (Deferring this until
     // the next item's inputs were staged let the stores drain in the
