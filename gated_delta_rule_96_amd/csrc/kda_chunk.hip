@@ -283,7 +283,7 @@ __device__ __forceinline__ float exp2_split(double x) {
 // [kNBlk][DK]; Gamma_p(a) = Gamma at row 16a - 1 (0 for a = 0; Gamma_p(4) =
 // Gamma_C at the chunk's last row), T_a = Gamma_p(a+1) - Gamma_p(a):
 constexpr int kBlkF = 0;     // rows 0-3   e^{Gamma_p(a)}
-constexpr int kBlkE = 4;     // rows 4-7   e^{Gamma_C - Gamma_p(a+1)}
+constexpr int kBlkE = 4;     // rows 4-7   (unused: Khat is formed from the scan registers)
 constexpr int kBlkD = 8;     // rows 8-13  e^{Gamma_p(a) - Gamma_p(b+1)}, off-diagonal
                              //            tiles (a, b) in kTileA/kTileB order 4..9
 constexpr int kBlkDec = 14;  // row 14     e^{Gamma_C}
@@ -317,11 +317,12 @@ constexpr int kNBlk = 19;
 //        -> Tm (Op [C][LB]) where A was                     [2b - 3]
 //   BLK: fp32 [kNBlk][DK] per-channel factors                [0 - 2b]
 // Phases: 0 stage inputs, block scans, exponentials, factors (kUnb: and the
-// diagonal tiles by position pairs); 1 Gram tiles (A -> LDS, scale M ->
-// record); 2a wave 0 inverts the diagonal blocks of I + A while waves 1-7
-// write Qbar, Khat, e^{Gamma_C} to the record; 2b Kbar^T and V^T staged,
-// off-diagonal blocks of the inverse, Tm; 3 W = Tm Kbar, Ut = Tm V to the
-// record.
+// diagonal tiles by position pairs); Khat goes to the record straight from
+// the scan registers (a thread holds 16 rows of one channel, four rows per
+// record lane); 1 Gram tiles (A -> LDS, scale M -> record); 2a wave 0
+// inverts the diagonal blocks of I + A while waves 1-7 write Qbar and
+// e^{Gamma_C} to the record; 2b Kbar^T and V^T staged, off-diagonal blocks
+// of the inverse, Tm; 3 W = Tm Kbar, Ut = Tm V to the record.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct IntraLds {
@@ -482,7 +483,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       ke[i] = kv * ee;
     }
   }
+  slot(std::integral_constant<int, kSlotCheck>{});
   __syncthreads();   // staged g read (kUnb: G written); block totals written
+  if (!slot(std::integral_constant<int, kSlotOk>{})) return false;
   if (kUnb) {
     // Diagonal tiles by position pairs, fp32: entry (i, j), j <= i, of tile
     // a is sum_c y_rc k_sc e^{G_rc - G_sc} (r = 16a + i, s = 16a + j, y = k
@@ -539,12 +542,18 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       for (int j = 0; j < 4; ++j) bs[j + 1] = bs[j] + (double)sTot[j * DK + c];
     }
     constexpr double l2e = 1.4426950408889634;
+    {   // Khat rows of this thread's block and channel, straight to the record:
+        // lane group g of tile (a, c / 16) holds rows 16a + 4g .. + 3
+      const double bn = a == 0 ? bs[1] : (a == 1 ? bs[2] : (a == 2 ? bs[3] : bs[4]));   // Gamma_p(a + 1)
+      const float e = exp2_split((bs[4] - bn) * l2e);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4<Op>(rK + tile_elem(tile_k<DK / 16>(a, c / 16), (c % 16) + 16 * g),
+                   narrow4<Op>(f32x4{ke[4 * g] * e, ke[4 * g + 1] * e, ke[4 * g + 2] * e, ke[4 * g + 3] * e}));
+    }
     if (a == 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sBlk[(kBlkF + j) * DK + c] = exp2_split(bs[j] * l2e);
-    } else if (a == 1) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sBlk[(kBlkE + j) * DK + c] = exp2_split((bs[4] - bs[j + 1]) * l2e);
     } else if (a == 2) {
       const int ta[6] = {1, 2, 3, 2, 3, 3}, tb[6] = {0, 0, 0, 1, 1, 2};
 #pragma unroll
@@ -556,9 +565,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       for (int j = 0; j < 4; ++j) sBlk[(kBlkM + j) * DK + c] = exp2_split(-(double)sTot[j * DK + c] * l2e);
     }
   }
-  slot(std::integral_constant<int, kSlotCheck>{});
   __syncthreads();
-  if (!slot(std::integral_constant<int, kSlotOk>{})) return false;
   prefetch(std::integral_constant<int, kLoadK | kLoadBeta>{});
 
   // ---- phase 1: Gram tiles (A -> LDS, scale M -> record)
@@ -642,7 +649,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   __syncthreads();   // A complete
 
   // ---- phase 2a: diagonal blocks of X = (I + A)^-1 (wave 0) while waves
-  // 1-7 write Qbar, Khat and e^{Gamma_C} to the record
+  // 1-7 write Qbar and e^{Gamma_C} to the record
   if (w == 0) {
     // forward substitution, right-looking: lane = (block a, column j); once
     // x_m is final it is eliminated from every later row at once
@@ -660,24 +667,13 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     for (int i = 0; i < 16; ++i) Xb[i * L::LA + j] = x[i];
   } else {
     if (tid >= 64 && tid < 64 + DK) rDec[tid - 64] = sBlk[kBlkDec * DK + tid - 64];
-    for (int t = w - 1; t < 2 * NQT; t += kNW - 1) {
-      if (t < NQT) {
-        // Qbar tile (ct, rt): lane holds row 16rt + l16, columns 16ct + g4 .. +3
-        const int ct = t >> 2, rt = t & 3;
-        const int row = 16 * rt + l16, col = 16 * ct + g4;
-        const f32x4 f = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + col);
-        store4<Op>(rQ + tile_elem(tile_cr(ct, rt), lane),
-                   narrow4<Op>(*reinterpret_cast<const f32x4*>(sQP + row * L::LG + col) * (f * scale)));
-      } else {
-        // Khat tile (st, ct): lane holds Khat[16st + g4 + i][16ct + l16]
-        const int tk = t - NQT, st = tk / (DK / 16), ct = tk % (DK / 16);
-        const int col = 16 * ct + l16, row0 = 16 * st + g4;
-        const float e = sBlk[(kBlkE + st) * DK + col];
-        f32x4 val;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) val[i] = sKE[(row0 + i) * L::LG + col] * e;
-        store4<Op>(rK + tile_elem(tile_k<DK / 16>(st, ct), lane), narrow4<Op>(val));
-      }
+    for (int t = w - 1; t < NQT; t += kNW - 1) {
+      // Qbar tile (ct, rt): lane holds row 16rt + l16, columns 16ct + g4 .. +3
+      const int ct = t >> 2, rt = t & 3;
+      const int row = 16 * rt + l16, col = 16 * ct + g4;
+      const f32x4 f = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + col);
+      store4<Op>(rQ + tile_elem(tile_cr(ct, rt), lane),
+                 narrow4<Op>(*reinterpret_cast<const f32x4*>(sQP + row * L::LG + col) * (f * scale)));
     }
   }
   prefetch(std::integral_constant<int, kLoadG>{});
@@ -731,9 +727,19 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     }
     __syncthreads();
   }
-  for (int n = tid; n < kC * kC; n += kThreads) {   // A is dead: Tm takes its place
-    const int r = n >> 6, s = n & 63;
-    sTm[r * L::LB + s] = from_f32<Op>(s <= r ? sX[r * L::LA + s] * sBeta[s] : 0.f);
+  static_assert(kC * kC == 8 * kThreads, "Tm: 8 entries per thread");
+  {   // A is dead: Tm takes its place (8 consecutive entries of a row per thread)
+    const int r = tid >> 3, s0 = (tid & 7) * 8;
+    f32x4 x[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(sX + r * L::LA + s0 + 4 * h2);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(sBeta + s0 + 4 * h2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[h2][i] = s0 + 4 * h2 + i <= r ? xv[i] * bv[i] : 0.f;
+    }
+    store4<Op>(sTm + r * L::LB + s0, narrow4<Op>(x[0]));
+    store4<Op>(sTm + r * L::LB + s0 + 4, narrow4<Op>(x[1]));
   }
   __syncthreads();   // Tm, Kbar^T, V^T complete
 
@@ -812,6 +818,8 @@ struct Ring {
 };
 
 constexpr int kSpinLimit = 1 << 20;   // about a second of polling before giving up
+constexpr int kFlagBase = 32;         // first flag word of the fused schedule's control block
+constexpr int kFlagLine = 32;         // ints per 128-byte cache line
 
 // The XCD (accelerator complex die, each with its own L2) this wave runs on.
 __device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xf; }
@@ -831,7 +839,7 @@ __device__ __forceinline__ int load_flag_l2(const int* p) {
 // condition goes through readfirstlane, so the loop is wave-uniform (no
 // lane-divergent loop inside code that also holds barriers).  Polls read
 // this XCD's L2; every 8th poll is a device-scope load (the writer may run
-// on another XCD), and checks the error word.  kSleep: pause between polls
+// on another XCD), and every 64th checks the error word.  kSleep: pause between polls
 // (units of 64 cycles).  Returns -1 after kSpinLimit polls, or as soon as
 // another work-group reported an error; sets *err on a timeout.
 template <int kSleep = 2>
@@ -841,7 +849,7 @@ __device__ __forceinline__ int spin_until_geq(const int* p, int target, int* err
     const int v = __builtin_amdgcn_readfirstlane(dev ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                                      : load_flag_l2(p));
     if (v >= target) return v;
-    if (dev) {
+    if ((it & 63) == 63) {
       const int e = __builtin_amdgcn_readfirstlane(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       if (e != 0) return -1;
     }
@@ -1127,6 +1135,20 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         accO[st] = mma(sb, Qa[sl], accO[st]);
       }
     }
+    // Khat, M and e^{Gamma_C} for the rest of the chunk, read while the
+    // products above run (the owner has the registers to spare)
+    Slab<Op> Ka[NCT][2], Ma[6];
+    f32x4 dv[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) Ka[ct][sl] = load_slab8<Op>(sK + tile_elem(tile_k<NCT>(2 * sl, ct), lane));
+      dv[ct] = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
+    }
+#pragma unroll
+    for (int rt = 0, m = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int sl = 0; sl < (rt < 2 ? 1 : 2); ++sl, ++m) Ma[m] = load_slab8<Op>(sM + tile_elem(tile_cr(2 * sl, rt), lane));
     // Uh must fit fp16.  It does unless U is more than 8x larger than S
     // (or the input holds inf/NaN): then Uh is scaled into range by a power
     // of two r (wave-uniform branch).
@@ -1151,33 +1173,20 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       for (int st = 0; st < 4; ++st) Ub[st] = narrow4<Op>(scl ? Uh[st] * r : Uh[st]);
       f32x4 accS[NCT];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const f32x4 d = *reinterpret_cast<const f32x4*>(sDec + 16 * ct + g4);
-        accS[ct] = scl ? S[ct] * d * r : S[ct] * d;
-      }
+      for (int ct = 0; ct < NCT; ++ct) accS[ct] = scl ? S[ct] * dv[ct] * r : S[ct] * dv[ct];
 #pragma unroll
-      for (int cp = 0; cp < NCT; cp += 2) {   // two column tiles of S per LDS batch
-        Slab<Op> Ka[2][2];
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int sl = 0; sl < 2; ++sl) Ka[cc][sl] = load_slab8<Op>(sK + tile_elem(tile_k<NCT>(2 * sl, cp + cc), lane));
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int sl = 0; sl < 2; ++sl)
-            accS[cp + cc] = mma(Ka[cc][sl], slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), accS[cp + cc]);
-      }
+        for (int sl = 0; sl < 2; ++sl) accS[ct] = mma(Ka[ct][sl], slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), accS[ct]);
       f32x4 Ov[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      for (int rt = 0, m = 0; rt < 4; ++rt) {
         const int nms = rt < 2 ? 1 : 2;   // slabs of M's row block rt that are not all zero
         f32x4 am = scl ? zero4() : accO[rt];
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl)
-          if (sl < nms)
-            am = mma(slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), load_slab8<Op>(sM + tile_elem(tile_cr(2 * sl, rt), lane)),
-                     am);
+          if (sl < nms) am = mma(slab_of<Op>(Ub[2 * sl], Ub[2 * sl + 1]), Ma[m + sl], am);
+        m += nms;
         Ov[rt] = (scl ? accO[rt] + am * ir : am) * isig;
       }
       if (kExt && lay.og) {   // output gate: o <- Sigmoid(og) o
@@ -1255,8 +1264,13 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
 //
 // ctrl layout (ints):
 //   [0..7]   unused                     [8] error word (status of the call)
-//   [16 ..)  ready[nheads][R], then done[nheads][NS], then cxcc[nheads][NS]
-// [16 ..) is zeroed before every launch; [0..16) once per API call
+//   [32 ..)  ready[nheads][kFlagLine] (a head's R <= kFlagLine slot words),
+//            then done[nheads * NS][kFlagLine] (one word used), then
+//            cxcc[nheads][NS]
+// Every head's ready words and every consumer's progress word have a cache
+// line of their own: waves that poll different words (and the error word)
+// then never queue behind each other on one line.
+// [32 ..) is zeroed before every launch; [0..16) once per API call
 // (launch_clear_status), so an error word set by any launch of a call (one
 // per batch of heads, or per sequence) stays set until the caller reads it,
 // and every later launch of the call gives up at its first wait.
@@ -1283,14 +1297,16 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   const int nloc = nheads > xcd ? (nheads - xcd + 7) / 8 : 0;   // heads j = xcd + 8m of this launch
   constexpr int NS = ConsumerLds<TIn, DK, DV>::NS;
   int* err = ctrl + 8;
-  int* ready = ctrl + 16;
-  int* done = ready + nheads * R;
-  int* cxcc = done + nheads * NS;
+  int* ready = ctrl + kFlagBase;
+  int* done = ready + nheads * kFlagLine;
+  int* cxcc = done + nheads * NS * kFlagLine;
 
   if (li < nloc * NS) {   // consumer vb of head jh
     const int jh = xcd + 8 * (li / NS), vb = li % NS, bh = head0 + jh;
     consume_chain<TIn, DK, DV, true, kExt>(smem, ring + (size_t)jh * R * Rc::BYTES,
-                                           Ring{ready + jh * R, done + jh * NS + vb, err, cxcc + jh * NS + vb, R}, vb,
+                                           Ring{ready + jh * kFlagLine, done + (jh * NS + vb) * kFlagLine, err,
+                                                cxcc + jh * NS + vb, R},
+                                           vb,
                                            h0, ht, o, bh / H, bh % H, T_len, H, nchunks, snap, lay);
     return;
   }
@@ -1332,7 +1348,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (w == 0 && lane == 0)
-      __hip_atomic_store(ready + pj * R + pc % R, ((pc + 1) << 4) | my_xcc, __ATOMIC_RELAXED,
+      __hip_atomic_store(ready + pj * kFlagLine + pc % R, ((pc + 1) << 4) | my_xcc, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   };
   for (;;) {
@@ -1350,15 +1366,16 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
       if (c < R) return true;
       if (s == kSlotPeek && w == 0) {
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc(done + jh * NS, (short)0, NS * 4, kBufferRsrcWord3);
+            __builtin_amdgcn_make_buffer_rsrc(done + jh * NS * kFlagLine, (short)0, NS * kFlagLine * 4, kBufferRsrcWord3);
 #pragma unroll
-        for (int vb = 0; vb < NS; ++vb) seen[vb] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * vb, 0, kCachePolicySc0);
+        for (int vb = 0; vb < NS; ++vb)
+          seen[vb] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * vb * kFlagLine, 0, kCachePolicySc0);
       } else if (s == kSlotCheck && w == 0) {
         bool ok = true;
 #pragma unroll
         for (int vb = 0; vb < NS; ++vb)
           if (ok && __builtin_amdgcn_readfirstlane(seen[vb]) < c - R + 1)
-            ok = spin_until_geq(done + jh * NS + vb, c - R + 1, err) >= 0;
+            ok = spin_until_geq(done + (jh * NS + vb) * kFlagLine, c - R + 1, err) >= 0;
         if (lane == 0) *sWord = ok ? 1 : 0;
       } else if (s == kSlotOk) {
         return __builtin_amdgcn_readfirstlane(*sWord) != 0;
@@ -1394,6 +1411,7 @@ __global__ void clear_ints_kernel(int* p, int n) {   // also zero-fills fp32 buf
 // Host side.
 // ---------------------------------------------------------------------------
 constexpr int kRingSlots = 8;         // ring slots per head (fused schedule)
+static_assert(kRingSlots <= kFlagLine, "a head's ready words share one line");
 constexpr int kMaxWgPerXcd = 32;      // MI355X: 256 CUs in 8 XCDs
 
 // Heads one fused launch can serve with `per_xcd` work-groups per XCD:
@@ -1407,7 +1425,7 @@ static int fused_heads_per_launch(int per_xcd, int ns) {
 template <typename TIn, int DK, int DV>
 static size_t fused_ctrl_bytes(int nheads) {
   constexpr int NS = ConsumerLds<TIn, DK, DV>::NS;
-  return ((size_t)(16 + nheads * kRingSlots + 2 * NS * nheads) * 4 + 255) / 256 * 256;
+  return ((size_t)(kFlagBase + nheads * kFlagLine + NS * nheads * kFlagLine + NS * nheads) * 4 + 255) / 256 * 256;
 }
 
 template <typename TIn, int DK, int DV>
@@ -1441,8 +1459,9 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   char* ring = reinterpret_cast<char*>(ws) + fused_ctrl_bytes<TIn, DK, DV>(batch);
   for (int head0 = 0; head0 < nbh; head0 += batch) {
     const int nh = nbh - head0 < batch ? nbh - head0 : batch;
-    const int nflags = nh * kRingSlots + 2 * NS * nh;   // ctrl[16 ..): this launch's flags only
-    hipLaunchKernelGGL(clear_ints_kernel, dim3((nflags + 255) / 256), dim3(256), 0, st, ctrl + 16, nflags);
+    // ctrl[kFlagBase ..): this launch's flags only
+    const int nflags = nh * kFlagLine + NS * nh * kFlagLine + NS * nh;
+    hipLaunchKernelGGL(clear_ints_kernel, dim3((nflags + 255) / 256), dim3(256), 0, st, ctrl + kFlagBase, nflags);
     // three variants: plain, unbounded decay, layer steps / snapshots
     const bool ext = lay.flags != 0 || lay.og != nullptr || (snap != nullptr && snap_every > 0);
     if (unb && ext) return hipErrorInvalidValue;
