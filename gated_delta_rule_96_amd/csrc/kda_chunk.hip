@@ -980,14 +980,22 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     const int htid = tid - 64 * kOwners;
     raw16 pre[PPT];
     bool ok = true;
-    // true once chunk c is published and may be read
-    auto ready_wait = [&](int c) -> bool {
+    // true once chunk c is published and may be read.  `seen` is chunk c's
+    // ready word as read one chunk earlier (device scope: an L2 copy of the
+    // word can lag behind the producer's agent-scope store); if it already
+    // shows the chunk, there is no polling at all.
+    auto ready_wait = [&](int c, int seen) -> bool {
       if (!kRing) return true;
-      const int v = spin_until_geq(ring.ready + c % ring.R, (c + 1) << 4, ring.err);
+      const int v = seen >= ((c + 1) << 4) ? seen : spin_until_geq(ring.ready + c % ring.R, (c + 1) << 4, ring.err);
       if (v < 0) return false;
       if ((v & 15) == my_xcc) asm volatile("buffer_inv sc0" ::: "memory");
       else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       return true;
+    };
+    auto peek = [&](int c) -> int {   // chunk c's ready word, read now, used a chunk later
+      return (kRing && c < nchunks)
+                 ? __hip_atomic_load(ring.ready + c % ring.R, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : 0;
     };
     // staged vector n: the shared part, then this work-group's Ut columns
     const int uoff16 = (int)((R::U_OFF_BYTES + (size_t)vb * CL::UPART) / 16) - NSH16;
@@ -1010,7 +1018,8 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       // handed back (after the next X)
       if (kRing) wait_vmem();
     };
-    ok = ready_wait(0);
+    ok = ready_wait(0, 0);
+    int seen_next = peek(1);
     if (ok) {
       load(0);
       stage(0);
@@ -1022,8 +1031,10 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
       // chunk c has been read completely: hand its slot back
       if (kRing && htid == 0) __hip_atomic_store(ring.done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int seen = __builtin_amdgcn_readfirstlane(seen_next);
+      seen_next = peek(c + 2);
       if (c + 1 < nchunks) {
-        ok = ready_wait(c + 1);
+        ok = ready_wait(c + 1, seen);
         if (ok) load(c + 1);
         else if (lane == 0) *sAbort = 1;
         if (NBUF == 1) __syncthreads();   // Y_c

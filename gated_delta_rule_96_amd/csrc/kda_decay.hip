@@ -10,7 +10,7 @@
 //
 // Layout [B, T, H, dk] with channels contiguous: one thread per
 // (b, chunk, h, 8 consecutive channels) walks the chunk's rows in order,
-// with one 16-byte load per row and eight rows in flight; a wave covers 512
+// with one 16-byte load per row and sixteen rows in flight; a wave covers 512
 // consecutive channels of a row (coalesced) and the scan needs no cross-lane
 // traffic.  Memory-bound; all arithmetic fp32.
 #include <stdlib.h>
@@ -23,13 +23,15 @@
 namespace kda {
 
 constexpr int kVE = 8;        // channels per thread
-constexpr int kRowsU = 8;     // rows loaded together
+constexpr int kRowsU = 16;    // rows loaded together
 
-// Eight consecutive elements of type T as fp32, and back (RNE).
+// Eight consecutive elements of type T as fp32, and back (RNE).  Every
+// element is read and written once: non-temporal accesses (streamed past
+// the caches).
 template <typename T> struct Eight;
 template <> struct Eight<bf16> {
   static __device__ __forceinline__ void load(const bf16* p, float (&x)[kVE]) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+    const bf16x8 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
 #pragma unroll
     for (int i = 0; i < kVE; ++i) x[i] = (float)v[i];
   }
@@ -37,12 +39,13 @@ template <> struct Eight<bf16> {
     bf16x8 v;
 #pragma unroll
     for (int i = 0; i < kVE; ++i) v[i] = (bf16)x[i];
-    *reinterpret_cast<bf16x8*>(p) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p));
   }
 };
 template <> struct Eight<float> {
   static __device__ __forceinline__ void load(const float* p, float (&x)[kVE]) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = a[i];
@@ -50,8 +53,8 @@ template <> struct Eight<float> {
     }
   }
   static __device__ __forceinline__ void store(float* p, const float (&x)[kVE]) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p + 4));
   }
 };
 
@@ -70,6 +73,7 @@ __global__ __launch_bounds__(256) void prepare_decay_kernel(const T* __restrict_
   const int t1 = min(t0 + chunk, T_len);
   const size_t base = (size_t)b * T_len * HD + hc;
   const float ea = kGate ? expf(A[hc / dk]) : 0.f;   // dk is a multiple of 8: one head per thread
+  const float nea2 = -ea * 1.4426950408889634f;        // -exp(A) log2(e)
   float acc[kVE];
 #pragma unroll
   for (int i = 0; i < kVE; ++i) acc[i] = 0.f;
@@ -90,9 +94,17 @@ __global__ __launch_bounds__(256) void prepare_decay_kernel(const T* __restrict_
       if (kGate) {
 #pragma unroll
         for (int i = 0; i < kVE; ++i) {
-          const float a = ea * x[u][i];
+          // bounded: gmin Sigmoid(a) = gmin / (1 + 2^{-a log2 e}) with v_exp_f32 and
+          // v_rcp_f32 (a few ulp of fp32, far below the bf16 rounding of g);
           // Softplus(a) = max(a, 0) + log(1 + e^{-|a|}), no overflow for large |a|
-          const float gf = kGate == 1 ? gmin / (1.0f + expf(-a)) : -(fmaxf(a, 0.f) + log1pf(expf(-fabsf(a))));
+          // (libm: near a = -inf it needs log1p's relative accuracy)
+          float gf;
+          if (kGate == 1) {
+            gf = gmin * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(nea2 * x[u][i]));
+          } else {
+            const float a = ea * x[u][i];
+            gf = -(fmaxf(a, 0.f) + log1pf(expf(-fabsf(a))));
+          }
           x[u][i] = (float)from_f32<T>(gf);   // the rounded g is what the scan sums
         }
         if (g && live) Eight<T>::store(g + idx, x[u]);
