@@ -288,6 +288,40 @@ int kda_fwd_chunked_varlen(const void* q, const void* k, const void* v, const vo
   const size_t esz = dtype == KDA_BF16 ? 2 : 4;
   const size_t hk = (size_t)H * dk, hv = (size_t)H * dv, sd = (size_t)H * dk * dv;
   const bool snaps = snap && snap_every > 0;
+  if (N <= kda::kMaxVarSeq) {
+    // one fused launch for all sequences: their chunks, in order, are every
+    // head's stream (the launch carries the sequence table)
+    kda::VarSeg vs{};
+    vs.n = N;
+    long long nch_total = 0, nsnap = 0;
+    for (int i = 0; i <= N; ++i) {
+      vs.cu[i] = cu_seqlens[i];
+      vs.cc[i] = (int)nch_total;
+      vs.sb[i] = (int)nsnap;
+      if (i == N) break;
+      const long long len = cu_seqlens[i + 1] - cu_seqlens[i];
+      const long long nch = (len + kChunk - 1) / kChunk;
+      nch_total += nch;
+      if (snaps && nch > 0) nsnap += (nch - 1) / snap_every;
+    }
+    for (int i = 0; i < N; ++i) {   // sequences without tokens: ht = h0 (or zero)
+      if (cu_seqlens[i + 1] != cu_seqlens[i]) continue;
+      const float* h0_i = h0 ? h0 + i * sd : nullptr;
+      float* ht_i = ht ? ht + i * sd : nullptr;
+      hipError_t e = hipSuccess;
+      if (ht_i && h0_i && ht_i != h0_i)
+        e = hipMemcpyAsync(ht_i, h0_i, sd * sizeof(float), hipMemcpyDeviceToDevice, hs);
+      else if (ht_i && !h0_i)
+        e = kda::launch_zero_words(ht_i, sd, hs);
+      if (e != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (nch_total == 0) return KDA_OK;
+    const hipError_t e = kda::launch_fwd_fused(dtype == KDA_BF16, q, k, v, g, nullptr, beta, scale, h0, ht, o, 1, T, H,
+                                               dk, dv, workspace, workspace_bytes, 0, snaps ? snap : nullptr,
+                                               snaps ? snap_every : 0, nullptr, nullptr, 0, hs, &vs);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
+  // more sequences than one launch carries: one fused launch per sequence
   long long snap_off = 0;
   for (int i = 0; i < N; ++i) {
     const size_t t0 = (size_t)cu_seqlens[i];

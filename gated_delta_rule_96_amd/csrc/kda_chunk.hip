@@ -235,12 +235,10 @@ template <typename TIn, int DK, int DV, int kParts = kLoadAll>
 __device__ __forceinline__ void load_inputs(InRegs<TIn, DK, DV>& in, const TIn* __restrict__ q,
                                             const TIn* __restrict__ k, const TIn* __restrict__ v,
                                             const TIn* __restrict__ g, const TIn* __restrict__ beta, int b, int h,
-                                            int T_len, int H, int ch) {
+                                            int T_len, int H, int t0, int Lrows) {
   using IR = InRegs<TIn, DK, DV>;
   constexpr int VE = IR::VE;
   const int tid = threadIdx.x;
-  const int t0 = ch * kC;
-  const int Lrows = min(kC, T_len - t0);
   const size_t tokk = (size_t)H * DK, tokv = (size_t)H * DV;
   const size_t base_k = ((size_t)b * T_len + t0) * tokk + (size_t)h * DK;
   const size_t base_v = ((size_t)b * T_len + t0) * tokv + (size_t)h * DV;
@@ -366,7 +364,8 @@ constexpr unsigned long long kTileB = 0x2110003210ull;
 constexpr unsigned long long kWaveTile0 = 0x94653210ull;
 constexpr unsigned long long kWaveTile1 = 0xff87ffffull;
 
-// Builds the record of chunk `ch` of head (b, h) at `rec`.  Called by a
+// Builds the record of the chunk of head (b, h) that starts at token t0 and
+// has Lrows rows (1 .. 64; the rest of the 64-row tile is zero) at `rec`.  Called by a
 // whole work-group of kThreads threads; `smem` holds IntraLds::BYTES.
 // `in` holds the chunk's inputs (load_inputs).  `slot(step)` (step an
 // std::integral_constant) is called by every thread: kSlotPeek once the
@@ -376,13 +375,13 @@ constexpr unsigned long long kWaveTile1 = 0xff87ffffull;
 // at four points of the later phases, with kLoadK | kLoadBeta, kLoadQ,
 // kLoadG, kLoadV in turn (as std::integral_constant), e.g. to load the next
 // chunk's inputs into `in` in portions while this one is computed.
-// kExt: the layer steps (Layer) may be requested; without it their code is
-// compiled out of the plain kernels.
+// kLay: the layer steps (Layer) may be requested; without it their code is
+// compiled out of the other kernels.
 constexpr int kSlotPeek = 0, kSlotCheck = 1, kSlotOk = 2;
 
-template <typename TIn, int DK, int DV, bool kUnb, bool kExt, typename Slot, typename Prefetch>
+template <typename TIn, int DK, int DV, bool kUnb, bool kLay, typename Slot, typename Prefetch>
 __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& in, const float* __restrict__ gcum,
-                                              float scale, int b, int h, int T_len, int H, int ch,
+                                              float scale, int b, int h, int T_len, int H, int t0, int Lrows,
                                               char* __restrict__ rec, Slot slot, Prefetch prefetch,
                                               Layer lay = Layer{nullptr, nullptr, 0}) {
   using P = Policy<TIn>;
@@ -413,8 +412,6 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = 4 * (lane >> 4);
-  const int t0 = ch * kC;
-  const int Lrows = min(kC, T_len - t0);
   const size_t tokk = (size_t)H * DK;
   const size_t base_k = ((size_t)b * T_len + t0) * tokk + (size_t)h * DK;
   __syncthreads();   // a previous call's LDS readers are done
@@ -427,8 +424,8 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   float* rUinv = reinterpret_cast<float*>(rec + R::UINV_OFF_BYTES);
 
   // ---- phase 0: stage k, q, beta (and g) from the input registers
-  const bool normqk = kExt && (lay.flags & kLayerNormQK) != 0;   // uniform
-  const bool gatez = kExt && (lay.flags & kLayerGateZ) != 0;
+  const bool normqk = kLay && (lay.flags & kLayerNormQK) != 0;   // uniform
+  const bool gatez = kLay && (lay.flags & kLayerGateZ) != 0;
   const float ea = gatez ? expf(lay.A[h]) : 0.f;   // exp(A), once per chunk
 #pragma unroll
   for (int i = 0; i < IR::NK; ++i) {
@@ -787,8 +784,9 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __rest
   __shared__ __align__(16) char smem[IntraLds<TIn, DK, DV>::BYTES];
   const int ch = blockIdx.x % nchunks, bh = blockIdx.x / nchunks;
   InRegs<TIn, DK, DV> in;
-  load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, ch);
-  produce_chunk<TIn, DK, DV, kUnb, false>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, ch,
+  const int t0 = ch * kC, rows = min(kC, T_len - t0);
+  load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, t0, rows);
+  produce_chunk<TIn, DK, DV, kUnb, false>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, t0, rows,
                                    ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [](auto) { return true; },
                                    [](auto) {});
 }
@@ -818,6 +816,23 @@ struct Ring {
 };
 
 constexpr int kSpinLimit = 1 << 20;   // about a second of polling before giving up
+
+// Position of stream chunk c of a head: first token, rows, sequence and the
+// chunk's index within it.  Without packed sequences (var->n == 0) chunk c
+// is tokens 64c .. of the one sequence; with them, sequence i owns stream
+// chunks cc[i] .. cc[i+1]-1.  Callers visit chunks in increasing order and
+// keep `seq` between calls (start at 0): it only moves forward, past the
+// sequences that end at or before c (empty ones included), so a sequence
+// change costs a few scalar loads and the usual call none beyond one.
+struct ChunkPos {
+  int t0, rows, seq, j;
+};
+__device__ __forceinline__ ChunkPos chunk_pos(const VarSeg* var, int c, int T_len, int& seq) {
+  if (var == nullptr || var->n == 0) return ChunkPos{c * kC, min(kC, T_len - c * kC), 0, c};
+  while (seq + 1 < var->n && var->cc[seq + 1] <= c) ++seq;
+  const int j = c - var->cc[seq], t0 = var->cu[seq] + j * kC;
+  return ChunkPos{t0, min(kC, var->cu[seq + 1] - t0), seq, j};
+}
 constexpr int kFlagBase = 32;         // first flag word of the fused schedule's control block
 constexpr int kFlagLine = 32;         // ints per 128-byte cache line
 
@@ -929,13 +944,14 @@ struct Snap {
   int nbh;
 };
 
-// kExt: snapshots and the output gate may be requested (compiled out
-// otherwise).
-template <typename TIn, int DK, int DV, bool kRing, bool kExt>
+// kLay: the output gate may be requested; kSeg: snapshots and packed
+// sequences may be requested (each compiled out otherwise).
+template <typename TIn, int DK, int DV, bool kRing, bool kLay, bool kSeg>
 __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
                                               const float* __restrict__ h0, float* __restrict__ ht,
                                               float* __restrict__ o, int b, int h, int T_len, int H,
-                                              int nchunks, Snap snap, Layer lay = Layer{nullptr, nullptr, 0}) {
+                                              int nchunks, Snap snap, Layer lay = Layer{nullptr, nullptr, 0},
+                                              const VarSeg* var = nullptr) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using R = Rec<TIn, DK, DV>;
@@ -1046,32 +1062,41 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     return;
   }
 
+  // Packed sequences (extended variant): the state restarts at every
+  // sequence's first chunk from its own h0 and is written to its own ht
+  // after its last.
+  const bool packed = kSeg && var != nullptr && var->n > 0;   // uniform
   // S from h0 (one wave-uniform branch around unconditional loads), used
   // before the loop, so that no wait inside the loop is tied to its loads
   f32x4 S[NCT];
   const size_t sbase = bh * DK * DV;
+  auto load_state = [&](const float* src) {   // src: this (b, h)'s dk x dv state, or null
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) S[ct] = zero4();
-  if (h0) {
+    for (int ct = 0; ct < NCT; ++ct) S[ct] = zero4();
+    if (src) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[ct][i] = h0[sbase + (size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16];
-  }
+        for (int i = 0; i < 4; ++i) S[ct][i] = src[(size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16];
+    }
+  };
   float m0 = 0.f;
+  if (!packed) {
+    load_state(h0 ? h0 + sbase : nullptr);
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) m0 = fmaxf(m0, absmax4(S[ct]));
-  m0 = wave_max_dpp(m0);
+    for (int ct = 0; ct < NCT; ++ct) m0 = fmaxf(m0, absmax4(S[ct]));
+    m0 = wave_max_dpp(m0);
+  }
 
-  // O of chunk c, as 16-byte non-temporal vectors (written once, not re-read)
-  auto store_out = [&](int c, const f32x4 (&Ov)[4]) {
-    const int t0 = c * kC;
+  // O of the chunk at tokens t0 .. t0 + rows - 1, as 16-byte non-temporal
+  // vectors (written once, not re-read)
+  auto store_out = [&](int t0, int rows, const f32x4 (&Ov)[4]) {
     float* orow = o + (((size_t)b * T_len + t0 + l16) * H + h) * DV + 16 * jt0 + g4;
     const size_t ors = (size_t)16 * H * DV;   // 16 rows
-    const bool full = t0 + kC <= T_len;       // uniform; only the last chunk is partial
+    const bool full = rows == kC;             // uniform; only a sequence's last chunk is partial
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
-      if (full || t0 + 16 * rt + l16 < T_len) __builtin_nontemporal_store(Ov[rt], reinterpret_cast<f32x4*>(orow + rt * ors));
+      if (full || 16 * rt + l16 < rows) __builtin_nontemporal_store(Ov[rt], reinterpret_cast<f32x4*>(orow + rt * ors));
   };
 
   const bool mixed = P::kMixed;
@@ -1080,6 +1105,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   // run split into several calls at chunk boundaries does the same
   // arithmetic as one call.
   int sig_e = 0;
+  int seq = 0;   // sequence cursor (packed sequences)
   for (int c = 0; c < nchunks; ++c) {
     __syncthreads();   // X_c
     if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
@@ -1091,10 +1117,21 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     const float* sDec = reinterpret_cast<const float*>(buf + R::DEC_OFF_BYTES);
     const float uinv = *reinterpret_cast<const float*>(buf + R::UINV_OFF_BYTES);
     const Op* sU = reinterpret_cast<const Op*>(buf + CL::SH);   // local column tiles, 4 jl + st
-    const int t0 = c * kC;
+    const ChunkPos pos = chunk_pos(packed ? var : nullptr, c, T_len, seq);
+    const int t0 = pos.t0;
+    const bool seq_last = packed && t0 + pos.rows == var->cu[pos.seq + 1];   // uniform
+    const size_t seq_state = ((size_t)pos.seq * H + h) * DK * DV;           // packed: this sequence's state
+    if (packed && pos.j == 0) {   // a sequence starts: its own initial state, sigma from it
+      load_state(h0 ? h0 + seq_state : nullptr);
+      m0 = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) m0 = fmaxf(m0, absmax4(S[ct]));
+      m0 = wave_max_dpp(m0);
+      sig_e = 0;
+    }
     // output gate values of this owner's outputs, loaded early
     f32x4 gz[4];
-    if (kExt && lay.og) {
+    if (kLay && lay.og) {
       const TIn* og = reinterpret_cast<const TIn*>(lay.og);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
@@ -1200,13 +1237,13 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         m += nms;
         Ov[rt] = (scl ? accO[rt] + am * ir : am) * isig;
       }
-      if (kExt && lay.og) {   // output gate: o <- Sigmoid(og) o
+      if (kLay && lay.og) {   // output gate: o <- Sigmoid(og) o
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) Ov[rt][i] *= sigmoid_fast(gz[rt][i]);
       }
-      store_out(c, Ov);
+      store_out(t0, pos.rows, Ov);
       float smax = 0.f;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -1217,17 +1254,26 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     };
     if (__builtin_amdgcn_readfirstlane(re)) tail(std::true_type{});
     else tail(std::false_type{});
-    if (kExt && snap.p && snap.every > 0 && (c + 1) % snap.every == 0 && (c + 1) * kC < T_len) {
-      float* sp = snap.p + ((size_t)((c + 1) / snap.every - 1) * snap.nbh + bh) * DK * DV;
+    if (kSeg && snap.p && snap.every > 0 && (pos.j + 1) % snap.every == 0 &&
+        (packed ? !seq_last : (c + 1) * kC < T_len)) {
+      const int si = (packed ? var->sb[pos.seq] : 0) + (pos.j + 1) / snap.every - 1;
+      float* sp = snap.p + ((size_t)si * snap.nbh + bh) * DK * DV;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sp[(size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
     }
+    if (packed && seq_last && ht) {   // the sequence's final state
+      const float isig = ldexpf(1.f, -sig_e);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ht[seq_state + (size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
+    }
     if (NBUF == 1) __syncthreads();   // Y_c
   }
 
-  if (ht) {
+  if (ht && !packed) {
     const float isig = ldexpf(1.f, -sig_e);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -1245,7 +1291,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
   using CL = ConsumerLds<TIn, DK, DV>;
   __shared__ __align__(16) char smem[CL::BYTES];
   const int bh = blockIdx.x / CL::NS, vb = blockIdx.x % CL::NS;
-  consume_chain<TIn, DK, DV, false, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
+  consume_chain<TIn, DK, DV, false, false, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
                                            Ring{nullptr, nullptr, nullptr, nullptr, 1}, vb, h0, ht, o, bh / H,
                                            bh % H, T_len, H, nchunks, snap);
 }
@@ -1292,7 +1338,7 @@ struct FusedLds {
   static constexpr size_t BYTES = (A > B ? A : B) + 16;
 };
 
-template <typename TIn, int DK, int DV, bool kUnb, bool kExt>
+template <typename TIn, int DK, int DV, bool kUnb, bool kLay, bool kSeg>
 __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                              const TIn* __restrict__ v, const TIn* __restrict__ g,
                                                              const float* __restrict__ gcum,
@@ -1300,9 +1346,11 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
                                                              const float* __restrict__ h0, float* __restrict__ ht,
                                                              float* __restrict__ o, int T_len, int H, int nchunks,
                                                              int head0, int nheads, char* __restrict__ ring,
-                                                             int* __restrict__ ctrl, int R, Snap snap, Layer lay) {
+                                                             int* __restrict__ ctrl, int R, Snap snap, Layer lay,
+                                                             VarSeg var) {
   using Rc = Rec<TIn, DK, DV>;
   __shared__ __align__(16) char smem[FusedLds<TIn, DK, DV>::BYTES];
+  const VarSeg* vp = kSeg ? &var : nullptr;   // packed sequences (snapshot variant only)
   int* sWord = reinterpret_cast<int*>(smem + FusedLds<TIn, DK, DV>::BYTES - 16);
   const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
   const int nloc = nheads > xcd ? (nheads - xcd + 7) / 8 : 0;   // heads j = xcd + 8m of this launch
@@ -1314,11 +1362,11 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
 
   if (li < nloc * NS) {   // consumer vb of head jh
     const int jh = xcd + 8 * (li / NS), vb = li % NS, bh = head0 + jh;
-    consume_chain<TIn, DK, DV, true, kExt>(smem, ring + (size_t)jh * R * Rc::BYTES,
+    consume_chain<TIn, DK, DV, true, kLay, kSeg>(smem, ring + (size_t)jh * R * Rc::BYTES,
                                            Ring{ready + jh * kFlagLine, done + (jh * NS + vb) * kFlagLine, err,
                                                 cxcc + jh * NS + vb, R},
                                            vb,
-                                           h0, ht, o, bh / H, bh % H, T_len, H, nchunks, snap, lay);
+                                           h0, ht, o, bh / H, bh % H, T_len, H, nchunks, snap, lay, vp);
     return;
   }
 
@@ -1334,9 +1382,11 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   InRegs<TIn, DK, DV> in;
   int it = li - nloc * NS;
   if (it >= total) return;
+  int seq_cur = 0, seq_next = 0;   // sequence cursors of this item and of the next one
   {
     const int jh = xcd + 8 * (it % nloc), bh = head0 + jh;
-    load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, it / nloc);
+    const ChunkPos ps = chunk_pos(vp, it / nloc, T_len, seq_next);
+    load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, ps.t0, ps.rows);
   }
   // Publishes item `pi` (its record stores were issued by every wave).
   // Release: if the head's consumers run on this XCD they read through the
@@ -1365,6 +1415,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   for (;;) {
     const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
     const int nxt = it + P;
+    const ChunkPos pc = chunk_pos(vp, c, T_len, seq_cur);
     // The ring slot of chunk c is free once the head's consumers have read
     // chunk c - R.  Wave 0 reads their progress words from this XCD's L2
     // once the inputs are staged (after the input registers are consumed:
@@ -1397,11 +1448,12 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     auto prefetch = [&](auto parts) {
       if (nxt < total) {
         const int jn = xcd + 8 * (nxt % nloc), bn = head0 + jn;
-        load_inputs<TIn, DK, DV, decltype(parts)::value>(in, q, k, v, g, beta, bn / H, bn % H, T_len, H,
-                                                         nxt / nloc);
+        const ChunkPos pn = chunk_pos(vp, nxt / nloc, T_len, seq_next);
+        load_inputs<TIn, DK, DV, decltype(parts)::value>(in, q, k, v, g, beta, bn / H, bn % H, T_len, H, pn.t0,
+                                                         pn.rows);
       }
     };
-    if (!produce_chunk<TIn, DK, DV, kUnb, kExt>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, c,
+    if (!produce_chunk<TIn, DK, DV, kUnb, kLay>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, pc.t0, pc.rows,
                                     ring + ((size_t)jh * R + c % R) * Rc::BYTES, slot, prefetch, lay))
       return;
     // Published as soon as its stores are in the L2.  (Deferring this until
@@ -1450,8 +1502,13 @@ template <typename TIn, int DK, int DV>
 static hipError_t go_fused(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                            const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
                            int H, void* ws, size_t ws_bytes, bool unb, float* snap, int snap_every, Layer lay,
-                           hipStream_t st) {
-  const int nchunks = (T_len + kC - 1) / kC;
+                           hipStream_t st, const VarSeg* var) {
+  // packed sequences: every head's stream is the sequences' chunks in order
+  const bool packed = var != nullptr && var->n > 0;
+  const int nchunks = packed ? var->cc[var->n] : (T_len + kC - 1) / kC;
+  if (packed && (B != 1 || unb || gcum)) return hipErrorInvalidValue;
+  if (nchunks <= 0) return hipSuccess;
+  static const VarSeg kNoVar{};
   const int nbh = B * H;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1473,14 +1530,17 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
     // ctrl[kFlagBase ..): this launch's flags only
     const int nflags = nh * kFlagLine + NS * nh * kFlagLine + NS * nh;
     hipLaunchKernelGGL(clear_ints_kernel, dim3((nflags + 255) / 256), dim3(256), 0, st, ctrl + kFlagBase, nflags);
-    // three variants: plain, unbounded decay, layer steps / snapshots
-    const bool ext = lay.flags != 0 || lay.og != nullptr || (snap != nullptr && snap_every > 0);
-    if (unb && ext) return hipErrorInvalidValue;
-    auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true, false>
-                    : (ext ? fused_fwd_kernel<TIn, DK, DV, false, true> : fused_fwd_kernel<TIn, DK, DV, false, false>);
+    // four variants: plain, unbounded decay, layer steps, snapshots / packed sequences
+    const bool with_lay = lay.flags != 0 || lay.og != nullptr;
+    const bool with_seg = (snap != nullptr && snap_every > 0) || packed;
+    if ((unb && (with_lay || with_seg)) || (with_lay && with_seg)) return hipErrorInvalidValue;
+    auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true, false, false>
+                    : with_lay ? fused_fwd_kernel<TIn, DK, DV, false, true, false>
+                               : (with_seg ? fused_fwd_kernel<TIn, DK, DV, false, false, true>
+                                           : fused_fwd_kernel<TIn, DK, DV, false, false, false>);
     hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q, (const TIn*)k, (const TIn*)v,
                        (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len, H, nchunks, head0, nh, ring,
-                       ctrl, kRingSlots, Snap{snap, snap_every, nbh}, lay);
+                       ctrl, kRingSlots, Snap{snap, snap_every, nbh}, lay, packed ? *var : kNoVar);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1537,9 +1597,9 @@ template <typename TIn>
 static hipError_t fused_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
                           const void* beta, float scale, const float* h0, float* ht, float* o, int B, int T_len,
                           int H, int dk, int dv, void* ws, size_t wsb, bool unb, float* snap, int snap_every,
-                          Layer lay, hipStream_t st) {
+                          Layer lay, hipStream_t st, const VarSeg* var) {
   KDA_DISPATCH_D(go_fused, q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, ws, wsb, unb, snap, snap_every,
-                 lay, st);
+                 lay, st, var);
 }
 template <typename TIn>
 static hipError_t stages_t(const void* q, const void* k, const void* v, const void* g, const float* gcum,
@@ -1554,14 +1614,14 @@ hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const voi
                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
                             int B, int T_len, int H, int dk, int dv, void* ws, size_t ws_bytes, int unbounded,
                             float* snap, int snap_every, const float* A, const void* og, int layer_flags,
-                            hipStream_t st) {
+                            hipStream_t st, const VarSeg* var) {
   const bool u = unbounded != 0;
   const Layer lay{A, og, layer_flags};
   if (is_bf16)
     return fused_t<bf16>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, snap,
-                         snap_every, lay, st);
+                         snap_every, lay, st, var);
   return fused_t<float>(q, k, v, g, gcum, beta, scale, h0, ht, o, B, T_len, H, dk, dv, ws, ws_bytes, u, snap,
-                        snap_every, lay, st);
+                        snap_every, lay, st, var);
 }
 
 hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,

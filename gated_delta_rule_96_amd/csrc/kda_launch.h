@@ -27,17 +27,33 @@ size_t fwd_record_bytes(int is_bf16, int dk, int dv);
 // Workspace of the fused single-pass schedule (ring buffers + control words).
 size_t fwd_fused_workspace_bytes(int is_bf16, int nbh, int dk, int dv);
 
+// Up to kMaxVarSeq packed sequences of one variable-length prefill, carried
+// in the fused kernel's launch arguments: sequence i is tokens cu[i] ..
+// cu[i+1]-1 of the packed axis, its chunks (every chunk starts at the
+// sequence start) are stream chunks cc[i] .. cc[i+1]-1 of every head, and its
+// first snapshot is snapshot sb[i].  n = 0: one plain sequence per (b, h).
+constexpr int kMaxVarSeq = 128;
+struct VarSeg {
+  int n;
+  int cu[kMaxVarSeq + 1];
+  int cc[kMaxVarSeq + 1];
+  int sb[kMaxVarSeq + 1];
+};
+
 // Chunked prefill, fused schedule (one persistent kernel per batch of heads).
 // unbounded != 0: the decay may go below -5 (diagonal tiles by position pairs).
 // snap != nullptr, snap_every > 0: states after every snap_every chunks
 // (excluding the end) to snap[j][b * H + h][dk][dv].
+// var != nullptr (B = 1): the packed sequences above, h0 / ht [n][H][dk][dv]
+// (h0 nullable), snapshots numbered per sequence from sb[i]; sequences
+// without tokens are not touched.
 // layer_flags (1: g is z, gate with A fused into the scan; 2: q/k rows L2
 // normalised in-kernel) and og (output gate pre-activation, nullable).
 hipError_t launch_fwd_fused(int is_bf16, const void* q, const void* k, const void* v, const void* g,
                             const float* gcum, const void* beta, float scale, const float* h0, float* ht, float* o,
                             int B, int T, int H, int dk, int dv, void* workspace, size_t workspace_bytes,
                             int unbounded, float* snap, int snap_every, const float* A, const void* og,
-                            int layer_flags, hipStream_t stream);
+                            int layer_flags, hipStream_t stream, const VarSeg* var = nullptr);
 
 // Chunked prefill, two-stage schedule: bit 0 intra-chunk kernel, bit 1 state pass.
 hipError_t launch_fwd_stages(int is_bf16, const void* q, const void* k, const void* v, const void* g,

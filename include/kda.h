@@ -264,8 +264,10 @@ int kda_fwd_chunked_layer(const void* q, const void* k, const void* v, const voi
  * [S,H,dk,dv] fp32, sequences in order, snapshots in order within one;
  * S = kda_fwd_varlen_snapshots(cu_seqlens, N, snap_every, chunk).
  * workspace: kda_fwd_workspace_bytes(1, T, H, dk, dv, chunk, dtype) bytes.
- * One fused launch per non-empty sequence, in order on `stream`; the
- * status word (kda_fwd_status) covers all of them.  gcum must be NULL (a
+ * Up to 128 sequences: one fused launch for all of them (each head's chunks
+ * of every sequence, in order, with the state restarted at each sequence's
+ * first chunk); more sequences: one fused launch per non-empty sequence, in
+ * order on `stream`.  The status word (kda_fwd_status) covers the call.  gcum must be NULL (a
  * gcum of the packed axis restarts at multiples of 64 tokens, not at each
  * sequence's own chunks): KDA_ERR_UNSUPPORTED otherwise.
  * Errors: as kda_fwd_chunked; KDA_ERR_NULL for cu_seqlens == NULL,
