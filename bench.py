@@ -748,12 +748,15 @@ def main():
     if not args.no_decode:
         log(f"decode B={DB} H={DH} steps={args.decode_steps}")
         st = torch.from_numpy(synth.initial_state(3, DB, DH, DK, DV)).to(dev)
-        pool = []
+        pool, lpool = [], []
         for s in range(DPOOL):
             tk = synth.decode_tokens(DB, DH, DK, DV, seed=3, step=s)
             tq, tkk, tv, tb, tz = (bf(tk[n]).to(dev) for n in ("q", "k", "v", "beta", "z"))
             tg, _ = kda.prepare_decay(tz[:, None].contiguous(), torch.from_numpy(tk["A"]).to(dev), want_gcum=False)
             pool.append((tq, tkk, tv, tg[:, 0].contiguous(), tb))
+            tog = bf(2.0 * tk["v"]).to(dev)   # an output-gate pre-activation of the same shape as v
+            lpool.append((tq, tkk, tv, tz, tb, tog))
+        A_dec = torch.from_numpy(synth.decode_tokens(DB, DH, DK, DV, seed=3, step=0)["A"]).to(dev)
         od = torch.empty((DB, DH, DV), dtype=torch.float32, device=dev)
         for s in range(5):
             kda.decode_step(*pool[s % DPOOL], st, out=od)
@@ -767,6 +770,22 @@ def main():
         d_ms = e0.elapsed_time(e1) / args.decode_steps
         d_bytes = decode_alg_bytes(DB, DH, DK, DV)
         d_gbs = d_bytes / (d_ms * 1e-3) / 1e9
+        # the same steps with the layer's steps fused in (gate of z, q/k
+        # normalisation, output gate): z replaces g, og adds 2 dv bytes
+        def layer_step(s):
+            q_, k_, v_, z_, b_, og_ = lpool[s % DPOOL]
+            kda.decode_step_layer(q_, k_, v_, z_, A_dec, b_, st, og=og_, qk_l2norm=True, out=od)
+        for s in range(5):
+            layer_step(s)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(args.decode_steps):
+            layer_step(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dl_ms = e0.elapsed_time(e1) / args.decode_steps
+        dl_bytes = d_bytes + DB * DH * 2 * DV
+        dl_gbs = dl_bytes / (dl_ms * 1e-3) / 1e9
         decode = {
             "workload": f"KDA decode step B={DB} H={DH} dk=dv={DK}, fp32 state, {args.decode_steps} consecutive steps "
                         f"(token inputs cycle through {DPOOL} seeded steps)",
@@ -775,9 +794,13 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(d_gbs / HBM_PEAK_GBS, 4), "traffic": None},
             "alg_bytes_per_step": d_bytes,
+            "layer_steps": {"what": "kda_decode_step_layer: gate of z, q/k L2 normalisation, sigmoid output gate",
+                            "us_per_step": round(dl_ms * 1e3, 2), "alg_bytes_per_step": dl_bytes,
+                            "hbm_frac": round(dl_gbs / HBM_PEAK_GBS, 4)},
         }
-        log(f"decode: {d_ms * 1e3:.1f} us/step, {d_gbs:.0f} GB/s")
-        del st, pool
+        log(f"decode: {d_ms * 1e3:.1f} us/step, {d_gbs:.0f} GB/s; with the layer steps "
+            f"{dl_ms * 1e3:.1f} us/step, {dl_gbs:.0f} GB/s")
+        del st, pool, lpool
 
     # ---------------- parity of the timed output on a sample + CPU oracle baseline
     parity = None

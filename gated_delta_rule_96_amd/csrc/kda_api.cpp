@@ -369,6 +369,24 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_decode_step_layer(const void* q, const void* k, const void* v, const void* z, const float* A,
+                          const void* beta, const void* og, float scale, float* state, float* o, int flags,
+                          int dtype, int B, int H, int dk, int dv, void* stream) {
+  if (!valid_dtype(dtype)) return KDA_ERR_DTYPE;
+  if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0 || !size_ok(B, H, dk, dv)) return KDA_ERR_SHAPE;
+  if (!supported_d(dk) || !supported_d(dv)) return KDA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !z || !A || !beta || !state || !o) return KDA_ERR_NULL;
+  if (flags & ~KDA_LAYER_QK_L2NORM) return KDA_ERR_SHAPE;
+  for (const void* p : {q, k, v, z, beta, (const void*)A, (const void*)state, (const void*)o})
+    if (!aligned16(p)) return KDA_ERR_ALIGN;
+  if (og && !aligned16(og)) return KDA_ERR_ALIGN;
+  if ((long long)B * H > 2147483647LL) return KDA_ERR_SHAPE;
+  const kda::DecodeLayer lay{A, og, (flags & KDA_LAYER_QK_L2NORM) ? kda::kDecodeLayerNormQK : 0};
+  hipError_t e = kda::launch_decode_step(dtype == KDA_BF16, q, k, v, z, beta, scale, state, o, B, H, dk, dv,
+                                         static_cast<hipStream_t>(stream), &lay);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace {

@@ -174,13 +174,6 @@ __device__ __forceinline__ void wave_tile(int w, int j, int per_wave, int& x, in
 //   og != nullptr output gate: o <- Sigmoid(og) * o, og [B,T,H,dv] of the
 //                 input type
 constexpr int kLayerGateZ = 1, kLayerNormQK = 2;
-// Sigmoid(x) = 1 / (1 + e^{-x}) with v_exp_f32 and v_rcp_f32 (about 2 ulp;
-// 0 and 1 at the far ends).
-__device__ __forceinline__ float sigmoid_fast(float x) {
-  return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-x * kLog2e));
-}
-constexpr float kGateMin = -5.0f;
-constexpr float kNormEps = 1e-6f;
 struct Layer {
   const float* A;
   const void* og;

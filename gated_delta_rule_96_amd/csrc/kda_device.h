@@ -129,6 +129,15 @@ __device__ __forceinline__ f32x4 exp2v(f32x4 x) {
   return f32x4{exp2_fast(x[0]), exp2_fast(x[1]), exp2_fast(x[2]), exp2_fast(x[3])};
 }
 constexpr float kLog2e = 1.4426950408889634f;
+// Sigmoid(x) = 1 / (1 + e^{-x}) with v_exp_f32 and v_rcp_f32 (about 2 ulp;
+// 0 and 1 at the far ends).
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-x * kLog2e));
+}
+// The layer's steps: lower bound of the decay gate g = gmin Sigmoid(exp(A) z)
+// and the epsilon of the q/k row normalisation x / sqrt(sum x^2 + eps).
+constexpr float kGateMin = -5.0f;
+constexpr float kNormEps = 1e-6f;
 
 __device__ __forceinline__ float absmax4(f32x4 v) {
   return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));

@@ -78,10 +78,22 @@ constexpr size_t kNoAllocScratchBytes = (size_t)40 << 20;
 hipError_t noalloc_scratch(void** ptr);
 
 
-// One decode token per (b, h), state updated in place.
+// The decode step's layer steps: g holds z and the gate is formed from
+// A [H] fp32; flags & kDecodeLayerNormQK normalises the q and k rows; og
+// [B,H,dv] of the input type (or null) gates the output.
+constexpr int kDecodeLayerNormQK = 2;
+struct DecodeLayer {
+  const float* A;
+  const void* og;
+  int flags;
+};
+
+// One decode token per (b, h), state updated in place (lay: the layer
+// variant, or null for the plain step).
 hipError_t launch_decode_step(int is_bf16, const void* q, const void* k, const void* v,
                               const void* g, const void* beta, float scale, float* state, float* o,
-                              int B, int H, int dk, int dv, hipStream_t stream);
+                              int B, int H, int dk, int dv, hipStream_t stream,
+                              const DecodeLayer* lay = nullptr);
 
 // Backward: fp32 words of one per-chunk record, and the three kernels after
 // a forward pass that kept the state entering every chunk in snap

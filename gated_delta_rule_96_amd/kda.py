@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked_stages.argtypes = [P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P, S, I, P]
         L.kda_decode_step.restype = I
         L.kda_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, I, P]
+        L.kda_decode_step_layer.restype = I
+        L.kda_decode_step_layer.argtypes = [P, P, P, P, P, P, P, F, P, P, I, I, I, I, I, I, P]
         L.kda_bwd_workspace_bytes.restype = S
         L.kda_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.kda_bwd_chunked.argtypes = [P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, S, P]
@@ -360,4 +362,33 @@ def decode_step(q, k, v, g, beta, state, *, scale=None, out=None):
         raise ValueError("out must be fp32 [B, H, dv]")
     _check(lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state),
                                  _ptr(o), dt, B, H, dk, dv, _stream(q.device)), "kda_decode_step")
+    return o
+
+
+def decode_step_layer(q, k, v, z, A, beta, state, *, og=None, qk_l2norm=False, scale=None, out=None):
+    """o = decode_step_layer(q, k, v, z, A, beta, state): decode_step with the
+    decay gate of z (A [H] fp32), optional q/k row L2 normalisation and an
+    optional sigmoid output gate og [B,H,dv] (same dtype as q) fused in;
+    state [B,H,dk,dv] fp32 is updated in place."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("z", z), ("beta", beta)) + ((("og", og),) if og is not None else ()):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} != q dtype {q.dtype}")
+    if A.dtype != torch.float32 or A.shape != (H,):
+        raise ValueError("A must be fp32 [H]")
+    if og is not None and og.shape != (B, H, dv):
+        raise ValueError("og must be [B, H, dv]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if state.dtype != torch.float32 or state.shape != (B, H, dk, dv):
+        raise ValueError("state must be fp32 [B, H, dk, dv]")
+    o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device) if out is None else out
+    if o.dtype != torch.float32 or o.shape != (B, H, dv):
+        raise ValueError("out must be fp32 [B, H, dv]")
+    flags = KDA_LAYER_QK_L2NORM if qk_l2norm else 0
+    _check(lib().kda_decode_step_layer(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A), _ptr(beta), _ptr(og),
+                                       float(scale), _ptr(state), _ptr(o), flags, dt, B, H, dk, dv,
+                                       _stream(q.device)), "kda_decode_step_layer")
     return o

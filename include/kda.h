@@ -314,6 +314,25 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
                     int B, int H, int dk, int dv, void* stream);
 
 /*
+ * Decode step with the layer's steps on either side fused in, as
+ * kda_fwd_chunked_layer does for the prefill (so that a sequence prefilled
+ * with the layer call continues with the same arithmetic):
+ *   - z [B,H,dk] of dtype instead of g, A [H] fp32: g = -5 Sigmoid(exp(A[h]) z)
+ *     in fp32 ("Key claims", section 2.1.1; "Method", section 2.1);
+ *   - flags & KDA_LAYER_QK_L2NORM: q and k rows divided by
+ *     sqrt(sum of squares + 1e-6) in fp32, then rounded to dtype;
+ *   - og != NULL ([B,H,dv] of dtype): o = Sigmoid(og) * o.
+ * Other arguments, layouts and errors as kda_decode_step; z is not range
+ * checked (the gate maps every finite z into [-5, 0]); KDA_ERR_NULL for z
+ * or A NULL, KDA_ERR_SHAPE for unknown flag bits, KDA_ERR_ALIGN for A or og
+ * not 16-byte aligned.
+ */
+int kda_decode_step_layer(const void* q, const void* k, const void* v, const void* z,
+                          const float* A, const void* beta, const void* og, float scale,
+                          float* state, float* o, int flags, int dtype, int B, int H, int dk,
+                          int dv, void* stream);
+
+/*
  * Backward of the chunked prefill: gradients of a loss L with respect to the
  * inputs of kda_fwd_chunked, given dout = dL/do and dht = dL/dht (Kimi K3
  * technical report summary, "Method", section 2.1: the chunkwise form; its

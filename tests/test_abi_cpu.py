@@ -91,6 +91,22 @@ def test_decode_validation():
     assert L.kda_decode_step(*bad) == 3
 
 
+def test_decode_layer_validation():
+    L = kda.lib()
+    args = [FAKE] * 6 + [None, 0.1, FAKE, FAKE, 1, 1, 2, 2, 128, 128, None]
+    for i in (3, 4):   # z, A
+        bad = list(args); bad[i] = None
+        assert L.kda_decode_step_layer(*bad) == 1
+    bad = list(args); bad[10] = 4   # unknown flag bit
+    assert L.kda_decode_step_layer(*bad) == 2
+    bad = list(args); bad[6] = FAKE + 8   # og misaligned
+    assert L.kda_decode_step_layer(*bad) == 4
+    bad = list(args); bad[14] = 32
+    assert L.kda_decode_step_layer(*bad) == 5
+    bad = list(args); bad[11] = 2
+    assert L.kda_decode_step_layer(*bad) == 3
+
+
 def test_prepare_decay_validation():
     L = kda.lib()
     # gate mode without A, scan mode without gcum, unsupported chunk
