@@ -301,19 +301,21 @@ constexpr int kNBlk = 19;
 //   P0 : g, then G (fp32 [C][LG])                        [phase 0]
 //        -> KP (fp32 [C][LG])                              [0 - 2b]
 //   P1 : k, q (input type, [C][LK] each)                   [phase 0]
-//        -> QP at 0, KE at PB (fp32 [C][LG] each)          [0 - 2a]
+//        -> QP at 0, KE at PB (fp32 [C][LG] each)          [0 - 1]
 //        -> Kbar^T (Op [DK][LB]) at 0, V^T (Op [DV][LB]) at KT   [2b - 3]
-//   X  : (phase 0: diagonal A tiles where A goes; M's diagonal tiles and
-//        the block totals where X goes), then A and X fp32 [C][LA]  [1 - 2b]
+//   X  : (phase 0: diagonal A tiles where A goes; the block totals where X
+//        goes), then A and X fp32 [C][LA]                  [1 - 2b]
 //        -> Tm (Op [C][LB]) where A was                     [2b - 3]
 //   BLK: fp32 [kNBlk][DK] per-channel factors                [0 - 2b]
+//   MD : (kUnb) M's diagonal tiles by position pairs       [0 - 1]
 // Phases: 0 stage inputs, block scans, exponentials, factors (kUnb: and the
 // diagonal tiles by position pairs); Khat goes to the record straight from
 // the scan registers (a thread holds 16 rows of one channel, four rows per
-// record lane); 1 Gram tiles (A -> LDS, scale M -> record); 2a wave 0
-// inverts the diagonal blocks of I + A while waves 1-7 write Qbar and
-// e^{Gamma_C} to the record; 2b Kbar^T and V^T staged, off-diagonal blocks
-// of the inverse, Tm; 3 W = Tm Kbar, Ut = Tm V to the record.
+// record lane); 1 Gram tiles (A -> LDS, scale M -> record), then each wave
+// that held a diagonal tile inverts that block of I + A while the others
+// write Qbar and e^{Gamma_C} to the record; 2b Kbar^T and V^T staged,
+// off-diagonal blocks of the inverse, Tm; 3 W = Tm Kbar, Ut = Tm V to the
+// record.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct IntraLds {
@@ -336,9 +338,10 @@ struct IntraLds {
   static constexpr size_t BLK = X + X_SIZE;
   static constexpr size_t BETA = BLK + (size_t)kNBlk * DK * 4;
   static constexpr size_t RED = BETA + kC * 4;
-  static constexpr size_t BYTES = RED + 16 * 4;
+  static constexpr size_t MD = RED + 16 * 4;
+  static constexpr size_t BYTES = MD + 4 * 256 * 4;
   static_assert((size_t)kC * LB * sizeof(Op) <= (size_t)kC * LA * 4, "Tm fits where A was");
-  static_assert(4 * 256 * 4 + 4 * (size_t)DK * 4 <= (size_t)kC * LA * 4, "M diagonal tiles and totals fit in X");
+  static_assert(4 * (size_t)DK * 4 <= (size_t)kC * LA * 4, "block totals fit in X");
 };
 
 // Small per-wave tables are packed into 64-bit immediates, 4 bits per
@@ -396,8 +399,8 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   Op* sVt = reinterpret_cast<Op*>(smem + L::P1 + L::KT);
   float* sA = reinterpret_cast<float*>(smem + L::X);
   float* sX = sA + kC * L::LA;
-  float* sMd = sX;                                        // [4][16][16], phase 0-1
-  float* sTot = sX + 4 * 256;                             // [4][DK], phase 0
+  float* sMd = reinterpret_cast<float*>(smem + L::MD);    // [4][16][16], phase 0-1 (kUnb)
+  float* sTot = sX;                                       // [4][DK], phase 0
   Op* sTm = reinterpret_cast<Op*>(smem + L::X);           // phases 2b-3
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
   float* sBlk = reinterpret_cast<float*>(smem + L::BLK);
@@ -626,6 +629,64 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     const int zt = w - 2, kt = nib(kTileA, 4 + zt), rt = nib(kTileB, 4 + zt);
     store4<Op>(rM + tile_elem(tile_cr(kt, rt), lane), narrow4<Op>(zero4()));
   }
+  if (w < 4) {
+    // The wave that held diagonal tile (a, a) (or, kUnb, any wave a < 4:
+    // the tiles were written in phase 0) inverts that block: X_aa =
+    // (I + A_aa)^-1 by forward substitution, lane j % 16 = column j (lanes
+    // of the same column compute the same values; those of lanes 0-15 are
+    // stored).  Row by row: x_i = -sum_{m<i} A_im x_m for i != j (x_m = 0
+    // for m < j), a 16-byte read of row i per four terms.  This wave wrote
+    // the block (or it was complete at the last barrier): LDS accesses of
+    // one wave are performed in order.
+    const int a = w;
+    const float* Ab = sA + 16 * a * L::LA + 16 * a;
+    const int j = lane & 15;
+    float x[16];
+    x[0] = j == 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int q4 = 0; 4 * q4 < i; ++q4) {
+        const f32x4 ar = *reinterpret_cast<const f32x4*>(Ab + i * L::LA + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q4 + e < i) s = fmaf(ar[e], x[4 * q4 + e], s);
+      }
+      x[i] = i == j ? 1.f : 0.f - s;
+    }
+    if (lane < 16) {
+      float* Xb = sX + 16 * a * L::LA + 16 * a;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Xb[i * L::LA + j] = x[i];
+    }
+  } else {
+    // Qbar tiles (ct, rt) and e^{Gamma_C} to the record: waves 4 and 5
+    // (two Gram tiles each) take NQT / 8 tiles, waves 6 and 7 (one) 3 NQT / 8,
+    // in groups of up to four whose operands are read before their stores.
+    auto qbar = [&](auto cnt, int t0q) {
+      constexpr int N = decltype(cnt)::value, NG = N % 4 == 0 ? 4 : (N % 3 == 0 ? 3 : N);
+      static_assert(N % NG == 0, "groups");
+#pragma unroll
+      for (int g0 = 0; g0 < N; g0 += NG) {
+        f32x4 qv[NG], fv[NG];
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+          const int tq = t0q + g0 + n, ct = tq >> 2, rt = tq & 3;
+          fv[n] = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + 16 * ct + g4);
+          qv[n] = *reinterpret_cast<const f32x4*>(sQP + (16 * rt + l16) * L::LG + 16 * ct + g4);
+        }
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+          const int tq = t0q + g0 + n, ct = tq >> 2, rt = tq & 3;
+          store4<Op>(rQ + tile_elem(tile_cr(ct, rt), lane), narrow4<Op>(qv[n] * (fv[n] * scale)));
+        }
+      }
+    };
+    if (w < 6) qbar(std::integral_constant<int, NQT / 8>{}, (w - 4) * (NQT / 8));
+    else qbar(std::integral_constant<int, 3 * NQT / 8>{}, NQT / 4 + (w - 6) * (3 * NQT / 8));
+    if (tid >= 6 * 64 && tid < 6 * 64 + DK) rDec[tid - 6 * 64] = sBlk[kBlkDec * DK + tid - 6 * 64];
+  }
   // V's range (for its fp16 staging): wave maxima of the chunk's v, combined
   // after the barrier
   float vmax = 0.f;
@@ -636,38 +697,8 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   vmax = wave_max_dpp(vmax);
   if (lane == 0) sRed[w] = vmax;
   prefetch(std::integral_constant<int, kLoadQ>{});
-  __syncthreads();   // A complete
-
-  // ---- phase 2a: diagonal blocks of X = (I + A)^-1 (wave 0) while waves
-  // 1-7 write Qbar and e^{Gamma_C} to the record
-  if (w == 0) {
-    // forward substitution, right-looking: lane = (block a, column j); once
-    // x_m is final it is eliminated from every later row at once
-    const int a = lane >> 4, j = lane & 15;
-    const float* Ab = sA + 16 * a * L::LA + 16 * a;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
-#pragma unroll
-    for (int m = 0; m < 15; ++m)
-#pragma unroll
-      for (int i = m + 1; i < 16; ++i) x[i] = fmaf(-Ab[i * L::LA + m], x[m], x[i]);
-    float* Xb = sX + 16 * a * L::LA + 16 * a;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Xb[i * L::LA + j] = x[i];
-  } else {
-    if (tid >= 64 && tid < 64 + DK) rDec[tid - 64] = sBlk[kBlkDec * DK + tid - 64];
-    for (int t = w - 1; t < NQT; t += kNW - 1) {
-      // Qbar tile (ct, rt): lane holds row 16rt + l16, columns 16ct + g4 .. +3
-      const int ct = t >> 2, rt = t & 3;
-      const int row = 16 * rt + l16, col = 16 * ct + g4;
-      const f32x4 f = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + col);
-      store4<Op>(rQ + tile_elem(tile_cr(ct, rt), lane),
-                 narrow4<Op>(*reinterpret_cast<const f32x4*>(sQP + row * L::LG + col) * (f * scale)));
-    }
-  }
+  __syncthreads();   // A and the diagonal blocks of X complete; QP, KE dead
   prefetch(std::integral_constant<int, kLoadG>{});
-  __syncthreads();   // QP, KM dead; diagonal blocks of X complete
 
   // ---- phase 2b: Kbar^T and V^T (range-scaled) into P1, then the
   // off-diagonal blocks of X, then Tm = X Diag(beta) where A was
