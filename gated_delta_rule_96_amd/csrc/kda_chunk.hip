@@ -912,9 +912,9 @@ constexpr int kOwners = 4;   // waves that own value columns, 16 each
 
 // The state pass of one head runs on NS work-groups (value-column blocks
 // of dv / NS = 64 columns), each staging the record's shared part (W, Qbar,
-// Khat, M, dec, uinv) and its own Ut columns.  LDS: NBUF such buffers (two
-// when they fit, so that the next chunk is staged while the current one is
-// computed) + abort word.
+// Khat, M, dec, uinv), its own Ut columns and (output gate) the chunk's og
+// rows of its columns.  LDS: NBUF such buffers (two when they fit, so that
+// the next chunk is staged while the current one is computed) + abort word.
 template <typename TIn, int DK, int DV>
 struct ConsumerLds {
   using R = Rec<TIn, DK, DV>;
@@ -923,12 +923,14 @@ struct ConsumerLds {
   static constexpr size_t SH = R::U_OFF_BYTES;
   static constexpr size_t UPART = (size_t)kC * (DV / NS) * sizeof(Op);
   static constexpr size_t USED = SH + UPART;
-  static constexpr size_t BUF = (USED + 255) / 256 * 256;
+  static constexpr size_t OG_OFF = USED;                              // og [kC][DV / NS] of TIn
+  static constexpr size_t OGB = (size_t)kC * (DV / NS) * sizeof(TIn);
+  static constexpr size_t BUF = (USED + OGB + 255) / 256 * 256;
   static constexpr int NBUF = 2 * BUF + 16 <= kLdsMax ? 2 : 1;
   static constexpr size_t BYTES = NBUF * BUF + 16;
   static_assert(NS * 16 * kOwners == DV, "dv must be 64 or 128");
   static_assert(BUF + 16 <= kLdsMax, "record does not fit in LDS");
-  static_assert(SH % 16 == 0 && UPART % 16 == 0, "16-byte staging");
+  static_assert(SH % 16 == 0 && UPART % 16 == 0 && OGB % 16 == 0, "16-byte staging");
 };
 
 // The state pass's fp16 domain: Sh = sigma S and Uh = sigma U with sigma a
@@ -1019,6 +1021,12 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   if (!owner) {
     const int htid = tid - 64 * kOwners;
     raw16 pre[PPT];
+    // output gate rows of the chunk (kLay with og): [kC][DV / NS] of TIn,
+    // OPT 16-byte pieces per thread, read once (non-temporal)
+    constexpr int ROWP = (DV / CL::NS) * (int)sizeof(TIn) / 16, OPT = (int)(CL::OGB / 16) / kHelpers;
+    static_assert(OPT * kHelpers * 16 == (int)CL::OGB, "og staging");
+    raw16 ogp[OPT];
+    const bool gate = kLay && lay.og != nullptr;   // uniform
     bool ok = true;
     // true once chunk c is published and may be read.  `seen` is chunk c's
     // ready word as read one chunk earlier (device scope: an L2 copy of the
@@ -1046,6 +1054,17 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         const int n = htid + kHelpers * i;
         if (n < NV16) pre[i] = rec[n < NSH16 ? n : n + uoff16];
       }
+      if (gate) {   // chunk c starts at token 64 c (the layer variant takes no packed sequences)
+        const TIn* og = reinterpret_cast<const TIn*>(lay.og);
+#pragma unroll
+        for (int i = 0; i < OPT; ++i) {
+          const int pc = htid + kHelpers * i, row = pc / ROWP, col = (pc % ROWP) * (16 / (int)sizeof(TIn));
+          const int tr = c * kC + row;
+          ogp[i] = tr < T_len ? __builtin_nontemporal_load(reinterpret_cast<const raw16*>(
+                                    og + (((size_t)b * T_len + tr) * H + h) * DV + vb * (DV / CL::NS) + col))
+                              : raw16{0.f, 0.f, 0.f, 0.f};
+        }
+      }
     };
     auto stage = [&](int c) {
       char* buf = buf_of(c);
@@ -1053,6 +1072,10 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       for (int i = 0; i < PPT; ++i) {
         const int n = htid + kHelpers * i;
         if (n < NV16) reinterpret_cast<raw16*>(buf)[n] = pre[i];
+      }
+      if (gate) {
+#pragma unroll
+        for (int i = 0; i < OPT; ++i) reinterpret_cast<raw16*>(buf + CL::OG_OFF)[htid + kHelpers * i] = ogp[i];
       }
       // every load of chunk c has returned its data before its slot is
       // handed back (after the next X)
@@ -1153,16 +1176,6 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       m0 = wave_max_dpp(m0);
       sig_e = 0;
     }
-    // output gate values of this owner's outputs, loaded early
-    f32x4 gz[4];
-    if (kLay && lay.og) {
-      const TIn* og = reinterpret_cast<const TIn*>(lay.og);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int row = t0 + 16 * rt + l16;
-        gz[rt] = row < T_len ? widen4(load4(og + (((size_t)b * T_len + row) * H + h) * DV + 16 * jt0 + g4)) : zero4();
-      }
-    }
 
     // The products run in the sigma domain (bf16 mode): Sh = sigma S and
     // Uh = sigma U are fp16 operands as they are (fp16 has the same
@@ -1261,11 +1274,14 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         m += nms;
         Ov[rt] = (scl ? accO[rt] + am * ir : am) * isig;
       }
-      if (kLay && lay.og) {   // output gate: o <- Sigmoid(og) o
+      if (kLay && lay.og) {   // output gate: o <- Sigmoid(og) o, og rows staged with the record
+        const TIn* sOg = reinterpret_cast<const TIn*>(buf + CL::OG_OFF);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt) {
+          const f32x4 gz = widen4(load4(sOg + (16 * rt + l16) * (DV / CL::NS) + 16 * jl0 + g4));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Ov[rt][i] *= sigmoid_fast(gz[rt][i]);
+          for (int i = 0; i < 4; ++i) Ov[rt][i] *= sigmoid_fast(gz[i]);
+        }
       }
       store_out(t0, pos.rows, Ov);
       float smax = 0.f;
