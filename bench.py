@@ -221,7 +221,8 @@ def extra_configs(args, torch, kda, synth, dev, stream, log, ms_c2):
     bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(BF)
 
     def timed(fn, n):
-        fn()
+        for _ in range(3):   # warm-up (the clock settles after a change of kernel)
+            fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(n):
@@ -452,6 +453,8 @@ def main():
     o2 = torch.empty_like(o)
 
     def time_stage(stages, n):
+        for _ in range(3):
+            kda.fwd_chunked(q, k, v, g, beta, h0, ht=None, final_state=False, workspace=ws2, out=o2, stages=stages)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(n):
@@ -460,7 +463,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    n_k = max(2, args.steps // 4)
+    n_k = max(4, args.steps // 2)
     ms_intra = time_stage(1, n_k)
     ms_state = time_stage(2, n_k)
     same = bool(torch.equal(o, o2))
@@ -502,7 +505,8 @@ def main():
         ht_a = torch.empty_like(ht)
 
         def time_unbounded(gg, n):
-            kda.fwd_chunked(q, k, v, gg, beta, h0, ht=ht_a, workspace=ws, out=o_a, unbounded=True)
+            for _ in range(3):
+                kda.fwd_chunked(q, k, v, gg, beta, h0, ht=ht_a, workspace=ws, out=o_a, unbounded=True)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(n):
@@ -568,7 +572,8 @@ def main():
             res["o"], res["ht"], res["snaps"] = kda.fwd_chunked_varlen(q, k, v, g, beta, cu, h0v, snap_every=every,
                                                                        workspace=ws, out=o_v)
 
-        run_varlen()
+        for _ in range(3):
+            run_varlen()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(n_k):
@@ -627,7 +632,8 @@ def main():
             return oo * torch.sigmoid(og.float())
 
         def timed(fn, n):
-            fn()
+            for _ in range(3):
+                fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(n):
