@@ -1525,6 +1525,37 @@ static int fused_heads_per_launch(int per_xcd, int ns) {
   return hx > 0 ? 8 * hx : 0;
 }
 
+// Heads per launch for nbh heads (at most cap per launch, wgs work-groups,
+// ns state-pass work-groups per head).  A launch of nh heads takes, per
+// chunk of its heads, about max(t_chain, nh t_item / (wgs - ns nh)): one
+// chunk of a head's state pass, or the producers' share of the records
+// (t_item: one record on one producer work-group).  The number of launches L
+// minimising L times that maximum gives the batch; measured t_item / t_chain
+// is about 5.7 (d_k = d_v = 128), so a launch of about 32 heads keeps both
+// sides busy, and 64 heads run as two launches of 32 rather than one with
+// half the work-groups holding state passes.
+static int fused_launch_batch(int nbh, int cap, int wgs, int ns) {
+  constexpr double kItemOverChain = 5.7;
+  int best = nbh < cap ? nbh : cap;
+  double best_cost = 1e300;
+  for (int L = (nbh + cap - 1) / cap; L <= nbh; ++L) {
+    int nh = (nbh + L - 1) / L;
+    if (nh > 8) nh = (nh + 7) / 8 * 8;   // whole rounds over the 8 XCDs
+    if (nh > cap) nh = cap;
+    const int launches = (nbh + nh - 1) / nh, prod = wgs - ns * nh;
+    if (prod > 0) {
+      const double per = nh * kItemOverChain / prod;
+      const double cost = launches * (per > 1.0 ? per : 1.0);
+      if (cost < best_cost * (1.0 - 1e-9)) {
+        best_cost = cost;
+        best = nh;
+      }
+    }
+    if (nh <= 8) break;
+  }
+  return best;
+}
+
 template <typename TIn, int DK, int DV>
 static size_t fused_ctrl_bytes(int nheads) {
   constexpr int NS = ConsumerLds<TIn, DK, DV>::NS;
@@ -1557,8 +1588,9 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   int per_xcd = cus / 8;
   if (per_xcd > kMaxWgPerXcd) per_xcd = kMaxWgPerXcd;
   constexpr int NS = ConsumerLds<TIn, DK, DV>::NS;
-  int batch = fused_heads_per_launch(per_xcd, NS);
-  if (batch <= 0) return hipErrorInvalidConfiguration;
+  const int cap = fused_heads_per_launch(per_xcd, NS);
+  if (cap <= 0) return hipErrorInvalidConfiguration;
+  int batch = fused_launch_batch(nbh, cap, 8 * per_xcd, NS);
   // what the workspace can hold
   while (batch > 0 && fused_ctrl_bytes<TIn, DK, DV>(batch) + (size_t)batch * kRingSlots * Rec<TIn, DK, DV>::BYTES > ws_bytes)
     --batch;
