@@ -1152,7 +1152,13 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   // run split into several calls at chunk boundaries does the same
   // arithmetic as one call.
   int sig_e = 0;
-  int seq = 0;   // sequence cursor (packed sequences)
+  // Packed sequences: the current sequence's stream chunks [c_beg, c_end)
+  // and tokens [t_beg, t_end) stay in registers; the sequence table is read
+  // when a sequence starts.  snap_left: chunks to the sequence's next
+  // snapshot.  (Reading the table, and dividing for the snapshot test, at
+  // every chunk cost the state pass 10%.)
+  int seq = -1, c_beg = 0, c_end = 0, t_beg = 0, t_end = 0;
+  int snap_left = snap.every;
   for (int c = 0; c < nchunks; ++c) {
     __syncthreads();   // X_c
     if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
@@ -1164,18 +1170,26 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     const float* sDec = reinterpret_cast<const float*>(buf + R::DEC_OFF_BYTES);
     const float uinv = *reinterpret_cast<const float*>(buf + R::UINV_OFF_BYTES);
     const Op* sU = reinterpret_cast<const Op*>(buf + CL::SH);   // local column tiles, 4 jl + st
-    const ChunkPos pos = chunk_pos(packed ? var : nullptr, c, T_len, seq);
-    const int t0 = pos.t0;
-    const bool seq_last = packed && t0 + pos.rows == var->cu[pos.seq + 1];   // uniform
-    const size_t seq_state = ((size_t)pos.seq * H + h) * DK * DV;           // packed: this sequence's state
-    if (packed && pos.j == 0) {   // a sequence starts: its own initial state, sigma from it
-      load_state(h0 ? h0 + seq_state : nullptr);
+    if (packed && c >= c_end) {   // a sequence starts: its range, its own initial state, sigma from it
+      do {
+        ++seq;
+        c_beg = var->cc[seq];
+        c_end = var->cc[seq + 1];
+      } while (c >= c_end);   // (past empty sequences)
+      t_beg = var->cu[seq];
+      t_end = var->cu[seq + 1];
+      snap_left = snap.every;
+      load_state(h0 ? h0 + ((size_t)seq * H + h) * DK * DV : nullptr);
       m0 = 0.f;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) m0 = fmaxf(m0, absmax4(S[ct]));
       m0 = wave_max_dpp(m0);
       sig_e = 0;
     }
+    const int j = packed ? c - c_beg : c;                        // chunk of the sequence
+    const int t0 = packed ? t_beg + j * kC : c * kC;
+    const int rows = min(kC, (packed ? t_end : T_len) - t0);
+    const bool seq_last = packed ? c + 1 == c_end : (c + 1) * kC >= T_len;   // uniform
 
     // The products run in the sigma domain (bf16 mode): Sh = sigma S and
     // Uh = sigma U are fp16 operands as they are (fp16 has the same
@@ -1283,7 +1297,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
           for (int i = 0; i < 4; ++i) Ov[rt][i] *= sigmoid_fast(gz[i]);
         }
       }
-      store_out(t0, pos.rows, Ov);
+      store_out(t0, rows, Ov);
       float smax = 0.f;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -1294,21 +1308,24 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     };
     if (__builtin_amdgcn_readfirstlane(re)) tail(std::true_type{});
     else tail(std::false_type{});
-    if (kSeg && snap.p && snap.every > 0 && (pos.j + 1) % snap.every == 0 &&
-        (packed ? !seq_last : (c + 1) * kC < T_len)) {
-      const int si = (packed ? var->sb[pos.seq] : 0) + (pos.j + 1) / snap.every - 1;
-      float* sp = snap.p + ((size_t)si * snap.nbh + bh) * DK * DV;
+    if (kSeg && snap.p && snap.every > 0 && --snap_left == 0) {
+      snap_left = snap.every;
+      if (!seq_last) {   // the state after chunk j of the sequence, (j + 1) a multiple of every
+        const int si = (packed ? var->sb[seq] : 0) + (j + 1) / snap.every - 1;
+        float* sp = snap.p + ((size_t)si * snap.nbh + bh) * DK * DV;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sp[(size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
+          for (int i = 0; i < 4; ++i) sp[(size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
+      }
     }
     if (packed && seq_last && ht) {   // the sequence's final state
       const float isig = ldexpf(1.f, -sig_e);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ht[seq_state + (size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
+        for (int i = 0; i < 4; ++i)
+          ht[((size_t)seq * H + h) * DK * DV + (size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
     }
     if (NBUF == 1) __syncthreads();   // Y_c
   }
@@ -1456,6 +1473,9 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
     const int nxt = it + P;
     const ChunkPos pc = chunk_pos(vp, c, T_len, seq_cur);
+    // the next item's position, once per item (its table reads wait for the
+    // LDS accesses in flight, so not inside the phases)
+    const ChunkPos pn = nxt < total ? chunk_pos(vp, nxt / nloc, T_len, seq_next) : pc;
     // The ring slot of chunk c is free once the head's consumers have read
     // chunk c - R.  Wave 0 reads their progress words from this XCD's L2
     // once the inputs are staged (after the input registers are consumed:
@@ -1488,7 +1508,6 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     auto prefetch = [&](auto parts) {
       if (nxt < total) {
         const int jn = xcd + 8 * (nxt % nloc), bn = head0 + jn;
-        const ChunkPos pn = chunk_pos(vp, nxt / nloc, T_len, seq_next);
         load_inputs<TIn, DK, DV, decltype(parts)::value>(in, q, k, v, g, beta, bn / H, bn % H, T_len, H, pn.t0,
                                                          pn.rows);
       }
