@@ -189,8 +189,18 @@ __device__ __forceinline__ raw16 l2norm_part(raw16 v) {
   float ss = 0.f;
 #pragma unroll
   for (int x = 0; x < VE; ++x) ss = fmaf(raw_elem<TIn>(v, x), raw_elem<TIn>(v, x), ss);
+  if constexpr (G <= 16) {
+    // within a row of 16 lanes by DPP moves (pairs, quads, half rows, rows:
+    // the same sums in the same order as an xor butterfly, without the LDS
+    // round trip of a lane shuffle)
+    if (G >= 2) ss += dpp_f<0xB1>(ss);    // quad_perm [1,0,3,2]
+    if (G >= 4) ss += dpp_f<0x4E>(ss);    // quad_perm [2,3,0,1]
+    if (G >= 8) ss += dpp_f<0x141>(ss);   // row_half_mirror
+    if (G >= 16) ss += dpp_f<0x140>(ss);  // row_mirror
+  } else {
 #pragma unroll
-  for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off);
+    for (int off = 1; off < G; off <<= 1) ss += __shfl_xor(ss, off);
+  }
   const float inv = 1.0f / sqrtf(ss + kNormEps);
   raw16 out;
   if constexpr (sizeof(TIn) == 4) {
