@@ -506,14 +506,21 @@ struct StateLds {
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_state_kernel(const float* __restrict__ rec, const float* __restrict__ dht,
                                                         float* __restrict__ dN, float* __restrict__ dU,
-                                                        float* __restrict__ dh0, int nch) {
+                                                        float* __restrict__ dh0, int nch, int nbh) {
   using LD = StateLds<DK, DV>;
   using RC = Rec<DK, DV>;
   constexpr int PK = LD::PK;
   constexpr int NS = DV / 16;
   __shared__ __align__(16) float sm[LD::WORDS];
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id();
-  const int bh = blockIdx.x / NS, js = blockIdx.x % NS, j0 = 16 * js;
+  // The NS work-groups of a head run on one XCD (work-group i runs on XCD
+  // i % 8): each reads the head's whole Kh and W^T every chunk, which then
+  // come from that XCD's L2 after one read from memory.  (With the groups
+  // of a head on consecutive work-groups, i.e. on all eight XCDs, every
+  // XCD fetched every head's records: about 17 GB per call at B1 H32 T64K.)
+  const int xg = blockIdx.x & 7, rest = blockIdx.x >> 3;
+  const int js = rest % NS, bh = xg + 8 * (rest / NS), j0 = 16 * js;
+  if (bh >= nbh) return;   // (the grid rounds the heads up to a multiple of 8)
   float* sKh = sm + LD::KH;
   float* sWT = sm + LD::WT;
   float* sNT = sm + LD::NT_;
@@ -1082,8 +1089,8 @@ hipError_t bwd_t(const void* q, const void* k, const void* v, const void* g, con
                      (const TIn*)beta, dO, scale, T, H, nch, rec);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_state_kernel<DK, DV>), dim3(nbh * (DV / 16)), dim3(256), 0, st, (const float*)rec, dht,
-                     dNb, dUb, dh0, nch);
+  hipLaunchKernelGGL((bwd_state_kernel<DK, DV>), dim3((nbh + 7) / 8 * 8 * (DV / 16)), dim3(256), 0, st,
+                     (const float*)rec, dht, dNb, dUb, dh0, nch, nbh);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_grad_kernel<TIn, DK, DV>), dim3(nrec), dim3(256), 0, st, qq, kk, (const TIn*)v,
