@@ -1542,7 +1542,7 @@ __global__ void clear_ints_kernel(int* p, int n) {   // also zero-fills fp32 buf
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
-constexpr int kRingSlots = 8;         // ring slots per head (fused schedule)
+constexpr int kRingSlots = 9;         // ring slots per head (fused schedule)
 static_assert(kRingSlots <= kFlagLine, "a head's ready words share one line");
 constexpr int kMaxWgPerXcd = 32;      // MI355X: 256 CUs in 8 XCDs
 
