@@ -220,8 +220,8 @@ def extra_configs(args, torch, kda, synth, dev, stream, log, ms_c2):
     BF = torch.bfloat16
     bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(BF)
 
-    def timed(fn, n):
-        for _ in range(3):   # warm-up (the clock settles after a change of kernel)
+    def timed(fn, n, warm=3):
+        for _ in range(warm):   # warm-up (the clock settles after a change of kernel)
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -244,7 +244,10 @@ def extra_configs(args, torch, kda, synth, dev, stream, log, ms_c2):
     ws = kda.alloc_workspace(Bc, Tc, Hc, DK, DV, BF, dev)
     o = torch.empty((Bc, Tc, Hc, DV), dtype=torch.float32, device=dev)
     ht = torch.empty((Bc, Hc, DK, DV), dtype=torch.float32, device=dev)
-    ms1 = timed(lambda: kda.fwd_chunked(q, k, v, g, beta, h0, ht=ht, workspace=ws, out=o), max(5, args.steps))
+    # a call takes about half a millisecond: 30 warm-up calls (15 ms) for the
+    # clock to settle, then at least 40 timed ones
+    ms1 = timed(lambda: kda.fwd_chunked(q, k, v, g, beta, h0, ht=ht, workspace=ws, out=o), max(40, 2 * args.steps),
+                warm=30)
     kda.check_workspace(ws)
     c1 = {"workload": f"KDA chunked prefill B={Bc} H={Hc} T={Tc} dk=dv={DK}, bf16 inputs, fp32 state and output",
           "ms_per_call": round(ms1, 4), "tokens_per_s": round(Bc * Tc / (ms1 * 1e-3), 1),
