@@ -887,14 +887,14 @@ __device__ __forceinline__ int load_flag_l2(const int* p) {
 // every lane of one whole wave: all lanes load the same word and the loop
 // condition goes through readfirstlane, so the loop is wave-uniform (no
 // lane-divergent loop inside code that also holds barriers).  Polls read
-// this XCD's L2; every 8th poll is a device-scope load (the writer may run
+// this XCD's L2; every 4th poll is a device-scope load (the writer may run
 // on another XCD), and every 64th checks the error word.  kSleep: pause between polls
 // (units of 64 cycles).  Returns -1 after kSpinLimit polls, or as soon as
 // another work-group reported an error; sets *err on a timeout.
 template <int kSleep = 2>
 __device__ __forceinline__ int spin_until_geq(const int* p, int target, int* err) {
   for (int it = 0; it < kSpinLimit; ++it) {
-    const bool dev = (it & 7) == 7;
+    const bool dev = (it & 3) == 3;
     const int v = __builtin_amdgcn_readfirstlane(dev ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                                      : load_flag_l2(p));
     if (v >= target) return v;
