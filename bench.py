@@ -21,6 +21,9 @@ Profiling helpers (for rocprofv3 runs; they print no JSON line):
   bench.py --probe fused|stages|copy [--calls N]
       a few calls of one prefill schedule on the benchmark workload, or a
       plain 1 GiB device copy that calibrates the memory counters;
+  bench.py --probe stamps [--calls N]
+      the fused prefill from the profiling build libkda_stamps.so: cycles
+      per item of each producer phase and per chunk of the state pass;
   bench.py --summarize RESULTS.db|kernel_stats.csv
       the kernel trace as a short table;
   bench.py --summarize-pmc KERNEL FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv COPY_BYTES
@@ -138,6 +141,88 @@ def probe(what: str, calls: int):
         kda.fwd_chunked(q, k, v, g, beta, h0, ht=ht, workspace=ws, out=o, stages=3 if stages else None)
     torch.cuda.synchronize()
     print(f"[probe] {what} x {calls} done", file=sys.stderr, flush=True)
+
+
+STAMP_NAMES = {
+    1: {0: "entry (item start, LDS free)", 1: "stage k/q/g/beta", 2: "block scans, exponentials",
+        3: "factors, K-hat to the record", 4: "Gram tiles, diagonal inverses, Q-bar",
+        5: "K-bar/V transposes, inverse d=1", 6: "inverse d=2", 7: "inverse d=3", 8: "Tm",
+        9: "W and U to the record", 10: "hand-off (publish)"},
+    2: {0: "loop top", 1: "barrier (record staged)", 2: "abort word", 3: "range scale, U accumulators",
+        4: "U and Q-bar products issued", 5: "K-hat/M/decay reads, U range", 6: "state update, output, stores",
+        7: "snapshots"},
+    3: {0: "loop top", 1: "barrier", 2: "abort word, progress store", 3: "wait for the next record",
+        4: "record loads issued", 5: "loads completed, LDS writes"},
+}
+
+
+def probe_stamps(calls: int):
+    """Cycle stamps of the fused prefill on the benchmark workload, from the
+    profiling build libkda_stamps.so: cycles per item for the producers
+    (phase work and the barrier that ends it) and per chunk for the state
+    pass's owner and staging waves, averaged over the launch's waves."""
+    import numpy as np
+    import torch
+
+    from gated_delta_rule_96_amd import kda, synth
+
+    kda.LIB_PATH = kda.STAMPS_LIB_PATH
+    dev = torch.device("cuda:0")
+    d = synth.make_inputs(B, T, H, DK, DV, seed=2)
+    bf = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
+    q, k, v, beta, z = (bf(d[n]) for n in ("q", "k", "v", "beta", "z"))
+    A = torch.from_numpy(d["A"].copy()).to(dev)
+    h0 = torch.from_numpy(d["h0"]).to(dev)
+    g, _ = kda.prepare_decay(z, A, want_gcum=False)
+    ws = kda.alloc_workspace(B, T, H, DK, DV, torch.bfloat16, dev)
+    o = torch.empty((B, T, H, DV), dtype=torch.float32, device=dev)
+    ht = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    for _ in range(10):
+        kda.fwd_chunked(q, k, v, g, beta, h0, ht=ht, workspace=ws, out=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        kda.fwd_chunked(q, k, v, g, beta, h0, ht=ht, workspace=ws, out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    kda.check_workspace(ws)
+    s = kda.stamps_read().astype(np.float64)   # [wg][wave][slot], the last call
+    role, cnt = s[:, :, kda.STAMP_ROLE], s[:, :, kda.STAMP_COUNT]
+    print(f"fused prefill B={B} H={H} T={T} dk={DK} dv={DV}, stamped build: {ms:.3f} ms per call "
+          f"(mean of {calls}); stamps of the last call")
+    longest = s[:, :, :kda.STAMP_ROLE].sum(-1).max()
+    print(f"longest wave: {longest:.0f} cycles = {longest / (ms * 1e6):.2f} GHz over the call's duration")
+    for r, what in ((1, "producer, cycles per item"), (2, "state-pass owner waves, cycles per chunk"),
+                    (3, "state-pass staging waves, cycles per chunk")):
+        sel = (role == r) & (cnt > 0)
+        if not sel.any():
+            continue
+        per = s[sel] / cnt[sel][:, None]            # [waves, slots]
+        nwg = int(((role == r).any(1)).sum())
+        print(f"\n{what}: {int(sel.sum())} waves in {nwg} work-groups, "
+              f"{cnt[sel].mean():.1f} {'items' if r == 1 else 'chunks'} per wave")
+        if r == 1:
+            # per-wave-index means (waves 0-3 and 4-7 take different tiles)
+            wi = np.nonzero(sel)[1]
+            byw = np.stack([per[wi == w].mean(0) for w in range(kda.STAMP_WAVES)])
+            print(f"  {'phase':<36} {'total':>7} {'work':>7} {'barrier':>8}   work by wave 0..7")
+            tot = 0.0
+            for sl, name in STAMP_NAMES[1].items():
+                work = per[:, sl].mean()
+                bar = per[:, 16 + sl].mean() if 1 <= sl <= 8 else 0.0
+                tot += work + bar
+                ww = " ".join(f"{x:6.0f}" for x in byw[:, sl]) if 1 <= sl <= 8 else ""
+                print(f"  {name:<36} {work + bar:7.0f} {work:7.0f} {bar:8.0f}   {ww}")
+            print(f"  {'total':<36} {tot:7.0f}")
+        else:
+            tot = 0.0
+            for sl, name in STAMP_NAMES[r].items():
+                x = per[:, sl].mean()
+                tot += x
+                print(f"  {name:<36} {x:7.0f}")
+            print(f"  {'total':<36} {tot:7.0f}")
 
 
 def summarize_trace(path: str):
@@ -387,7 +472,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="skip the B=4 H=16 T=8192 and million-token prefill lines")
-    ap.add_argument("--probe", choices=("fused", "stages", "copy"))
+    ap.add_argument("--probe", choices=("fused", "stages", "copy", "stamps"))
     ap.add_argument("--calls", type=int, default=3)
     ap.add_argument("--summarize")
     ap.add_argument("--summarize-pmc", nargs=6)
@@ -397,6 +482,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.probe == "stamps":
+        probe_stamps(args.calls)
         return
     if args.probe:
         probe(args.probe, args.calls)

@@ -65,6 +65,48 @@ constexpr int kC = 64;   // chunk rows
 constexpr int kNW = 8;                // waves per work-group (every kernel here)
 constexpr int kThreads = 64 * kNW;
 
+// Cycle stamps, compiled in only with KDA_CYCLE_STAMPS (a profiling build of
+// the library; the product build has empty marks and identical code).  Each
+// wave of the fused kernel adds up the shader-clock cycles (s_memtime)
+// between consecutive marks into the slot named by the later mark and, when
+// it leaves, lane 0 writes its sums to g_stamps[(block * kNW + wave) * 32 +
+// slot].  Slot kStampRole says which loop the wave ran (1 producer, 2 state
+// pass owner, 3 state pass staging), slot kStampCount how many items or
+// chunks it handled.  Reading the clock waits for the wave's outstanding
+// LDS and scalar accesses, so stamped runs are a few percent slower.
+constexpr int kStampSlots = 32, kStampRole = 29, kStampCount = 30;
+constexpr int kStampMaxWgs = 256;   // the fused grid (one work-group per CU)
+#ifdef KDA_CYCLE_STAMPS
+__device__ unsigned long long g_stamps[kStampMaxWgs * kNW * kStampSlots];
+struct Stamps {
+  unsigned long long acc[kStampSlots];
+  unsigned long long last;
+  __device__ Stamps() : last(__builtin_amdgcn_s_memtime()) {
+#pragma unroll
+    for (int i = 0; i < kStampSlots; ++i) acc[i] = 0;
+  }
+  template <int i> __device__ __forceinline__ void mark() {
+    const unsigned long long now = __builtin_amdgcn_s_memtime();
+    acc[i] += now - last;
+    last = now;
+  }
+  template <int i> __device__ __forceinline__ void add(unsigned long long n) { acc[i] += n; }
+  __device__ __forceinline__ void flush() {
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < kStampMaxWgs) {
+#pragma unroll
+      for (int i = 0; i < kStampSlots; ++i) g_stamps[((size_t)blockIdx.x * kNW + w) * kStampSlots + i] = acc[i];
+    }
+  }
+};
+#else
+struct Stamps {
+  template <int i> __device__ __forceinline__ void mark() {}
+  template <int i> __device__ __forceinline__ void add(unsigned long long) {}
+  __device__ __forceinline__ void flush() {}
+};
+#endif
+
 template <typename TIn> struct Policy;
 template <> struct Policy<float> {
   using Op = float;
@@ -388,7 +430,7 @@ constexpr int kSlotPeek = 0, kSlotCheck = 1, kSlotOk = 2;
 template <typename TIn, int DK, int DV, bool kUnb, bool kLay, typename Slot, typename Prefetch>
 __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& in, const float* __restrict__ gcum,
                                               float scale, int b, int h, int T_len, int H, int t0, int Lrows,
-                                              char* __restrict__ rec, Slot slot, Prefetch prefetch,
+                                              char* __restrict__ rec, Slot slot, Prefetch prefetch, Stamps& stp,
                                               Layer lay = Layer{nullptr, nullptr, 0}) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
@@ -421,6 +463,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   const size_t tokk = (size_t)H * DK;
   const size_t base_k = ((size_t)b * T_len + t0) * tokk + (size_t)h * DK;
   __syncthreads();   // a previous call's LDS readers are done
+  stp.mark<0>();   // producer slots: 0 entry, 1-8 phase work, 17-24 their barriers, 9 phase 3, 10 publish
   Op* rW = reinterpret_cast<Op*>(rec) + R::W;
   Op* rQ = reinterpret_cast<Op*>(rec) + R::Q;
   Op* rK = reinterpret_cast<Op*>(rec) + R::K;
@@ -453,7 +496,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     }
   }
   if (tid < kC) sBeta[tid] = to_f32(in.beta);
+  stp.mark<1>();
   __syncthreads();
+  stp.mark<17>();
   slot(std::integral_constant<int, kSlotPeek>{});
 
   // Block scans: thread (block a, channel c) forms G for its 16 rows (local
@@ -487,7 +532,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     }
   }
   slot(std::integral_constant<int, kSlotCheck>{});
+  stp.mark<2>();
   __syncthreads();   // staged g read (kUnb: G written); block totals written
+  stp.mark<18>();
   if (!slot(std::integral_constant<int, kSlotOk>{})) return false;
   if (kUnb) {
     // Diagonal tiles by position pairs, fp32: entry (i, j), j <= i, of tile
@@ -568,7 +615,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       for (int j = 0; j < 4; ++j) sBlk[(kBlkM + j) * DK + c] = exp2_split(-(double)sTot[j * DK + c] * l2e);
     }
   }
+  stp.mark<3>();
   __syncthreads();
+  stp.mark<19>();
   prefetch(std::integral_constant<int, kLoadK | kLoadBeta>{});
 
   // ---- phase 1: Gram tiles (A -> LDS, scale M -> record)
@@ -707,7 +756,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   vmax = wave_max_dpp(vmax);
   if (lane == 0) sRed[w] = vmax;
   prefetch(std::integral_constant<int, kLoadQ>{});
+  stp.mark<4>();
   __syncthreads();   // A and the diagonal blocks of X complete; QP, KE dead
+  stp.mark<20>();
   prefetch(std::integral_constant<int, kLoadG>{});
 
   // ---- phase 2b: Kbar^T and V^T (range-scaled) into P1, then the
@@ -756,7 +807,13 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
 #pragma unroll
       for (int i = 0; i < 4; ++i) sX[(16 * a + g4 + i) * L::LA + 16 * bb + l16] = -xr[i];
     }
+    if (d == 1) stp.mark<5>();
+    else if (d == 2) stp.mark<6>();
+    else stp.mark<7>();
     __syncthreads();
+    if (d == 1) stp.mark<21>();
+    else if (d == 2) stp.mark<22>();
+    else stp.mark<23>();
   }
   static_assert(kC * kC == 8 * kThreads, "Tm: 8 entries per thread");
   {   // A is dead: Tm takes its place (8 consecutive entries of a row per thread)
@@ -772,7 +829,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     store4<Op>(sTm + r * L::LB + s0, narrow4<Op>(x[0]));
     store4<Op>(sTm + r * L::LB + s0 + 4, narrow4<Op>(x[1]));
   }
+  stp.mark<8>();
   __syncthreads();   // Tm, Kbar^T, V^T complete
+  stp.mark<24>();
 
   // ---- phase 3: W = Tm Kbar (as W^T tiles) and Ut = Tm V into the record
 #pragma unroll
@@ -803,6 +862,7 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
     store4<Op>(rU + tile_elem(jt * 4 + st, lane), narrow4<Op>(ut[j] * su));
   }
   if (tid == 0) *rUinv = suinv;
+  stp.mark<9>();
   return true;
 }
 
@@ -820,9 +880,10 @@ __global__ __launch_bounds__(kThreads) void intra_chunk_kernel(const TIn* __rest
   InRegs<TIn, DK, DV> in;
   const int t0 = ch * kC, rows = min(kC, T_len - t0);
   load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, t0, rows);
+  Stamps stp;
   produce_chunk<TIn, DK, DV, kUnb, false>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, t0, rows,
                                    ws + ((size_t)bh * nchunks + ch) * Rec<TIn, DK, DV>::BYTES, [](auto) { return true; },
-                                   [](auto) {});
+                                   [](auto) {}, stp);
 }
 
 // ---------------------------------------------------------------------------
@@ -986,8 +1047,8 @@ template <typename TIn, int DK, int DV, bool kRing, bool kLay, bool kSeg>
 __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
                                               const float* __restrict__ h0, float* __restrict__ ht,
                                               float* __restrict__ o, int b, int h, int T_len, int H,
-                                              int nchunks, Snap snap, Layer lay = Layer{nullptr, nullptr, 0},
-                                              const VarSeg* var = nullptr) {
+                                              int nchunks, Snap snap, Stamps& stp,
+                                              Layer lay = Layer{nullptr, nullptr, 0}, const VarSeg* var = nullptr) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
   using R = Rec<TIn, DK, DV>;
@@ -1099,22 +1160,32 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     } else if (lane == 0) {
       *sAbort = 1;
     }
+    // staging slots: 0 loop top, 1 barrier X, 2 abort word, progress
+    // store and peek, 3 ready wait, 4 load issue, 5 stage (loads' wait, LDS writes)
+    stp.add<kStampRole>(3);
     for (int c = 0; c < nchunks; ++c) {
+      stp.mark<0>();
       __syncthreads();   // X_c
+      stp.mark<1>();
       if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
       // chunk c has been read completely: hand its slot back
       if (kRing && htid == 0) __hip_atomic_store(ring.done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int seen = __builtin_amdgcn_readfirstlane(seen_next);
       seen_next = peek(c + 2);
+      stp.mark<2>();
       if (c + 1 < nchunks) {
         ok = ready_wait(c + 1, seen);
+        stp.mark<3>();
         if (ok) load(c + 1);
         else if (lane == 0) *sAbort = 1;
+        stp.mark<4>();
         if (NBUF == 1) __syncthreads();   // Y_c
         if (ok) stage(c + 1);
+        stp.mark<5>();
       } else if (NBUF == 1) {
         __syncthreads();   // Y_c
       }
+      stp.add<kStampCount>(1);
     }
     return;
   }
@@ -1169,9 +1240,16 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   // every chunk cost the state pass 10%.)
   int seq = -1, c_beg = 0, c_end = 0, t_beg = 0, t_end = 0;
   int snap_left = snap.every;
+  // owner slots: 0 loop top, 1 barrier X, 2 abort word, 3 sigma, Sh and
+  // the U accumulators, 4 U and Qbar products issued, 5 Khat/M/decay reads
+  // and the U range, 6 state update, output and stores, 7 snapshots
+  stp.add<kStampRole>(2);
   for (int c = 0; c < nchunks; ++c) {
+    stp.mark<0>();
     __syncthreads();   // X_c
+    stp.mark<1>();
     if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
+    stp.mark<2>();
     const char* buf = buf_of(c);
     const Op* sW = reinterpret_cast<const Op*>(buf) + R::W;
     const Op* sQ = reinterpret_cast<const Op*>(buf) + R::Q;
@@ -1229,6 +1307,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       Uh[st] = widen4(load4(sU + tile_elem(jl0 * 4 + st, lane))) * cu;
       accO[st] = zero4();
     }
+    stp.mark<3>();
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       Slab<Op> Wa[DK / 32], Qa[DK / 32];
@@ -1244,6 +1323,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         accO[st] = mma(sb, Qa[sl], accO[st]);
       }
     }
+    stp.mark<4>();
     // Khat, M and e^{Gamma_C} for the rest of the chunk, read while the
     // products above run (the owner has the registers to spare)
     Slab<Op> Ka[NCT][2], Ma[6];
@@ -1270,6 +1350,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       if (!(umax <= kFp16Safe)) re = fp16_domain_exp(umax);
     }
     const float r = ldexpf(1.f, re), ir = ldexpf(1.f, -re);
+    stp.mark<5>();
     // The rest of the chunk, one straight-line block per case (so that the
     // output work and stores can be scheduled into the gaps of the state
     // update's products).  Sh <- e^{Gamma_C} Sh + Khat^T Uh: MFMAs
@@ -1318,6 +1399,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     };
     if (__builtin_amdgcn_readfirstlane(re)) tail(std::true_type{});
     else tail(std::false_type{});
+    stp.mark<6>();
     if (kSeg && snap.p && snap.every > 0 && --snap_left == 0) {
       snap_left = snap.every;
       if (!seq_last) {   // the state after chunk j of the sequence, (j + 1) a multiple of every
@@ -1337,6 +1419,8 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
         for (int i = 0; i < 4; ++i)
           ht[((size_t)seq * H + h) * DK * DV + (size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
     }
+    stp.mark<7>();
+    stp.add<kStampCount>(1);
     if (NBUF == 1) __syncthreads();   // Y_c
   }
 
@@ -1358,9 +1442,10 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
   using CL = ConsumerLds<TIn, DK, DV>;
   __shared__ __align__(16) char smem[CL::BYTES];
   const int bh = blockIdx.x / CL::NS, vb = blockIdx.x % CL::NS;
+  Stamps stp;
   consume_chain<TIn, DK, DV, false, false, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
                                            Ring{nullptr, nullptr, nullptr, nullptr, 1}, vb, h0, ht, o, bh / H,
-                                           bh % H, T_len, H, nchunks, snap);
+                                           bh % H, T_len, H, nchunks, snap, stp);
 }
 
 // ---------------------------------------------------------------------------
@@ -1426,6 +1511,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   int* ready = ctrl + kFlagBase;
   int* done = ready + nheads * kFlagLine;
   int* cxcc = done + nheads * NS * kFlagLine;
+  Stamps stp;
 
   if (li < nloc * NS) {   // consumer vb of head jh
     const int jh = xcd + 8 * (li / NS), vb = li % NS, bh = head0 + jh;
@@ -1433,7 +1519,8 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
                                            Ring{ready + jh * kFlagLine, done + (jh * NS + vb) * kFlagLine, err,
                                                 cxcc + jh * NS + vb, R},
                                            vb,
-                                           h0, ht, o, bh / H, bh % H, T_len, H, nchunks, snap, lay, vp);
+                                           h0, ht, o, bh / H, bh % H, T_len, H, nchunks, snap, stp, lay, vp);
+    stp.flush();
     return;
   }
 
@@ -1448,7 +1535,11 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   const int my_xcc = xcc_id();
   InRegs<TIn, DK, DV> in;
   int it = li - nloc * NS;
-  if (it >= total) return;
+  stp.add<kStampRole>(1);
+  if (it >= total) {
+    stp.flush();
+    return;
+  }
   int seq_cur = 0, seq_next = 0;   // sequence cursors of this item and of the next one
   {
     const int jh = xcd + 8 * (it % nloc), bh = head0 + jh;
@@ -1523,14 +1614,21 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
       }
     };
     if (!produce_chunk<TIn, DK, DV, kUnb, kLay>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, pc.t0, pc.rows,
-                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, slot, prefetch, lay))
+                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, slot, prefetch, stp, lay)) {
+      stp.flush();
       return;
+    }
     // Published as soon as its stores are in the L2.  (Deferring this until
     // the next item's inputs were staged let the stores drain in the
     // background but made every record visible some 4-5k cycles later; the
     // consumers then waited for records and the producers for ring slots.)
     publish(it);
-    if (nxt >= total) return;
+    stp.mark<10>();
+    stp.add<kStampCount>(1);
+    if (nxt >= total) {
+      stp.flush();
+      return;
+    }
     it = nxt;
   }
 }
@@ -1760,3 +1858,18 @@ hipError_t launch_clear_status(void* ws, hipStream_t st) {
 }
 
 }  // namespace kda
+
+#ifdef KDA_CYCLE_STAMPS
+#include "kda_stamps.h"
+extern "C" int kda_stamps_read(unsigned long long* host, size_t count) {
+  static_assert(KDA_STAMP_WGS == kda::kStampMaxWgs && KDA_STAMP_SLOTS == kda::kStampSlots &&
+                    KDA_STAMP_ROLE == kda::kStampRole && KDA_STAMP_COUNT == kda::kStampCount,
+                "stamp layout");
+  constexpr size_t kTotal = (size_t)kda::kStampMaxWgs * kda::kNW * kda::kStampSlots;
+  if (host == nullptr) return KDA_ERR_NULL;
+  if (count != kTotal) return KDA_ERR_SHAPE;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(kda::g_stamps), kTotal * sizeof(unsigned long long)) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_HIP;
+}
+#endif

@@ -16,6 +16,10 @@ import torch
 
 PKG = Path(__file__).resolve().parent
 LIB_PATH = PKG / "libkda.so"
+# profiling build with the fused prefill's cycle stamps (include/kda_stamps.h);
+# set LIB_PATH to it before the first call to use it
+STAMPS_LIB_PATH = PKG / "libkda_stamps.so"
+STAMP_WGS, STAMP_WAVES, STAMP_SLOTS, STAMP_ROLE, STAMP_COUNT = 256, 8, 32, 29, 30
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_ERR_UNSUPPORTED, KDA_ERR_RANGE, KDA_ERR_INCOMPLETE = 5, 7, 9
@@ -78,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_status.argtypes = [P, P]
         L.kda_fwd_status_word.restype = P
         L.kda_fwd_status_word.argtypes = [P]
+        if hasattr(L, "kda_stamps_read"):
+            L.kda_stamps_read.restype = I
+            L.kda_stamps_read.argtypes = [P, S]
         _lib = L
     return _lib
 
@@ -392,3 +399,19 @@ def decode_step_layer(q, k, v, z, A, beta, state, *, og=None, qk_l2norm=False, s
                                        float(scale), _ptr(state), _ptr(o), flags, dt, B, H, dk, dv,
                                        _stream(q.device)), "kda_decode_step_layer")
     return o
+
+
+def stamps_read():
+    """kda_stamps_read: the fused prefill's cycle stamps of the last launch,
+    numpy uint64 [STAMP_WGS, STAMP_WAVES, STAMP_SLOTS] (layout in
+    include/kda_stamps.h).  Only the profiling build libkda_stamps.so has
+    them."""
+    import numpy as np
+
+    L = lib()
+    if not hasattr(L, "kda_stamps_read"):
+        raise RuntimeError(f"{LIB_PATH.name} has no cycle stamps: set kda.LIB_PATH = kda.STAMPS_LIB_PATH "
+                           "before the first call")
+    buf = np.zeros((STAMP_WGS, STAMP_WAVES, STAMP_SLOTS), dtype=np.uint64)
+    _check(L.kda_stamps_read(buf.ctypes.data, buf.size), "kda_stamps_read")
+    return buf

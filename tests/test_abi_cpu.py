@@ -32,6 +32,24 @@ def test_library_exports_every_declared_symbol():
         assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
 
 
+def test_profiling_build_exports_the_same_calls_and_the_stamps():
+    # libkda_stamps.so: the same sources with the fused prefill's cycle
+    # stamps (include/kda_stamps.h); the product library has no stamps
+    L = ctypes.CDLL(str(kda.STAMPS_LIB_PATH))
+    text = re.sub(r"/\*.*?\*/", "", (ROOT / "include" / "kda_stamps.h").read_text(), flags=re.S)
+    stamps = sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+    assert stamps == ["kda_stamps_read"]
+    for n in declared_functions() + stamps:
+        assert hasattr(L, n), n
+    assert not hasattr(kda.lib(), "kda_stamps_read")
+    L.kda_stamps_read.restype = ctypes.c_int
+    L.kda_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    n = kda.STAMP_WGS * kda.STAMP_WAVES * kda.STAMP_SLOTS
+    assert L.kda_stamps_read(None, n) == 1                     # KDA_ERR_NULL
+    buf = (ctypes.c_uint64 * n)()
+    assert L.kda_stamps_read(ctypes.addressof(buf), n - 1) == 2   # KDA_ERR_SHAPE
+
+
 def test_version_and_status_strings():
     assert kda.abi_version() == 1
     for s in range(9):
