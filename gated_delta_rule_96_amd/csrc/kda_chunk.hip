@@ -151,6 +151,20 @@ template <int NCT> __host__ __device__ constexpr int tile_k(int st, int ct) {
 // with one 16-byte load.
 __host__ __device__ constexpr int tile_elem(int t, int lane) { return (t >> 1) * 512 + lane * 8 + (t & 1) * 4; }
 
+// A lane's values of record tiles 2j (lo) and 2j + 1 (hi) at p = the even
+// tile's tile_elem: one 16-byte store for 2-byte elements (half-filled
+// 8-byte stores cost the record writes twice the requests), two for fp32.
+template <typename T> __device__ __forceinline__ void store_pair(T* p, f32x4 lo, f32x4 hi) {
+  if constexpr (sizeof(T) == 2) {
+    const V4<T> a = narrow4<T>(lo), b = narrow4<T>(hi);
+    typedef T T8 __attribute__((ext_vector_type(8)));
+    *reinterpret_cast<T8*>(p) = T8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  } else {
+    store4<T>(p, narrow4<T>(lo));
+    store4<T>(p + 4, narrow4<T>(hi));
+  }
+}
+
 typedef float raw16 __attribute__((ext_vector_type(4)));   // 16 raw bytes
 
 // Element x of 16 raw bytes holding values of type T, as fp32.
@@ -638,35 +652,71 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       const float* d0p = sBlk + (diag ? kBlkM + a : kBlkD + t0i - 4) * DK;
       const float* d1p = sBlk + (kBlkD + (ntile > 1 ? t1i - 4 : 0)) * DK;
       f32x4 accA0 = zero4(), accM0 = zero4(), accA1 = zero4(), accM1 = zero4();
-#pragma unroll
-      for (int sl = 0; sl < DK / 32; ++sl) {
-        const int c0 = 32 * sl + g4, c1 = c0 + 16;
+      // One straight-line slab loop per kind of wave (kind 0: the diagonal
+      // tile with split operands for M, 1: one tile, 2: two tiles of the
+      // same row block), chosen once, with the next slab's operands read
+      // from LDS while the current slab's are converted and multiplied
+      // (with the kind tested inside the loop every slab's reads waited for
+      // the previous slab's products).
+      auto tiles = [&](auto kind) {
+        // the products KE x factor are rounded before they are split (no
+        // contraction into the split's subtraction), the same arithmetic in
+        // every instantiation
+#pragma clang fp contract(off)
+        constexpr int K = decltype(kind)::value, NR = K == 2 ? 12 : 8, NSL = DK / 32;
         auto ld = [&](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
-        const Slab<Gm> RK = make_slab<Gm>(ld(sKP + r * L::LG + c0), ld(sKP + r * L::LG + c1));
-        const f32x4 rq0 = ld(sQP + r * L::LG + c0), rq1 = ld(sQP + r * L::LG + c1);
-        // column operand: KE times e^{-T_a} (diagonal) or e^{Gamma_p(a) - Gamma_p(b+1)}
-        const f32x4 ck0 = ld(sKE + s0 * L::LG + c0) * ld(d0p + c0), ck1 = ld(sKE + s0 * L::LG + c1) * ld(d0p + c1);
-        if (P::kMixed && diag) {
-          Slab<Gm> CKh, CKl, RQh, RQl;
-          make_slab_split<Gm>(ck0, ck1, CKh, CKl);
-          make_slab_split<Gm>(rq0, rq1, RQh, RQl);
-          accA0 = mma(CKh, RK, accA0);
-          accM0 = mma(CKh, RQh, accM0);
-          accM0 = mma(CKl, RQh, accM0);
-          accM0 = mma(CKh, RQl, accM0);
-        } else {
-          const Slab<Gm> RQ = make_slab<Gm>(rq0, rq1);
-          const Slab<Gm> CK = make_slab<Gm>(ck0, ck1);
-          accA0 = mma(CK, RK, accA0);   // A^T tile: lane holds A[r][16bb + g4 + i]
-          accM0 = mma(CK, RQ, accM0);   // M^T tile: lane holds M[r][16bb + g4 + i]
-          if (ntile > 1) {
-            const Slab<Gm> CK1 = make_slab<Gm>(ld(sKE + s1 * L::LG + c0) * ld(d1p + c0),
-                                               ld(sKE + s1 * L::LG + c1) * ld(d1p + c1));
-            accA1 = mma(CK1, RK, accA1);
-            accM1 = mma(CK1, RQ, accM1);
+        // a slab's operands: KP and QP of row r, KE of rows s0 (and s1) with
+        // their per-channel factors, each as the halves c0 and c1 = c0 + 16
+        auto load = [&](int sl, f32x4 (&x)[NR]) {
+          const int c0 = 32 * sl + g4, c1 = c0 + 16;
+          x[0] = ld(sKP + r * L::LG + c0);
+          x[1] = ld(sKP + r * L::LG + c1);
+          x[2] = ld(sQP + r * L::LG + c0);
+          x[3] = ld(sQP + r * L::LG + c1);
+          x[4] = ld(sKE + s0 * L::LG + c0);
+          x[5] = ld(sKE + s0 * L::LG + c1);
+          x[6] = ld(d0p + c0);
+          x[7] = ld(d0p + c1);
+          if constexpr (K == 2) {
+            x[8] = ld(sKE + s1 * L::LG + c0);
+            x[9] = ld(sKE + s1 * L::LG + c1);
+            x[10] = ld(d1p + c0);
+            x[11] = ld(d1p + c1);
+          }
+        };
+        f32x4 xb[2][NR];
+        load(0, xb[0]);
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+          if (sl + 1 < NSL) load(sl + 1, xb[(sl + 1) & 1]);
+          const f32x4(&x)[NR] = xb[sl & 1];
+          const Slab<Gm> RK = make_slab<Gm>(x[0], x[1]);
+          // column operand: KE times e^{-T_a} (diagonal) or e^{Gamma_p(a) - Gamma_p(b+1)}
+          const f32x4 ck0 = x[4] * x[6], ck1 = x[5] * x[7];
+          if constexpr (K == 0) {
+            Slab<Gm> CKh, CKl, RQh, RQl;
+            make_slab_split<Gm>(ck0, ck1, CKh, CKl);
+            make_slab_split<Gm>(x[2], x[3], RQh, RQl);
+            accA0 = mma(CKh, RK, accA0);
+            accM0 = mma(CKh, RQh, accM0);
+            accM0 = mma(CKl, RQh, accM0);
+            accM0 = mma(CKh, RQl, accM0);
+          } else {
+            const Slab<Gm> RQ = make_slab<Gm>(x[2], x[3]);
+            const Slab<Gm> CK = make_slab<Gm>(ck0, ck1);
+            accA0 = mma(CK, RK, accA0);   // A^T tile: lane holds A[r][16bb + g4 + i]
+            accM0 = mma(CK, RQ, accM0);   // M^T tile: lane holds M[r][16bb + g4 + i]
+            if constexpr (K == 2) {
+              const Slab<Gm> CK1 = make_slab<Gm>(x[8] * x[10], x[9] * x[11]);
+              accA1 = mma(CK1, RK, accA1);
+              accM1 = mma(CK1, RQ, accM1);
+            }
           }
         }
-      }
+      };
+      if (P::kMixed && diag) tiles(std::integral_constant<int, 0>{});
+      else if (ntile > 1) tiles(std::integral_constant<int, 2>{});
+      else tiles(std::integral_constant<int, 1>{});
       const float br = sBeta[r];
       for (int ti = 0; ti < ntile; ++ti) {
         const int bb = ti ? bb1 : bb0;
@@ -720,30 +770,37 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
       for (int i = 0; i < 16; ++i) Xb[i * L::LA + j] = x[i];
     }
   } else {
-    // Qbar tiles (ct, rt) and e^{Gamma_C} to the record: waves 4 and 5
-    // (two Gram tiles each) take NQT / 8 tiles, waves 6 and 7 (one) 3 NQT / 8,
-    // in groups of up to four whose operands are read before their stores.
-    auto qbar = [&](auto cnt, int t0q) {
-      constexpr int N = decltype(cnt)::value, NG = N % 4 == 0 ? 4 : (N % 3 == 0 ? 3 : N);
+    // Qbar tiles and e^{Gamma_C} to the record, by tile pairs (ct = 2c2,
+    // 2c2 + 1; rt) that one 16-byte store per lane writes: waves 4 and 5
+    // (two Gram tiles each) take NQT / 16 pairs, waves 6 and 7 (one)
+    // 3 NQT / 16, in groups of up to two pairs whose operands are read
+    // before their stores.
+    auto qbar = [&](auto cnt, int m0) {
+      constexpr int N = decltype(cnt)::value, NG = N % 2 == 0 ? 2 : N;
       static_assert(N % NG == 0, "groups");
 #pragma unroll
       for (int g0 = 0; g0 < N; g0 += NG) {
-        f32x4 qv[NG], fv[NG];
+        f32x4 qv[NG][2], fv[NG][2];
 #pragma unroll
         for (int n = 0; n < NG; ++n) {
-          const int tq = t0q + g0 + n, ct = tq >> 2, rt = tq & 3;
-          fv[n] = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + 16 * ct + g4);
-          qv[n] = *reinterpret_cast<const f32x4*>(sQP + (16 * rt + l16) * L::LG + 16 * ct + g4);
+          const int m = m0 + g0 + n, c2 = m >> 2, rt = m & 3;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int ct = 2 * c2 + e;
+            fv[n][e] = *reinterpret_cast<const f32x4*>(sBlk + (kBlkF + rt) * DK + 16 * ct + g4);
+            qv[n][e] = *reinterpret_cast<const f32x4*>(sQP + (16 * rt + l16) * L::LG + 16 * ct + g4);
+          }
         }
 #pragma unroll
         for (int n = 0; n < NG; ++n) {
-          const int tq = t0q + g0 + n, ct = tq >> 2, rt = tq & 3;
-          store4<Op>(rQ + tile_elem(tile_cr(ct, rt), lane), narrow4<Op>(qv[n] * (fv[n] * scale)));
+          const int m = m0 + g0 + n, c2 = m >> 2, rt = m & 3;
+          store_pair<Op>(rQ + tile_elem(tile_cr(2 * c2, rt), lane), qv[n][0] * (fv[n][0] * scale),
+                         qv[n][1] * (fv[n][1] * scale));
         }
       }
     };
-    if (w < 6) qbar(std::integral_constant<int, NQT / 8>{}, (w - 4) * (NQT / 8));
-    else qbar(std::integral_constant<int, 3 * NQT / 8>{}, NQT / 4 + (w - 6) * (3 * NQT / 8));
+    if (w < 6) qbar(std::integral_constant<int, NQT / 16>{}, (w - 4) * (NQT / 16));
+    else qbar(std::integral_constant<int, 3 * NQT / 16>{}, NQT / 8 + (w - 6) * (3 * NQT / 16));
     if (tid >= 6 * 64 && tid < 6 * 64 + DK) rDec[tid - 6 * 64] = sBlk[kBlkDec * DK + tid - 6 * 64];
   }
   // V's range (for its fp16 staging): wave maxima of the chunk's v, combined
@@ -834,12 +891,33 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   stp.mark<24>();
 
   // ---- phase 3: W = Tm Kbar (as W^T tiles) and Ut = Tm V into the record
+  // (the record holds -W)
+  if constexpr (NQW == 4) {
+    // tile pairs (ct = 2cp, 2cp + 1; rt), one 16-byte store per lane each:
+    // wave w takes column pair w / 2 and row tiles {0, 3} (even w) or
+    // {1, 2} (odd w), five 16-wide steps per column either way
+    const int cp = w >> 1;
+    auto wpair = [&](auto rtc) {
+      constexpr int rt = decltype(rtc)::value;
+      const f32x4 a0 = tri_mma(sKbt + (32 * cp + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
+      const f32x4 a1 = tri_mma(sKbt + (32 * cp + 16 + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
+      store_pair<Op>(rW + tile_elem(tile_cr(2 * cp, rt), lane), -a0, -a1);
+    };
+    if (w & 1) {
+      wpair(std::integral_constant<int, 1>{});
+      wpair(std::integral_constant<int, 2>{});
+    } else {
+      wpair(std::integral_constant<int, 0>{});
+      wpair(std::integral_constant<int, 3>{});
+    }
+  } else {
 #pragma unroll
-  for (int j = 0; j < NQW; ++j) {   // W^T tile (ct, rt)
-    int ct, rt;
-    wave_tile(w, j, NQW, ct, rt);
-    const f32x4 acc = tri_mma(sKbt + (16 * ct + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
-    store4<Op>(rW + tile_elem(tile_cr(ct, rt), lane), narrow4<Op>(-acc));   // the record holds -W
+    for (int j = 0; j < NQW; ++j) {   // W^T tile (ct, rt)
+      int ct, rt;
+      wave_tile(w, j, NQW, ct, rt);
+      const f32x4 acc = tri_mma(sKbt + (16 * ct + l16) * L::LB, sTm + (16 * rt + l16) * L::LB, rt + 1);
+      store4<Op>(rW + tile_elem(tile_cr(ct, rt), lane), narrow4<Op>(-acc));
+    }
   }
   constexpr int NUT = (DV / 16) * 4;
   constexpr int NUW = NUT / kNW;
@@ -855,11 +933,16 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   // Ut into the record as Op, range-scaled by su (exact power of two)
   float su = 1.f, suinv = 1.f;
   if (P::kMixed) fp16_range_scale2(block_max(umax, sRed + 8), su, suinv);
+  if constexpr (NUW == 4) {   // wave w holds tiles 4w .. 4w + 3: two pairs
 #pragma unroll
-  for (int j = 0; j < NUW; ++j) {
-    int jt, st;
-    wave_tile(w, j, NUW, jt, st);
-    store4<Op>(rU + tile_elem(jt * 4 + st, lane), narrow4<Op>(ut[j] * su));
+    for (int j = 0; j < 4; j += 2) store_pair<Op>(rU + tile_elem(4 * w + j, lane), ut[j] * su, ut[j + 1] * su);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NUW; ++j) {
+      int jt, st;
+      wave_tile(w, j, NUW, jt, st);
+      store4<Op>(rU + tile_elem(jt * 4 + st, lane), narrow4<Op>(ut[j] * su));
+    }
   }
   if (tid == 0) *rUinv = suinv;
   stp.mark<9>();
