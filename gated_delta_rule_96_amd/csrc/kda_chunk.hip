@@ -476,7 +476,9 @@ __device__ __forceinline__ bool produce_chunk(char* smem, InRegs<TIn, DK, DV>& i
   const int l16 = lane & 15, g4 = 4 * (lane >> 4);
   const size_t tokk = (size_t)H * DK;
   const size_t base_k = ((size_t)b * T_len + t0) * tokk + (size_t)h * DK;
-  __syncthreads();   // a previous call's LDS readers are done
+  // (no barrier here: a caller running several chunks in one work-group
+  // passes a barrier between them, after the previous chunk's last LDS
+  // access; the fused loop's hand-off has one)
   stp.mark<0>();   // producer slots: 0 entry, 1-8 phase work, 17-24 their barriers, 9 phase 3, 10 publish
   Op* rW = reinterpret_cast<Op*>(rec) + R::W;
   Op* rQ = reinterpret_cast<Op*>(rec) + R::Q;
@@ -1635,6 +1637,8 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   // the L2; otherwise an agent-scope release (L2 write-back).
   // A consumer's XCD word is written once, at its start, so a head whose
   // consumers were seen on this XCD is remembered (bit of same_mask).
+  // Its barrier also separates the item's last LDS accesses from the next
+  // item's first (produce_chunk has no barrier of its own at entry).
   unsigned same_mask = 0;
   auto publish = [&](int pi) {
     const int pc = pi / nloc, pl = pi % nloc, pj = xcd + 8 * pl;
