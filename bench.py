@@ -150,7 +150,7 @@ STAMP_NAMES = {
         9: "W and U to the record", 10: "hand-off (publish)"},
     2: {0: "loop top", 1: "barrier (record staged)", 2: "abort word", 3: "range scale, U accumulators",
         4: "U and Q-bar products issued", 5: "K-hat/M/decay reads, U range", 6: "state update, output, stores",
-        7: "snapshots"},
+        7: "snapshots, next range scale and Sh"},
     3: {0: "loop top", 1: "barrier", 2: "abort word, progress store", 3: "wait for the next record",
         4: "record loads issued", 5: "loads completed, LDS writes"},
 }

@@ -1325,9 +1325,35 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   // every chunk cost the state pass 10%.)
   int seq = -1, c_beg = 0, c_end = 0, t_beg = 0, t_end = 0;
   int snap_left = snap.every;
-  // owner slots: 0 loop top, 1 barrier X, 2 abort word, 3 sigma, Sh and
-  // the U accumulators, 4 U and Qbar products issued, 5 Khat/M/decay reads
-  // and the U range, 6 state update, output and stores, 7 snapshots
+  // The products run in the sigma domain (bf16 mode): Sh = sigma S and
+  // Uh = sigma U are fp16 operands as they are (fp16 has the same relative
+  // precision at every normal magnitude; sigma keeps the largest values in
+  // range), and the record holds -W, so the MFMAs accumulating onto sigma
+  // Ut give Uh directly.  A chunk's sigma and fp16 Sh depend on the state
+  // alone, so they are formed at the end of the chunk before (ahead of the
+  // barrier the owners then wait at), and here for the first chunk.
+  float sig = 1.f, isig = 1.f;
+  V4<Op> Sb[NCT];
+  auto prepare_state = [&]() {
+    if (mixed) {
+      const int k = domain_rescale_exp(m0, sig_e);
+      if (k != 0) {
+        const float f = ldexpf(1.f, k);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) S[ct] = S[ct] * f;
+        sig_e += k;
+      }
+    }
+    sig = ldexpf(1.f, sig_e);
+    isig = ldexpf(1.f, -sig_e);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) Sb[ct] = narrow4<Op>(S[ct]);
+  };
+  if (!packed) prepare_state();
+  // owner slots: 0 loop top, 1 barrier X, 2 abort word, 3 the U
+  // accumulators, 4 U and Qbar products issued, 5 Khat/M/decay reads and the
+  // U range, 6 state update, output and stores, 7 snapshots and the next
+  // chunk's sigma and Sh
   stp.add<kStampRole>(2);
   for (int c = 0; c < nchunks; ++c) {
     stp.mark<0>();
@@ -1358,30 +1384,13 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       for (int ct = 0; ct < NCT; ++ct) m0 = fmaxf(m0, absmax4(S[ct]));
       m0 = wave_max_dpp(m0);
       sig_e = 0;
+      prepare_state();
     }
     const int j = packed ? c - c_beg : c;                        // chunk of the sequence
     const int t0 = packed ? t_beg + j * kC : c * kC;
     const int rows = min(kC, (packed ? t_end : T_len) - t0);
     const bool seq_last = packed ? c + 1 == c_end : (c + 1) * kC >= T_len;   // uniform
 
-    // The products run in the sigma domain (bf16 mode): Sh = sigma S and
-    // Uh = sigma U are fp16 operands as they are (fp16 has the same
-    // relative precision at every normal magnitude; sigma keeps the
-    // largest values in range), and the record holds -W, so the MFMAs
-    // accumulating onto sigma Ut give Uh directly.
-    if (mixed) {
-      const int k = domain_rescale_exp(m0, sig_e);
-      if (k != 0) {
-        const float f = ldexpf(1.f, k);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) S[ct] = S[ct] * f;
-        sig_e += k;
-      }
-    }
-    const float sig = ldexpf(1.f, sig_e), isig = ldexpf(1.f, -sig_e);
-    V4<Op> Sb[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) Sb[ct] = narrow4<Op>(S[ct]);
     // Uh = sigma Ut - W Sh and the Qbar Sh part of O, row block by row
     // block (both need only Sh); O^T = Sh^T Qbar^T + Uh^T (scale M)^T:
     // lane l holds row 16rt + l%16, columns 16jt + 4(l/16) .. +3.
@@ -1497,13 +1506,15 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       }
     }
     if (packed && seq_last && ht) {   // the sequence's final state
-      const float isig = ldexpf(1.f, -sig_e);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           ht[((size_t)seq * H + h) * DK * DV + (size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
     }
+    // the next chunk's sigma and Sh (a sequence's first chunk forms its own;
+    // none after the last chunk, whose state goes out as it is)
+    if (c + 1 < nchunks && !(packed && seq_last)) prepare_state();
     stp.mark<7>();
     stp.add<kStampCount>(1);
     if (NBUF == 1) __syncthreads();   // Y_c

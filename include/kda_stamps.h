@@ -25,9 +25,10 @@
  *     the distance-1 inverse blocks, 6 distance 2, 7 distance 3, 8 Tm) and
  *     17-24 the wait at the barrier that ends each of them, 9 W and U to the
  *     record, 10 the hand-off (record visible, ready flag).
- *   owner: 0 loop top, 1 barrier, 2 abort word, 3 range scale and U
- *     accumulators, 4 U and Q-bar products issued, 5 K-hat/M/decay operands
- *     and the U range, 6 state update, output and stores, 7 snapshots.
+ *   owner: 0 loop top, 1 barrier, 2 abort word, 3 U accumulators, 4 U and
+ *     Q-bar products issued, 5 K-hat/M/decay operands and the U range,
+ *     6 state update, output and stores, 7 snapshots and the next chunk's
+ *     range scale and fp16 copy of the state.
  *   staging: 0 loop top, 1 barrier, 2 abort word and progress store,
  *     3 wait for the next record, 4 loads issued, 5 loads completed and
  *     written to LDS.
