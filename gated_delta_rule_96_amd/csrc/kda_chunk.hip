@@ -1127,12 +1127,15 @@ struct Snap {
 };
 
 // kLay: the output gate may be requested; kSeg: snapshots and packed
-// sequences may be requested (each compiled out otherwise).
+// sequences may be requested (each compiled out otherwise).  cbase: the
+// ring's chunk count before this head (a ring serves the heads of several
+// rounds in turn; its flags and progress count on across them).  Returns
+// false if the chain stopped early (a hand-off wait gave up).
 template <typename TIn, int DK, int DV, bool kRing, bool kLay, bool kSeg>
-__device__ __forceinline__ void consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
+__device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict__ recbase, Ring ring, int vb,
                                               const float* __restrict__ h0, float* __restrict__ ht,
                                               float* __restrict__ o, int b, int h, int T_len, int H,
-                                              int nchunks, Snap snap, Stamps& stp,
+                                              int nchunks, int cbase, Snap snap, Stamps& stp,
                                               Layer lay = Layer{nullptr, nullptr, 0}, const VarSeg* var = nullptr) {
   using P = Policy<TIn>;
   using Op = typename P::Op;
@@ -1152,7 +1155,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
   const int jl0 = owner ? w : 0;                   // local column tile
   const int jt0 = vb * kOwners + jl0;              // column tile of the head
   const size_t bh = (size_t)b * H + h;
-  auto rec_of = [&](int c) { return recbase + (size_t)(kRing ? c % ring.R : c) * R::BYTES; };
+  auto rec_of = [&](int c) { return recbase + (size_t)(kRing ? (cbase + c) % ring.R : c) * R::BYTES; };
   auto buf_of = [&](int c) { return smem + (size_t)(NBUF == 2 ? (c & 1) : 0) * CL::BUF; };
 
   // A producer on this XCD wrote the chunk into the L2 this work-group
@@ -1190,7 +1193,8 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     // shows the chunk, there is no polling at all.
     auto ready_wait = [&](int c, int seen) -> bool {
       if (!kRing) return true;
-      const int v = seen >= ((c + 1) << 4) ? seen : spin_until_geq(ring.ready + c % ring.R, (c + 1) << 4, ring.err);
+      const int cg = cbase + c;
+      const int v = seen >= ((cg + 1) << 4) ? seen : spin_until_geq(ring.ready + cg % ring.R, (cg + 1) << 4, ring.err);
       if (v < 0) return false;
       if ((v & 15) == my_xcc) asm volatile("buffer_inv sc0" ::: "memory");
       else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -1198,7 +1202,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     };
     auto peek = [&](int c) -> int {   // chunk c's ready word, read now, used a chunk later
       return (kRing && c < nchunks)
-                 ? __hip_atomic_load(ring.ready + c % ring.R, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 ? __hip_atomic_load(ring.ready + (cbase + c) % ring.R, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                  : 0;
     };
     // staged vector n: the shared part, then this work-group's Ut columns
@@ -1252,9 +1256,10 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       stp.mark<0>();
       __syncthreads();   // X_c
       stp.mark<1>();
-      if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
+      if (__builtin_amdgcn_readfirstlane(*sAbort)) return false;
       // chunk c has been read completely: hand its slot back
-      if (kRing && htid == 0) __hip_atomic_store(ring.done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (kRing && htid == 0)
+        __hip_atomic_store(ring.done, cbase + c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int seen = __builtin_amdgcn_readfirstlane(seen_next);
       seen_next = peek(c + 2);
       stp.mark<2>();
@@ -1272,7 +1277,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
       }
       stp.add<kStampCount>(1);
     }
-    return;
+    return true;
   }
 
   // Packed sequences (extended variant): the state restarts at every
@@ -1359,7 +1364,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
     stp.mark<0>();
     __syncthreads();   // X_c
     stp.mark<1>();
-    if (__builtin_amdgcn_readfirstlane(*sAbort)) return;
+    if (__builtin_amdgcn_readfirstlane(*sAbort)) return false;
     stp.mark<2>();
     const char* buf = buf_of(c);
     const Op* sW = reinterpret_cast<const Op*>(buf) + R::W;
@@ -1527,6 +1532,7 @@ __device__ __forceinline__ void consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i) ht[sbase + (size_t)(16 * ct + g4 + i) * DV + 16 * jt0 + l16] = S[ct][i] * isig;
   }
+  return true;
 }
 
 // Two-stage schedule, stage 2: NS work-groups per head.
@@ -1541,7 +1547,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
   Stamps stp;
   consume_chain<TIn, DK, DV, false, false, false>(smem, ws + (size_t)bh * nchunks * Rec<TIn, DK, DV>::BYTES,
                                            Ring{nullptr, nullptr, nullptr, nullptr, 1}, vb, h0, ht, o, bh / H,
-                                           bh % H, T_len, H, nchunks, snap, stp);
+                                           bh % H, T_len, H, nchunks, 0, snap, stp);
 }
 
 // ---------------------------------------------------------------------------
@@ -1576,9 +1582,11 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(const char* __rest
 // line of their own: waves that poll different words (and the error word)
 // then never queue behind each other on one line.
 // [32 ..) is zeroed before every launch; [0..16) once per API call
-// (launch_clear_status), so an error word set by any launch of a call (one
-// per batch of heads, or per sequence) stays set until the caller reads it,
-// and every later launch of the call gives up at its first wait.
+// (launch_clear_status), so an error word set by any launch of a call stays
+// set until the caller reads it, and every later launch of the call gives
+// up at its first wait.  A launch runs its heads in rounds of nheads head
+// slots; a slot's ready and progress words count its ring's chunks across
+// the rounds.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 struct FusedLds {
@@ -1586,22 +1594,30 @@ struct FusedLds {
   static constexpr size_t BYTES = (A > B ? A : B) + 16;
 };
 
-template <typename TIn, int DK, int DV, bool kUnb, bool kLay, bool kSeg>
+// kRounds: the launch may hold more heads than one round (otherwise
+// nbh_run == nheads, and the round arithmetic is compiled out).
+template <typename TIn, int DK, int DV, bool kUnb, bool kLay, bool kSeg, bool kRounds>
 __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                              const TIn* __restrict__ v, const TIn* __restrict__ g,
                                                              const float* __restrict__ gcum,
                                                              const TIn* __restrict__ beta, float scale,
                                                              const float* __restrict__ h0, float* __restrict__ ht,
                                                              float* __restrict__ o, int T_len, int H, int nchunks,
-                                                             int head0, int nheads, char* __restrict__ ring,
-                                                             int* __restrict__ ctrl, int R, Snap snap, Layer lay,
-                                                             VarSeg var) {
+                                                             int head0, int nheads, int nbh_run,
+                                                             char* __restrict__ ring, int* __restrict__ ctrl, int R,
+                                                             Snap snap, Layer lay, VarSeg var) {
   using Rc = Rec<TIn, DK, DV>;
   __shared__ __align__(16) char smem[FusedLds<TIn, DK, DV>::BYTES];
   const VarSeg* vp = kSeg ? &var : nullptr;   // packed sequences (snapshot variant only)
   int* sWord = reinterpret_cast<int*>(smem + FusedLds<TIn, DK, DV>::BYTES - 16);
   const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
-  const int nloc = nheads > xcd ? (nheads - xcd + 7) / 8 : 0;   // heads j = xcd + 8m of this launch
+  // The launch's nbh_run heads (from head0) go in rounds of nheads: head
+  // slot j (0 <= j < nheads) of round r is head head0 + r nheads + j; slot j
+  // keeps its ring, flags and state-pass work-groups for every round.
+  const int rounds = kRounds ? (nbh_run + nheads - 1) / nheads : 1;
+  const int last_n = kRounds ? nbh_run - (rounds - 1) * nheads : nheads;   // heads of the last round
+  const int nloc = nheads > xcd ? (nheads - xcd + 7) / 8 : 0;              // slots j = xcd + 8m of this XCD
+  const int nloc_last = kRounds ? (last_n > xcd ? (last_n - xcd + 7) / 8 : 0) : nloc;   // ... in the last round
   constexpr int NS = ConsumerLds<TIn, DK, DV>::NS;
   int* err = ctrl + 8;
   int* ready = ctrl + kFlagBase;
@@ -1609,26 +1625,41 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
   int* cxcc = done + nheads * NS * kFlagLine;
   Stamps stp;
 
-  if (li < nloc * NS) {   // consumer vb of head jh
-    const int jh = xcd + 8 * (li / NS), vb = li % NS, bh = head0 + jh;
-    consume_chain<TIn, DK, DV, true, kLay, kSeg>(smem, ring + (size_t)jh * R * Rc::BYTES,
-                                           Ring{ready + jh * kFlagLine, done + (jh * NS + vb) * kFlagLine, err,
-                                                cxcc + jh * NS + vb, R},
-                                           vb,
-                                           h0, ht, o, bh / H, bh % H, T_len, H, nchunks, snap, stp, lay, vp);
+  if (li < nloc * NS) {   // state pass vb of head slot jh, one head per round
+    const int jh = xcd + 8 * (li / NS), vb = li % NS;
+    const Ring rg{ready + jh * kFlagLine, done + (jh * NS + vb) * kFlagLine, err, cxcc + jh * NS + vb, R};
+    for (int r = 0; r < rounds && (r + 1 < rounds || jh < last_n); ++r) {
+      const int bh = head0 + r * nheads + jh;
+      if (!consume_chain<TIn, DK, DV, true, kLay, kSeg>(smem, ring + (size_t)jh * R * Rc::BYTES, rg, vb, h0, ht, o,
+                                                        bh / H, bh % H, T_len, H, nchunks, r * nchunks, snap, stp,
+                                                        lay, vp))
+        break;
+    }
     stp.flush();
     return;
   }
 
   // producer p of this XCD's P producers: items p, p + P, p + 2P, ... of
-  // this XCD's heads in chunk-major order (item = chunk * nloc + local head).
-  // No deadlock: the smallest item any producer waits on only needs chunks
-  // of smaller items, and every smaller item is finished because each
-  // producer handles its items in increasing order.
-  const int total = nloc * nchunks;
+  // this XCD's head slots, round by round and chunk-major within a round
+  // (item = (r nchunks + chunk) nloc + local slot in the full rounds).  A
+  // slot's ring counts its chunks across rounds: ring chunk cg = r nchunks
+  // + chunk.  No deadlock: the smallest item any producer waits on only
+  // needs chunks of smaller items, and every smaller item is finished
+  // because each producer handles its items in increasing order.
+  const int per_round = nloc * nchunks;
+  const int total = (rounds - 1) * per_round + nloc_last * nchunks;
   const int P = (int)(gridDim.x >> 3) - nloc * NS;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int my_xcc = xcc_id();
+  struct Item {
+    int r, c, pl;   // round, chunk of the head, local head slot
+  };
+  auto item_of = [&](int i) -> Item {
+    if (!kRounds) return Item{0, i / nloc, i % nloc};
+    const int r = min(i / per_round, rounds - 1), rem = i - r * per_round;
+    if (r + 1 < rounds) return Item{r, rem / nloc, rem % nloc};
+    return Item{r, rem / nloc_last, rem % nloc_last};
+  };
   InRegs<TIn, DK, DV> in;
   int it = li - nloc * NS;
   stp.add<kStampRole>(1);
@@ -1636,23 +1667,27 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     stp.flush();
     return;
   }
-  int seq_cur = 0, seq_next = 0;   // sequence cursors of this item and of the next one
+  // sequence cursors of this item and of the next one (reset when the
+  // round changes: chunk indices start again from 0)
+  int seq_cur = 0, seq_next = 0, r_cur = 0, r_next = 0;
+  Item xc = item_of(it);   // this item (the next one is carried over)
   {
-    const int jh = xcd + 8 * (it % nloc), bh = head0 + jh;
-    const ChunkPos ps = chunk_pos(vp, it / nloc, T_len, seq_next);
+    const int bh = head0 + xc.r * nheads + xcd + 8 * xc.pl;
+    r_next = xc.r;
+    const ChunkPos ps = chunk_pos(vp, xc.c, T_len, seq_next);
     load_inputs<TIn, DK, DV>(in, q, k, v, g, beta, bh / H, bh % H, T_len, H, ps.t0, ps.rows);
   }
-  // Publishes item `pi` (its record stores were issued by every wave).
-  // Release: if the head's consumers run on this XCD they read through the
-  // same L2, so it is enough that every wave's record stores have reached
-  // the L2; otherwise an agent-scope release (L2 write-back).
-  // A consumer's XCD word is written once, at its start, so a head whose
+  // Publishes ring chunk cg of slot pl (its record stores were issued by
+  // every wave).  Release: if the slot's consumers run on this XCD they read
+  // through the same L2, so it is enough that every wave's record stores
+  // have reached the L2; otherwise an agent-scope release (L2 write-back).
+  // A consumer's XCD word is written at its start, so a slot whose
   // consumers were seen on this XCD is remembered (bit of same_mask).
   // Its barrier also separates the item's last LDS accesses from the next
   // item's first (produce_chunk has no barrier of its own at entry).
   unsigned same_mask = 0;
-  auto publish = [&](int pi) {
-    const int pc = pi / nloc, pl = pi % nloc, pj = xcd + 8 * pl;
+  auto publish = [&](int cg, int pl) {
+    const int pj = xcd + 8 * pl;
     bool same = pl < 32 && ((same_mask >> pl) & 1u);
     if (!same) {
       same = true;
@@ -1665,26 +1700,40 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (w == 0 && lane == 0)
-      __hip_atomic_store(ready + pj * kFlagLine + pc % R, ((pc + 1) << 4) | my_xcc, __ATOMIC_RELAXED,
+      __hip_atomic_store(ready + pj * kFlagLine + cg % R, ((cg + 1) << 4) | my_xcc, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   };
   for (;;) {
-    const int c = it / nloc, jh = xcd + 8 * (it % nloc), bh = head0 + jh;
+    const Item x = xc;
+    const int c = x.c, cg = x.r * nchunks + c, jh = xcd + 8 * x.pl, bh = head0 + x.r * nheads + jh;
     const int nxt = it + P;
+    if (x.r != r_cur) {
+      r_cur = x.r;
+      seq_cur = 0;
+    }
     const ChunkPos pc = chunk_pos(vp, c, T_len, seq_cur);
-    // the next item's position, once per item (its table reads wait for the
-    // LDS accesses in flight, so not inside the phases)
-    const ChunkPos pn = nxt < total ? chunk_pos(vp, nxt / nloc, T_len, seq_next) : pc;
-    // The ring slot of chunk c is free once the head's consumers have read
-    // chunk c - R.  Wave 0 reads their progress words from this XCD's L2
-    // once the inputs are staged (after the input registers are consumed:
-    // vector loads complete in order), checks them at the end of the block
-    // scans, polling only if the slot is still taken, and leaves its verdict
-    // in LDS for the other waves to read after the next barrier.
+    // the next item and its position, once per item (its table reads wait
+    // for the LDS accesses in flight, so not inside the phases)
+    Item xn = x;
+    ChunkPos pn = pc;
+    if (nxt < total) {
+      xn = item_of(nxt);
+      if (xn.r != r_next) {
+        r_next = xn.r;
+        seq_next = 0;
+      }
+      pn = chunk_pos(vp, xn.c, T_len, seq_next);
+    }
+    // The ring slot of ring chunk cg is free once the slot's consumers have
+    // read ring chunk cg - R.  Wave 0 reads their progress words from this
+    // XCD's L2 once the inputs are staged (after the input registers are
+    // consumed: vector loads complete in order), checks them at the end of
+    // the block scans, polling only if the slot is still taken, and leaves
+    // its verdict in LDS for the other waves to read after the next barrier.
     int seen[NS] = {};
     auto slot = [&](auto step) -> bool {
       constexpr int s = decltype(step)::value;
-      if (c < R) return true;
+      if (cg < R) return true;
       if (s == kSlotPeek && w == 0) {
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(done + jh * NS * kFlagLine, (short)0, NS * kFlagLine * 4, kBufferRsrcWord3);
@@ -1695,8 +1744,8 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
         bool ok = true;
 #pragma unroll
         for (int vb = 0; vb < NS; ++vb)
-          if (ok && __builtin_amdgcn_readfirstlane(seen[vb]) < c - R + 1)
-            ok = spin_until_geq(done + (jh * NS + vb) * kFlagLine, c - R + 1, err) >= 0;
+          if (ok && __builtin_amdgcn_readfirstlane(seen[vb]) < cg - R + 1)
+            ok = spin_until_geq(done + (jh * NS + vb) * kFlagLine, cg - R + 1, err) >= 0;
         if (lane == 0) *sWord = ok ? 1 : 0;
       } else if (s == kSlotOk) {
         return __builtin_amdgcn_readfirstlane(*sWord) != 0;
@@ -1706,13 +1755,13 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     // the next item's inputs, loaded in portions during this item's phases
     auto prefetch = [&](auto parts) {
       if (nxt < total) {
-        const int jn = xcd + 8 * (nxt % nloc), bn = head0 + jn;
+        const int bn = head0 + xn.r * nheads + xcd + 8 * xn.pl;
         load_inputs<TIn, DK, DV, decltype(parts)::value>(in, q, k, v, g, beta, bn / H, bn % H, T_len, H, pn.t0,
                                                          pn.rows);
       }
     };
     if (!produce_chunk<TIn, DK, DV, kUnb, kLay>(smem, in, gcum, scale, bh / H, bh % H, T_len, H, pc.t0, pc.rows,
-                                    ring + ((size_t)jh * R + c % R) * Rc::BYTES, slot, prefetch, stp, lay)) {
+                                    ring + ((size_t)jh * R + cg % R) * Rc::BYTES, slot, prefetch, stp, lay)) {
       stp.flush();
       return;
     }
@@ -1720,7 +1769,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
     // the next item's inputs were staged let the stores drain in the
     // background but made every record visible some 4-5k cycles later; the
     // consumers then waited for records and the producers for ring slots.)
-    publish(it);
+    publish(cg, x.pl);
     stp.mark<10>();
     stp.add<kStampCount>(1);
     if (nxt >= total) {
@@ -1728,6 +1777,7 @@ __global__ __launch_bounds__(kThreads) void fused_fwd_kernel(const TIn* __restri
       return;
     }
     it = nxt;
+    xc = xn;
   }
 }
 
@@ -1750,15 +1800,17 @@ static int fused_heads_per_launch(int per_xcd, int ns) {
   return hx > 0 ? 8 * hx : 0;
 }
 
-// Heads per launch for nbh heads (at most cap per launch, wgs work-groups,
-// ns state-pass work-groups per head).  A launch of nh heads takes, per
+// Heads per round for nbh heads (at most cap per round, wgs work-groups,
+// ns state-pass work-groups per head).  A round of nh heads takes, per
 // chunk of its heads, about max(t_chain, nh t_item / (wgs - ns nh)): one
 // chunk of a head's state pass, or the producers' share of the records
-// (t_item: one record on one producer work-group).  The number of launches L
+// (t_item: one record on one producer work-group).  The number of rounds L
 // minimising L times that maximum gives the batch; measured t_item / t_chain
-// is about 5.7 (d_k = d_v = 128), so a launch of about 32 heads keeps both
-// sides busy, and 64 heads run as two launches of 32 rather than one with
-// half the work-groups holding state passes.
+// is about 5.7 (d_k = d_v = 128), so a round of about 32 heads keeps both
+// sides busy, and 64 heads run as two rounds of 32 rather than one with
+// half the work-groups holding state passes.  The rounds share one launch:
+// the producers go on to the next round's records while the last chunks of
+// the round before are still in the state passes.
 static int fused_launch_batch(int nbh, int cap, int wgs, int ns) {
   constexpr double kItemOverChain = 5.7;
   int best = nbh < cap ? nbh : cap;
@@ -1822,26 +1874,25 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   if (batch <= 0) return hipErrorInvalidValue;
   int* ctrl = reinterpret_cast<int*>(ws);
   char* ring = reinterpret_cast<char*>(ws) + fused_ctrl_bytes<TIn, DK, DV>(batch);
-  for (int head0 = 0; head0 < nbh; head0 += batch) {
-    const int nh = nbh - head0 < batch ? nbh - head0 : batch;
-    // ctrl[kFlagBase ..): this launch's flags only
-    const int nflags = nh * kFlagLine + NS * nh * kFlagLine + NS * nh;
-    hipLaunchKernelGGL(clear_ints_kernel, dim3((nflags + 255) / 256), dim3(256), 0, st, ctrl + kFlagBase, nflags);
-    // four variants: plain, unbounded decay, layer steps, snapshots / packed sequences
-    const bool with_lay = lay.flags != 0 || lay.og != nullptr;
-    const bool with_seg = (snap != nullptr && snap_every > 0) || packed;
-    if ((unb && (with_lay || with_seg)) || (with_lay && with_seg)) return hipErrorInvalidValue;
-    auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true, false, false>
-                    : with_lay ? fused_fwd_kernel<TIn, DK, DV, false, true, false>
-                               : (with_seg ? fused_fwd_kernel<TIn, DK, DV, false, false, true>
-                                           : fused_fwd_kernel<TIn, DK, DV, false, false, false>);
-    hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q, (const TIn*)k, (const TIn*)v,
-                       (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len, H, nchunks, head0, nh, ring,
-                       ctrl, kRingSlots, Snap{snap, snap_every, nbh}, lay, packed ? *var : kNoVar);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  // one launch: rounds of `batch` heads (slot j of every round shares ring j)
+  const int nh = nbh < batch ? nbh : batch;
+  const int nflags = nh * kFlagLine + NS * nh * kFlagLine + NS * nh;   // ctrl[kFlagBase ..)
+  hipLaunchKernelGGL(clear_ints_kernel, dim3((nflags + 255) / 256), dim3(256), 0, st, ctrl + kFlagBase, nflags);
+  // four variants: plain, unbounded decay, layer steps, snapshots / packed sequences
+  const bool with_lay = lay.flags != 0 || lay.og != nullptr;
+  const bool with_seg = (snap != nullptr && snap_every > 0) || packed;
+  if ((unb && (with_lay || with_seg)) || (with_lay && with_seg)) return hipErrorInvalidValue;
+  // (the plain variant also comes as a one-round kernel, used when the
+  // heads fit one round: the round arithmetic cost it 1% at 32 heads)
+  auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true, false, false, true>
+                  : with_lay ? fused_fwd_kernel<TIn, DK, DV, false, true, false, true>
+                             : (with_seg ? fused_fwd_kernel<TIn, DK, DV, false, false, true, true>
+                                         : (nbh > nh ? fused_fwd_kernel<TIn, DK, DV, false, false, false, true>
+                                                     : fused_fwd_kernel<TIn, DK, DV, false, false, false, false>));
+  hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q, (const TIn*)k, (const TIn*)v,
+                     (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len, H, nchunks, 0, nh, nbh, ring,
+                     ctrl, kRingSlots, Snap{snap, snap_every, nbh}, lay, packed ? *var : kNoVar);
+  return hipGetLastError();
 }
 
 template <typename TIn, int DK, int DV>
