@@ -45,14 +45,14 @@ def _oracle_seq(c, i, upto=None):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("lengths,dk,dv,every", [
-    ([1, 64, 130, 0, 257, 33], 128, 128, 2),
-    ([700, 5, 128], 64, 64, 3),
-    ([0, 190, 64], 128, 64, 1),
+@pytest.mark.parametrize("lengths,dk,dv,every,H", [
+    ([1, 64, 130, 0, 257, 33], 128, 128, 2, 2),
+    ([700, 5, 128], 64, 64, 3, 2),
+    ([0, 190, 64], 128, 64, 1, 2),
+    ([130, 1, 257], 128, 128, 2, 70),   # the fused launch runs 70 heads as rounds of 40 and 30
 ])
-def test_varlen_matches_oracle_with_snapshots(dtype, lengths, dk, dv, every):
-    say(f"varlen dtype={dtype} lengths={lengths} dk={dk} dv={dv} every={every}")
-    H = 2
+def test_varlen_matches_oracle_with_snapshots(dtype, lengths, dk, dv, every, H):
+    say(f"varlen dtype={dtype} lengths={lengths} dk={dk} dv={dv} every={every} H={H}")
     c = _packed(lengths, H, dk, dv, seed=41, dtype=dtype)
     dev = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in c.items()}
     o, ht, snaps = kda.fwd_chunked_varlen(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], c["cu"], dev["h0"],
@@ -77,11 +77,13 @@ def test_varlen_matches_oracle_with_snapshots(dtype, lengths, dk, dv, every):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_varlen_equals_separate_calls_bitwise(dtype):
+@pytest.mark.parametrize("H", [3, 70])
+def test_varlen_equals_separate_calls_bitwise(dtype, H):
     # Packing changes nothing: each sequence gets exactly the result of its
-    # own kda_fwd_chunked call (same kernels, same chunking from its start).
+    # own kda_fwd_chunked call (same chunking from its start; with 70 heads
+    # both run the fused launch in two rounds, of 40 and 30 heads).
     lengths = [300, 1, 64, 129]
-    H, dk, dv = 3, 128, 128
+    dk, dv = 128, 128
     c = _packed(lengths, H, dk, dv, seed=42, dtype=dtype)
     dev = {n: (t.cuda() if isinstance(t, torch.Tensor) else t) for n, t in c.items()}
     o, ht, _ = kda.fwd_chunked_varlen(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], c["cu"], dev["h0"])
