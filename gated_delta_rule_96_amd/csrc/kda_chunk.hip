@@ -1882,13 +1882,17 @@ static hipError_t go_fused(const void* q, const void* k, const void* v, const vo
   const bool with_lay = lay.flags != 0 || lay.og != nullptr;
   const bool with_seg = (snap != nullptr && snap_every > 0) || packed;
   if ((unb && (with_lay || with_seg)) || (with_lay && with_seg)) return hipErrorInvalidValue;
-  // (the plain variant also comes as a one-round kernel, used when the
-  // heads fit one round: the round arithmetic cost it 1% at 32 heads)
+  // (the plain, layer and packed-sequence variants also come as one-round
+  // kernels, used when the heads fit one round: the round arithmetic cost
+  // the plain one 1% at 32 heads, and spilled in the others' chunk loops)
+  const bool multi = nbh > nh;
   auto kern = unb ? fused_fwd_kernel<TIn, DK, DV, true, false, false, true>
-                  : with_lay ? fused_fwd_kernel<TIn, DK, DV, false, true, false, true>
-                             : (with_seg ? fused_fwd_kernel<TIn, DK, DV, false, false, true, true>
-                                         : (nbh > nh ? fused_fwd_kernel<TIn, DK, DV, false, false, false, true>
-                                                     : fused_fwd_kernel<TIn, DK, DV, false, false, false, false>));
+              : with_lay ? (multi ? fused_fwd_kernel<TIn, DK, DV, false, true, false, true>
+                                  : fused_fwd_kernel<TIn, DK, DV, false, true, false, false>)
+              : with_seg ? (multi ? fused_fwd_kernel<TIn, DK, DV, false, false, true, true>
+                                  : fused_fwd_kernel<TIn, DK, DV, false, false, true, false>)
+                         : (multi ? fused_fwd_kernel<TIn, DK, DV, false, false, false, true>
+                                  : fused_fwd_kernel<TIn, DK, DV, false, false, false, false>);
   hipLaunchKernelGGL(kern, dim3(8 * per_xcd), dim3(kThreads), 0, st, (const TIn*)q, (const TIn*)k, (const TIn*)v,
                      (const TIn*)g, gcum, (const TIn*)beta, scale, h0, ht, o, T_len, H, nchunks, 0, nh, nbh, ring,
                      ctrl, kRingSlots, Snap{snap, snap_every, nbh}, lay, packed ? *var : kNoVar);
