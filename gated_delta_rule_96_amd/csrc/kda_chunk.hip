@@ -1207,12 +1207,27 @@ __device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict
     };
     // staged vector n: the shared part, then this work-group's Ut columns
     const int uoff16 = (int)((R::U_OFF_BYTES + (size_t)vb * CL::UPART) / 16) - NSH16;
+    // With two buffers the record goes straight from memory into chunk c's
+    // LDS buffer (16-byte direct-to-LDS loads: lane l of a wave's load
+    // writes 16 bytes at the wave's base + 16 l; lanes that are switched off
+    // write nothing), so the staging waves hold no record in registers and
+    // issue no LDS writes for it; with one buffer it waits in registers for
+    // the owners to finish the chunk before.
     auto load = [&](int c) {
       const raw16* rec = reinterpret_cast<const raw16*>(rec_of(c));
+      if constexpr (NBUF == 2) {
+        raw16* buf = reinterpret_cast<raw16*>(buf_of(c)) + (htid & ~63);
 #pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int n = htid + kHelpers * i;
-        if (n < NV16) pre[i] = rec[n < NSH16 ? n : n + uoff16];
+        for (int i = 0; i < PPT; ++i) {
+          const int n = htid + kHelpers * i;
+          if (n < NV16) __builtin_amdgcn_global_load_lds(rec + (n < NSH16 ? n : n + uoff16), buf + kHelpers * i, 16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+          const int n = htid + kHelpers * i;
+          if (n < NV16) pre[i] = rec[n < NSH16 ? n : n + uoff16];
+        }
       }
       if (gate) {   // chunk c starts at token 64 c (the layer variant takes no packed sequences)
         const TIn* og = reinterpret_cast<const TIn*>(lay.og);
@@ -1228,18 +1243,21 @@ __device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict
     };
     auto stage = [&](int c) {
       char* buf = buf_of(c);
+      if constexpr (NBUF != 2) {
 #pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int n = htid + kHelpers * i;
-        if (n < NV16) reinterpret_cast<raw16*>(buf)[n] = pre[i];
+        for (int i = 0; i < PPT; ++i) {
+          const int n = htid + kHelpers * i;
+          if (n < NV16) reinterpret_cast<raw16*>(buf)[n] = pre[i];
+        }
       }
       if (gate) {
 #pragma unroll
         for (int i = 0; i < OPT; ++i) reinterpret_cast<raw16*>(buf + CL::OG_OFF)[htid + kHelpers * i] = ogp[i];
       }
-      // every load of chunk c has returned its data before its slot is
-      // handed back (after the next X)
-      if (kRing) wait_vmem();
+      // every load of chunk c has returned its data (and the direct-to-LDS
+      // loads have written it) before the next X, where the owners start
+      // reading it and its slot is handed back
+      wait_vmem();
     };
     ok = ready_wait(0, 0);
     int seen_next = peek(1);
