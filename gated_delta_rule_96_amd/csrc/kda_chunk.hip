@@ -1320,7 +1320,7 @@ __device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict
   if (!packed) {
     load_state(h0 ? h0 + sbase : nullptr);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) m0 = fmaxf(m0, absmax4(S[ct]));
+    for (int ct = 0; ct < NCT; ++ct) m0 = absmax_acc(m0, S[ct]);
     m0 = wave_max_dpp(m0);
   }
 
@@ -1404,7 +1404,7 @@ __device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict
       load_state(h0 ? h0 + ((size_t)seq * H + h) * DK * DV : nullptr);
       m0 = 0.f;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) m0 = fmaxf(m0, absmax4(S[ct]));
+      for (int ct = 0; ct < NCT; ++ct) m0 = absmax_acc(m0, S[ct]);
       m0 = wave_max_dpp(m0);
       sig_e = 0;
       prepare_state();
@@ -1460,7 +1460,7 @@ __device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict
     // of two r (wave-uniform branch).
     float umax = 0.f;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) umax = fmaxf(umax, absmax4(Uh[st]));
+    for (int st = 0; st < 4; ++st) umax = absmax_acc(umax, Uh[st]);
     int re = 0;
     if (mixed) {
       umax = wave_max_dpp(umax);
@@ -1510,7 +1510,7 @@ __device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         S[ct] = scl ? accS[ct] * ir : accS[ct];
-        smax = fmaxf(smax, absmax4(S[ct]));
+        smax = absmax_acc(smax, S[ct]);
       }
       m0 = mixed ? wave_max_dpp(smax) : 0.f;   // the next chunk's sigma comes from it
     };

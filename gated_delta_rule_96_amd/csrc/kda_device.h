@@ -142,6 +142,16 @@ constexpr float kNormEps = 1e-6f;
 __device__ __forceinline__ float absmax4(f32x4 v) {
   return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 }
+// max(m, |v[0]|, |v[1]|, |v[2]|, |v[3]|) for m >= 0, as two v_max3_f32 with
+// abs modifiers on the new values.  For finite values the same as fmaxf over
+// fabsf; it skips the canonicalising moves that fmaxf's NaN rules add to
+// each operand (a NaN operand is dropped, as fmaxf drops it).
+__device__ __forceinline__ float absmax_acc(float m, f32x4 v) {
+  float r, s;
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(v[0]), "v"(v[1]), "v"(m));
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(s) : "v"(v[2]), "v"(v[3]), "v"(r));
+  return s;
+}
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
