@@ -174,7 +174,7 @@ int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const v
   const int st = check_fwd(q, k, v, g, gcum, beta, h0, ht, o, dtype, B, T, H, dk, dv, chunk, kNoAllocWs, 3);
   if (st != KDA_OK) return st;
   // the scratch holds at least one head's ring for every supported size
-  // (more heads run as further launches); checked for completeness
+  // (more heads run as further rounds of the launch); checked for completeness
   if (kda_fwd_workspace_bytes(1, 1, 1, dk, dv, chunk, dtype) > kda::kNoAllocScratchBytes) return KDA_ERR_WORKSPACE;
   const int rs = check_range(dtype, g, gcum, 1, B, T, H, dk, stream);
   if (rs != KDA_OK) return rs;

@@ -130,8 +130,10 @@ int kda_prepare_decay_softplus(const void* z, const float* A, void* g, float* gc
 
 /* Bytes of device workspace kda_fwd_chunked needs for these sizes (0 if
  * the sizes are invalid or unsupported): ring buffers of a few chunk
- * records per head for at most one launch's batch of heads plus control
- * words, independent of T (about 45 MiB at B*H >= 84, dk = dv = 128, bf16). */
+ * records per head for at most one round of heads (the fused kernel runs
+ * more heads as further rounds of the same launch, reusing the rings) plus
+ * control words, independent of T (about 45 MiB at B*H >= 84, dk = dv =
+ * 128, bf16). */
 size_t kda_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
 
 /* Bytes of device workspace kda_fwd_chunked_stages needs: one record per
@@ -172,8 +174,9 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* g,
  * in a library-owned device array of 40 MiB per GPU (a file-scope array in
  * the code object, held until the process ends; no allocation by this call
  * or by the library).  The array holds the rings of 34 heads (fp32 inputs,
- * dk = dv = 128) to 70 heads (bf16 inputs): larger batches of heads run as
- * further launches, so no supported size is refused for lack of scratch.
+ * dk = dv = 128) to 70 heads (bf16 inputs): more heads run as further
+ * rounds of the one launch, so no supported size is refused for lack of
+ * scratch.
  * Every call on one GPU uses that GPU's array: calls that overlap on one
  * GPU (unordered streams) race and must not be issued.  Status:
  * kda_fwd_status(NULL, stream) reads this array's status word (current
