@@ -237,10 +237,26 @@ def test_fused_and_two_stage_schedules_agree_bitwise():
     assert torch.equal(o1, o3) and torch.equal(h1, h3)
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64)])
+def test_fused_rounds_one_state_pass_per_head(dk, dv):
+    """d_v = 64: one state-pass work-group per head, and 200 heads run as
+    several rounds of one launch (five of 40 by the launch cost model); all
+    heads against the oracle."""
+    B, H, T = 2, 100, 130
+    say(f"fused rounds dk={dk} dv={dv} B={B} H={H} T={T}")
+    c = prefill_case(B, T, H, dk, dv, seed=16, dtype=torch.bfloat16)
+    d = to_dev(c)
+    ws = kda.alloc_workspace(B, T, H, dk, dv, torch.bfloat16, "cuda")
+    o, ht = kda.fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], workspace=ws)
+    assert kda.workspace_error(ws) == 0
+    o_ref, h_ref = _oracle(c, c["h0"])
+    assert err_ratio(f32(o), o_ref) <= 2e-2 and err_ratio(ht.cpu().numpy(), h_ref) <= 2e-2
+
+
 @pytest.mark.parametrize("B,H", [(2, 64), (1, 3), (3, 1)])
 def test_fused_head_batching(B, H):
-    """More heads than one persistent launch serves (B*H = 128 > 96), and
-    fewer heads than XCDs."""
+    """More heads than one round of the persistent launch serves (B*H = 128
+    > 96), and fewer heads than XCDs."""
     say(f"fused head batching B={B} H={H}")
     c = prefill_case(B, 130, H, 128, 128, seed=15, dtype=torch.bfloat16)
     d = to_dev(c)
