@@ -1068,8 +1068,8 @@ constexpr int kOwners = 4;   // waves that own value columns, 16 each
 
 // The state pass of one head runs on NS work-groups (value-column blocks
 // of dv / NS = 64 columns), each staging the record's shared part (W, Qbar,
-// Khat, M, dec, uinv), its own Ut columns and (output gate) the chunk's og
-// rows of its columns.  LDS: NBUF such buffers (two when they fit, so that
+// Khat, M, dec, uinv), its own Ut columns and (output gate) the gates
+// Sigmoid(og) of the chunk's rows and its columns.  LDS: NBUF such buffers (two when they fit, so that
 // the next chunk is staged while the current one is computed) + abort word.
 template <typename TIn, int DK, int DV>
 struct ConsumerLds {
