@@ -1068,8 +1068,8 @@ constexpr int kOwners = 4;   // waves that own value columns, 16 each
 
 // The state pass of one head runs on NS work-groups (value-column blocks
 // of dv / NS = 64 columns), each staging the record's shared part (W, Qbar,
-// Khat, M, dec, uinv), its own Ut columns and (output gate) the gates
-// Sigmoid(og) of the chunk's rows and its columns.  LDS: NBUF such buffers (two when they fit, so that
+// Khat, M, dec, uinv), its own Ut columns and (output gate) the chunk's og
+// rows of its columns.  LDS: NBUF such buffers (two when they fit, so that
 // the next chunk is staged while the current one is computed) + abort word.
 template <typename TIn, int DK, int DV>
 struct ConsumerLds {
@@ -1079,7 +1079,7 @@ struct ConsumerLds {
   static constexpr size_t SH = R::U_OFF_BYTES;
   static constexpr size_t UPART = (size_t)kC * (DV / NS) * sizeof(Op);
   static constexpr size_t USED = SH + UPART;
-  static constexpr size_t OG_OFF = USED;                              // Sigmoid(og) [kC][DV / NS], sizeof(TIn) each
+  static constexpr size_t OG_OFF = USED;                              // og [kC][DV / NS] of TIn
   static constexpr size_t OGB = (size_t)kC * (DV / NS) * sizeof(TIn);
   static constexpr size_t BUF = (USED + OGB + 255) / 256 * 256;
   static constexpr int NBUF = 2 * BUF + 16 <= kLdsMax ? 2 : 1;
@@ -1181,11 +1181,7 @@ __device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict
     const int htid = tid - 64 * kOwners;
     raw16 pre[PPT];
     // output gate rows of the chunk (kLay with og): [kC][DV / NS] of TIn,
-    // OPT 16-byte pieces per thread, read once (non-temporal); the staging
-    // waves stage Sigmoid(og) in their place (fp16 for 2-byte inputs, fp32
-    // for fp32), so that the owners only multiply (the owners' two
-    // transcendental instructions per output value had cost the layer call
-    // 4%: 2.169 -> 2.090 ms)
+    // OPT 16-byte pieces per thread, read once (non-temporal)
     constexpr int ROWP = (DV / CL::NS) * (int)sizeof(TIn) / 16, OPT = (int)(CL::OGB / 16) / kHelpers;
     static_assert(OPT * kHelpers * 16 == (int)CL::OGB, "og staging");
     raw16 ogp[OPT];
@@ -1256,19 +1252,7 @@ __device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict
       }
       if (gate) {
 #pragma unroll
-        for (int i = 0; i < OPT; ++i) {   // the gates Sigmoid(og), in the size of og's type
-          raw16 gt;
-          if constexpr (sizeof(TIn) == 2) {
-            f16x8 h8;
-#pragma unroll
-            for (int x = 0; x < 8; ++x) h8[x] = (f16)sigmoid_fast(raw_elem<TIn>(ogp[i], x));
-            gt = __builtin_bit_cast(raw16, h8);
-          } else {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) gt[x] = sigmoid_fast(ogp[i][x]);
-          }
-          reinterpret_cast<raw16*>(buf + CL::OG_OFF)[htid + kHelpers * i] = gt;
-        }
+        for (int i = 0; i < OPT; ++i) reinterpret_cast<raw16*>(buf + CL::OG_OFF)[htid + kHelpers * i] = ogp[i];
       }
       // every load of chunk c has returned its data (and the direct-to-LDS
       // loads have written it) before the next X, where the owners start
@@ -1512,14 +1496,13 @@ __device__ __forceinline__ bool consume_chain(char* smem, const char* __restrict
         m += nms;
         Ov[rt] = (scl ? accO[rt] + am * ir : am) * isig;
       }
-      if (kLay && lay.og) {   // output gate: o <- Sigmoid(og) o, the gates staged with the record
-        using GT = typename std::conditional<sizeof(TIn) == 2, f16, float>::type;
-        const GT* sOg = reinterpret_cast<const GT*>(buf + CL::OG_OFF);
+      if (kLay && lay.og) {   // output gate: o <- Sigmoid(og) o, og rows staged with the record
+        const TIn* sOg = reinterpret_cast<const TIn*>(buf + CL::OG_OFF);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const f32x4 gz = widen4(load4(sOg + (16 * rt + l16) * (DV / CL::NS) + 16 * jl0 + g4));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Ov[rt][i] *= gz[i];
+          for (int i = 0; i < 4; ++i) Ov[rt][i] *= sigmoid_fast(gz[i]);
         }
       }
       store_out(t0, rows, Ov);
