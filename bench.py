@@ -18,9 +18,10 @@ parity check of the timed output against the CPU oracle on a sample, and the
 CPU oracle's own throughput (cpu_baseline).
 
 Profiling helpers (for rocprofv3 runs; they print no JSON line):
-  bench.py --probe fused|stages|copy [--calls N]
-      a few calls of one prefill schedule on the benchmark workload, or a
-      plain 1 GiB device copy that calibrates the memory counters;
+  bench.py --probe fused|stages|copy [--calls N] [--heads H]
+      a few calls of one prefill schedule on the benchmark workload (with H
+      heads in place of 32, if given), or a plain 1 GiB device copy that
+      calibrates the memory counters;
   bench.py --probe stamps [--calls N]
       the fused prefill from the profiling build libkda_stamps.so: cycles
       per item of each producer phase and per chunk of the state pass;
@@ -110,10 +111,11 @@ def measured_traffic():
 COPY_BYTES = 1 << 30
 
 
-def probe(what: str, calls: int):
-    """A few calls of one prefill schedule on the benchmark workload (or a
-    plain device copy of COPY_BYTES, which reads and writes exactly that many
-    bytes and so calibrates FETCH_SIZE / WRITE_SIZE), for rocprofv3 runs."""
+def probe(what: str, calls: int, heads: int = H):
+    """A few calls of one prefill schedule on the benchmark workload, or on
+    it with fewer heads (fewer records in each XCD's L2 at once), or a plain
+    device copy of COPY_BYTES, which reads and writes exactly that many bytes
+    and so calibrates FETCH_SIZE / WRITE_SIZE, for rocprofv3 runs."""
     import torch
 
     from gated_delta_rule_96_amd import kda, synth
@@ -127,20 +129,20 @@ def probe(what: str, calls: int):
         torch.cuda.synchronize()
         print(f"[probe] copy of {COPY_BYTES} bytes x {calls}", file=sys.stderr, flush=True)
         return
-    d = synth.make_inputs(B, T, H, DK, DV, seed=2)
+    d = synth.make_inputs(B, T, heads, DK, DV, seed=2)
     bf = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)
     q, k, v, beta, z = (bf(d[n]) for n in ("q", "k", "v", "beta", "z"))
     A = torch.from_numpy(d["A"].copy()).to(dev)
     h0 = torch.from_numpy(d["h0"]).to(dev)
     g, _ = kda.prepare_decay(z, A, want_gcum=False)
     stages = what == "stages"
-    ws = kda.alloc_workspace(B, T, H, DK, DV, torch.bfloat16, dev, stages=stages)
-    o = torch.empty((B, T, H, DV), dtype=torch.float32, device=dev)
-    ht = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    ws = kda.alloc_workspace(B, T, heads, DK, DV, torch.bfloat16, dev, stages=stages)
+    o = torch.empty((B, T, heads, DV), dtype=torch.float32, device=dev)
+    ht = torch.empty((B, heads, DK, DV), dtype=torch.float32, device=dev)
     for _ in range(calls):
         kda.fwd_chunked(q, k, v, g, beta, h0, ht=ht, workspace=ws, out=o, stages=3 if stages else None)
     torch.cuda.synchronize()
-    print(f"[probe] {what} x {calls} done", file=sys.stderr, flush=True)
+    print(f"[probe] {what} H={heads} x {calls} done", file=sys.stderr, flush=True)
 
 
 STAMP_NAMES = {
@@ -474,6 +476,7 @@ def main():
                     help="skip the B=4 H=16 T=8192 and million-token prefill lines")
     ap.add_argument("--probe", choices=("fused", "stages", "copy", "stamps"))
     ap.add_argument("--calls", type=int, default=3)
+    ap.add_argument("--heads", type=int, default=H, help="heads of the --probe fused/stages workload")
     ap.add_argument("--summarize")
     ap.add_argument("--summarize-pmc", nargs=6)
     args = ap.parse_args()
@@ -487,7 +490,7 @@ def main():
         probe_stamps(args.calls)
         return
     if args.probe:
-        probe(args.probe, args.calls)
+        probe(args.probe, args.calls, args.heads)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards by "
